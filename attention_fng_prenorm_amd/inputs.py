@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the fused-normalization workloads.
+
+This module only draws random numbers and rounds them to bf16 bit patterns;
+it holds none of the normalisation, GEMM or attention arithmetic, so both the
+HIP path and the fp64 oracle can consume its output without sharing method
+code.
+
+Recipe (all draws from numpy.random.Generator(PCG64(seed)), float32, then
+round-to-nearest-even to bf16 on the host; the same bf16 bits feed both
+sides).  "N(mu, v)" is mean and *variance*:
+
+  prenorm_rms_small   X[256,128] ~ N(0,1), W[128,128] ~ N(0,1/128), eps 1e-6
+  postnorm_ln_smalln  X[8192,256] ~ N(0,1), W[256,256] ~ N(0,1/256), eps 1e-5
+  prenorm_rms_mlp     X[4096,4096] = exp(xi_m) * z[m,k], xi, z ~ N(0,1);
+                      W[4096,14336] ~ N(0,1/4096), eps 1e-6
+  prenorm_rms_mlp_gamma  as above plus gamma[4096] ~ N(1, 0.1)
+  postnorm_rms_largen X[16384,1024] ~ N(0,1), W[1024,4096] ~ N(0,1/1024),
+                      eps 1e-6
+  norm_attention      Q, K, V [32,1024,4,128] (BSHD) ~ N(0,1),
+                      eps_ln 1e-5, eps_rms 1e-6, sm_scale 1/sqrt(128)
+
+Draw order inside one generator: X (row scales first when present), W,
+gamma; for attention Q, K, V.
+"""
+
+import math
+
+import numpy as np
+
+
+# Workload table.  "kind" selects the operation; sizes may be overridden for
+# reduced-size parity cases (the recipe above stays the same).
+WORKLOADS = {
+    "prenorm_rms_small": dict(kind="prenorm_rms", M=256, K=128, N=128, eps=1e-6,
+                              x_dist="normal", gamma=False, seed=1001),
+    "postnorm_ln_smalln": dict(kind="postnorm_ln", M=8192, K=256, N=256, eps=1e-5,
+                               x_dist="normal", gamma=False, seed=1002),
+    "prenorm_rms_mlp": dict(kind="prenorm_rms", M=4096, K=4096, N=14336, eps=1e-6,
+                            x_dist="lognormal_rows", gamma=False, seed=1003),
+    "prenorm_rms_mlp_gamma": dict(kind="prenorm_rms", M=4096, K=4096, N=14336, eps=1e-6,
+                                  x_dist="lognormal_rows", gamma=True, seed=1013),
+    "postnorm_rms_largen": dict(kind="postnorm_rms", M=16384, K=1024, N=4096, eps=1e-6,
+                                x_dist="normal", gamma=False, seed=1004),
+    "norm_attention": dict(kind="norm_attention", B=32, Sq=1024, Skv=1024, H=4, D=128,
+                           eps_ln=1e-5, eps_rms=1e-6, seed=1005),
+}
+
+
+def f32_to_bf16_bits(a):
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(bits):
+    """Widen bf16 bit patterns to float32 (exact); for host-side checks."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def _normal(rng, shape, var=1.0, mean=0.0):
+    z = rng.standard_normal(size=shape, dtype=np.float32)
+    if var != 1.0:
+        z *= np.float32(math.sqrt(var))
+    if mean != 0.0:
+        z += np.float32(mean)
+    return z
+
+
+def workload(name, **overrides):
+    """The workload spec for `name`, with sizes or seed overridden."""
+    if name not in WORKLOADS:
+        raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}")
+    spec = dict(WORKLOADS[name])
+    spec.update(overrides)
+    spec["name"] = name
+    return spec
+
+
+def make_gemm_inputs(spec):
+    """Inputs of a norm+GEMM workload as bf16 bit arrays: dict X, W, gamma."""
+    rng = np.random.Generator(np.random.PCG64(spec["seed"]))
+    M, K, N = spec["M"], spec["K"], spec["N"]
+    if spec["x_dist"] == "normal":
+        x = _normal(rng, (M, K))
+    elif spec["x_dist"] == "lognormal_rows":
+        s = np.exp(_normal(rng, (M, 1)))
+        x = s * _normal(rng, (M, K))
+    else:
+        raise ValueError(spec["x_dist"])
+    w = _normal(rng, (K, N), var=1.0 / K)
+    out = {"X": f32_to_bf16_bits(x), "W": f32_to_bf16_bits(w), "gamma": None}
+    if spec.get("gamma"):
+        out["gamma"] = f32_to_bf16_bits(_normal(rng, (K,), var=0.1, mean=1.0))
+    return out
+
+
+def make_attention_inputs(spec):
+    """Q, K, V of the attention workload as bf16 bit arrays (BSHD)."""
+    rng = np.random.Generator(np.random.PCG64(spec["seed"]))
+    B, Sq, Skv, H, D = spec["B"], spec["Sq"], spec["Skv"], spec["H"], spec["D"]
+    q = f32_to_bf16_bits(_normal(rng, (B, Sq, H, D)))
+    k = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
+    v = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
+    return {"Q": q, "K": k, "V": v}
+
+
+def make_inputs(name, **overrides):
+    """Spec and inputs for workload `name` (see the recipe in the header)."""
+    spec = workload(name, **overrides)
+    if spec["kind"] == "norm_attention":
+        return spec, make_attention_inputs(spec)
+    return spec, make_gemm_inputs(spec)

@@ -1,0 +1,15 @@
+"""fp64 CPU oracle (test infrastructure only; see fng_oracle's header)."""
+
+from .fng_oracle import (  # noqa: F401
+    attention,
+    bf16_to_f64,
+    compare,
+    gemm,
+    gemm_postnorm,
+    layernorm_rows,
+    norm_attention,
+    prenorm_rms_gemm,
+    rms_rstd,
+    rmsnorm_rows,
+    softmax_rows,
+)

@@ -1,0 +1,217 @@
+"""Plain fp64 CPU oracle for the fused-normalization hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+and imports nothing from the product package.
+
+Every function is the plain mathematical definition written out in numpy
+float64, with no blocking, fusion or reordering: the fused kernels reach the
+same real-number result because
+
+  * Lazy Pre-Norm only moves a row scale across a matrix product
+    ("Towards Free Normalization: Fusing Normalization into GEMM and Attention
+    Kernels", section 2, the row-scale commutation identity and its proof);
+  * the multi-CTA / split-N post-norm only re-associates a per-row sum
+    (same page, section 3, the reduction/elementwise decomposition);
+  * FlashNormAttention only re-orders a normalise -> attend -> normalise chain
+    (same page, section 4, the fused short-KV pseudocode).
+
+So the oracle is the definition, evaluated in fp64 on the exact bf16 inputs,
+with nothing rounded inside it.
+
+Readings of points the page leaves open (each also listed in the design notes):
+  * eps sits inside the square root and is an argument (section 2 writes the
+    rstd with eps inside the rsqrt).
+  * RMS divides by the length of the normalised axis (section 2 divides by the
+    last dimension of A).
+  * LayerNorm uses the biased (population) variance and no affine, as
+    torch.nn.LayerNorm does (linked from the introduction's note on affines;
+    benchmarks there disable affines).
+  * the optional RMSNorm gain gamma multiplies after normalisation
+    (y = rmsnorm(x) * gamma), then the product with W follows.
+  * attention: per (batch, head) LayerNorm of each query row over head_dim,
+    scores scaled by sm_scale after the product, max-subtracted softmax over
+    all keys (non-causal, no mask), product with V, then RMSNorm of each output
+    row over head_dim; K and V are not normalised; layout BSHD (section 4's
+    pseudocode header gives [batch, seq, H, head_dim]).
+"""
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# exact bf16 decoding (input plumbing, not arithmetic of the method)
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits):
+    """Decode raw bf16 bit patterns (uint16/int16 array) to float64, exactly.
+
+    A bf16 value is the upper 16 bits of an IEEE binary32; widening the bit
+    pattern by 16 zero bits gives the identical binary32 value, which converts
+    to binary64 without rounding.
+    """
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# row normalisations (section 2's rstd; section 3's LayerNorm/RMSNorm)
+# ---------------------------------------------------------------------------
+
+def rms_rstd(x, eps):
+    """rstd[m] = 1 / sqrt(mean_k x[m,k]^2 + eps)   (section 2, rstd(A))."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1)
+    return 1.0 / np.sqrt(ms + eps)
+
+
+def rmsnorm_rows(x, eps, gamma=None):
+    """RMSNorm over the last axis: y = x * rstd[:, None] (* gamma).
+
+    Section 2: rmsnorm(A) = A * rstd(A)[:, None].  gamma is the optional
+    elementwise gain (applied after the row scale).
+    Returns (y, rstd).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    r = rms_rstd(x, eps)
+    y = x * r[..., None]
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    return y, r
+
+
+def layernorm_rows(x, eps):
+    """LayerNorm over the last axis, no affine, biased variance.
+
+    mu = mean(x); var = mean((x - mu)^2); y = (x - mu) / sqrt(var + eps).
+    Returns (y, mean, rstd).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.mean(x, axis=-1)
+    d = x - mu[..., None]
+    var = np.mean(d * d, axis=-1)
+    r = 1.0 / np.sqrt(var + eps)
+    return d * r[..., None], mu, r
+
+
+# ---------------------------------------------------------------------------
+# norm + GEMM (sections 1-3)
+# ---------------------------------------------------------------------------
+
+def prenorm_rms_gemm(x, w, eps, gamma=None):
+    """Y = rmsnorm(X) @ W   (section 2, C = rmsnorm(A) @ B).
+
+    X is [M, K], W is [K, N]; the RMS statistic is taken over K from the raw X
+    (the gain, if any, is applied after the statistic).  Returns (Y, rstd[M]).
+    """
+    xn, r = rmsnorm_rows(x, eps, gamma)
+    return xn @ np.asarray(w, dtype=np.float64), r
+
+
+def gemm(x, w):
+    """Z = X @ W, X [M, K], W [K, N]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
+
+
+def gemm_postnorm(x, w, eps, kind):
+    """Y = norm(X @ W) over the N axis  (section 1 naive fusion and section 3
+    multi-CTA fusion both compute this; statistics come from the exact
+    product, i.e. the fp32 accumulator in a kernel, before output rounding).
+
+    kind is "ln" or "rms".  Returns (Y, mean[M] or None, rstd[M]).
+    """
+    z = gemm(x, w)
+    if kind == "ln":
+        return layernorm_rows(z, eps)
+    if kind == "rms":
+        y, r = rmsnorm_rows(z, eps)
+        return y, None, r
+    raise ValueError(f"unknown norm kind {kind!r}")
+
+
+# ---------------------------------------------------------------------------
+# attention (section 4)
+# ---------------------------------------------------------------------------
+
+def softmax_rows(s):
+    """Max-subtracted softmax over the last axis."""
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention(q, k, v, sm_scale):
+    """Plain softmax attention, BSHD: O[b,s,h,:] = softmax(q k^T * scale) v.
+
+    q is [B, Sq, H, D]; k, v are [B, Skv, H, D].  Non-causal, no mask.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    o = np.empty((B, Sq, H, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, :, h, :] @ k[b, :, h, :].T) * sm_scale
+            o[b, :, h, :] = softmax_rows(s) @ v[b, :, h, :]
+    return o
+
+
+def norm_attention(q, k, v, eps_ln, eps_rms, sm_scale):
+    """out = rmsnorm(softmax(layernorm(q) k^T * scale) v), per (b, h), BSHD.
+
+    Section 4: ln_q = layernorm(q) before the score product, and an RMSNorm of
+    the attention output after it; both norms here run over head_dim of one
+    head, softmax replaces the generic activation and there are no residual
+    adds (the norm-sandwiched attention workload).  Returns
+    (out, ln_mean[B,Sq,H], ln_rstd[B,Sq,H], rms_rstd[B,Sq,H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    out = np.empty((B, Sq, H, v.shape[-1]), dtype=np.float64)
+    ln_mean = np.empty((B, Sq, H))
+    ln_rstd = np.empty((B, Sq, H))
+    rms_rstd = np.empty((B, Sq, H))
+    for b in range(B):
+        for h in range(H):
+            qn, mu, r1 = layernorm_rows(q[b, :, h, :], eps_ln)
+            s = (qn @ k[b, :, h, :].T) * sm_scale
+            o = softmax_rows(s) @ v[b, :, h, :]
+            y, r2 = rmsnorm_rows(o, eps_rms)
+            out[b, :, h, :] = y
+            ln_mean[b, :, h] = mu
+            ln_rstd[b, :, h] = r1
+            rms_rstd[b, :, h] = r2
+    return out, ln_mean, ln_rstd, rms_rstd
+
+
+# ---------------------------------------------------------------------------
+# the agreed comparison metric
+# ---------------------------------------------------------------------------
+
+def compare(y, ref):
+    """Errors of a result y against an fp64 reference.
+
+    Returns a dict with
+      normwise_rel = max|y - ref| / max|ref|  (the "max relative error", read
+                                               normwise so it is defined when
+                                               ref has zeros)
+      mae          = mean|y - ref|
+      max_abs      = max|y - ref|
+    """
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {ref.shape}")
+    if y.size == 0:
+        return {"normwise_rel": 0.0, "mae": 0.0, "max_abs": 0.0}
+    err = np.abs(y - ref)
+    scale = float(np.max(np.abs(ref)))
+    return {
+        "normwise_rel": float(np.max(err)) / scale if scale > 0 else float(np.max(err)),
+        "mae": float(np.mean(err)),
+        "max_abs": float(np.max(err)),
+    }

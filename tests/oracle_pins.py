@@ -1,0 +1,464 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each check takes the oracle module (or a planted-mistake copy of it) as its
+argument and raises AssertionError when the oracle disagrees with:
+  * pure-Python brute force (math module, explicit loops) on tiny inputs,
+  * closed forms and invariants the mathematics fixes,
+  * special cases that reduce to torch CPU fp64 library routines
+    (F.rms_norm, F.layer_norm, F.scaled_dot_product_attention).
+They are shared by test_oracle_pins.py (real oracle: all must pass) and
+test_oracle_mutants.py (planted mistakes: at least one must fail).
+
+Formulas follow "Towards Free Normalization: Fusing Normalization into GEMM
+and Attention Kernels": section 2 (rstd with eps inside the rsqrt, division by
+the row length, the row-scale commutation identity), section 3 (post-norm over
+the GEMM output rows) and section 4 (LayerNorm before attention, RMSNorm
+after it).
+"""
+
+import math
+
+import numpy as np
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------------------
+# brute force in plain Python (no numpy arithmetic)
+# ---------------------------------------------------------------------------
+
+def bf_rmsnorm(rows, eps, gamma=None):
+    out, rs = [], []
+    for row in rows:
+        n = len(row)
+        ss = 0.0
+        for v in row:
+            ss += v * v
+        r = 1.0 / math.sqrt(ss / n + eps)
+        y = [v * r for v in row]
+        if gamma is not None:
+            y = [y[i] * gamma[i] for i in range(n)]
+        out.append(y)
+        rs.append(r)
+    return out, rs
+
+
+def bf_layernorm(rows, eps):
+    out, mus, rs = [], [], []
+    for row in rows:
+        n = len(row)
+        mu = 0.0
+        for v in row:
+            mu += v
+        mu /= n
+        var = 0.0
+        for v in row:
+            var += (v - mu) * (v - mu)
+        var /= n
+        r = 1.0 / math.sqrt(var + eps)
+        out.append([(v - mu) * r for v in row])
+        mus.append(mu)
+        rs.append(r)
+    return out, mus, rs
+
+
+def bf_matmul(a, b):
+    M, K, N = len(a), len(b), len(b[0])
+    assert all(len(r) == K for r in a)
+    c = [[0.0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += a[i][k] * b[k][j]
+            c[i][j] = s
+    return c
+
+
+def bf_softmax(row):
+    m = max(row)
+    e = [math.exp(v - m) for v in row]
+    s = sum(e)
+    return [v / s for v in e]
+
+
+def bf_norm_attention(q, k, v, eps_ln, eps_rms, scale):
+    """q[b][s][h][d] nested lists; returns out nested lists."""
+    B, Sq, H, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Skv = len(k[0])
+    out = [[[None] * H for _ in range(Sq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            qrows = [q[b][s][h] for s in range(Sq)]
+            qn, _, _ = bf_layernorm(qrows, eps_ln)
+            for s in range(Sq):
+                sc = []
+                for t in range(Skv):
+                    acc = 0.0
+                    for d in range(D):
+                        acc += qn[s][d] * k[b][t][h][d]
+                    sc.append(acc * scale)
+                p = bf_softmax(sc)
+                o = [0.0] * D
+                for t in range(Skv):
+                    for d in range(D):
+                        o[d] += p[t] * v[b][t][h][d]
+                y, _ = bf_rmsnorm([o], eps_rms)
+                out[b][s][h] = y[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# bf16 decoding
+# ---------------------------------------------------------------------------
+
+def check_bf16_decode(O):
+    bits = np.array([0x3F80, 0xC000, 0x4049, 0x0001, 0x7F7F, 0x0000, 0x8000, 0x3E80,
+                     0x7F80, 0xFF80], dtype=np.uint16)
+    want = [1.0, -2.0, 3.140625, 2.0 ** -133, (2.0 - 2.0 ** -7) * 2.0 ** 127, 0.0, -0.0,
+            0.25, math.inf, -math.inf]
+    got = O.bf16_to_f64(bits)
+    for g, w, b in zip(got, want, bits):
+        assert g == w, f"bf16 0x{int(b):04x} -> {g!r}, want {w!r}"
+    assert math.copysign(1.0, got[6]) == -1.0
+    assert np.isnan(O.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16))[0])
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def check_rmsnorm_closed_form(O):
+    # x = [3, 4]: mean square 12.5; eps = 0 -> rstd = 1/sqrt(12.5)
+    y, r = O.rmsnorm_rows(np.array([[3.0, 4.0]]), 0.0)
+    _close(r, [1.0 / math.sqrt(12.5)], 1e-15, "rstd([3,4])")
+    _close(y, [[3.0 / math.sqrt(12.5), 4.0 / math.sqrt(12.5)]], 1e-15, "rmsnorm([3,4])")
+    # constant row c: y = c / sqrt(c^2 + eps)
+    y, _ = O.rmsnorm_rows(np.full((1, 5), 2.0), 0.25)
+    _close(y, np.full((1, 5), 2.0 / math.sqrt(4.25)), 1e-15, "rmsnorm(const)")
+    # zero row: y = 0, rstd = 1/sqrt(eps)
+    y, r = O.rmsnorm_rows(np.zeros((1, 4)), 1e-6)
+    _close(y, np.zeros((1, 4)), 0.0, "rmsnorm(0)")
+    _close(r, [1e3], 1e-9, "rstd(0)")
+
+
+def check_rmsnorm_bruteforce(O):
+    rng = _rng(11)
+    x = rng.standard_normal((5, 7)) * rng.uniform(0.1, 3.0, (5, 1))
+    g = rng.standard_normal(7)
+    for gamma in (None, g):
+        y, r = O.rmsnorm_rows(x, 1e-3, gamma)
+        by, br = bf_rmsnorm(x.tolist(), 1e-3, None if gamma is None else gamma.tolist())
+        _close(y, by, 1e-13, "rmsnorm vs brute force")
+        _close(r, br, 1e-13, "rstd vs brute force")
+
+
+def check_rmsnorm_invariants(O):
+    rng = _rng(12)
+    x = rng.standard_normal((64, 48)) * rng.lognormal(0.0, 1.0, (64, 1))
+    eps = 1e-6
+    y, _ = O.rmsnorm_rows(x, eps)
+    ms = np.mean(x * x, axis=1)
+    # mean(y^2) = ms / (ms + eps) exactly
+    _close(np.mean(y * y, axis=1), ms / (ms + eps), 1e-12, "rms of rmsnorm output")
+    # eps = 0: invariant under positive row scaling
+    y0, _ = O.rmsnorm_rows(x, 0.0)
+    y1, _ = O.rmsnorm_rows(x * 37.5, 0.0)
+    _close(y0, y1, 1e-12, "rmsnorm scale invariance")
+    _close(np.mean(y0 * y0, axis=1), np.ones(64), 1e-12, "unit rms at eps=0")
+
+
+def check_rmsnorm_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(13)
+    x = rng.standard_normal((33, 96))
+    g = rng.standard_normal(96)
+    for gamma in (None, g):
+        ref = F.rms_norm(torch.from_numpy(x), (96,),
+                         None if gamma is None else torch.from_numpy(gamma), eps=1e-5).numpy()
+        y, _ = O.rmsnorm_rows(x, 1e-5, gamma)
+        _close(y, ref, 1e-12, "rmsnorm vs torch F.rms_norm fp64")
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm
+# ---------------------------------------------------------------------------
+
+def check_layernorm_closed_form(O):
+    # x = [1,2,3,4]: mu = 2.5, biased var = 1.25
+    y, mu, r = O.layernorm_rows(np.array([[1.0, 2.0, 3.0, 4.0]]), 0.0)
+    _close(mu, [2.5], 1e-15, "ln mean")
+    _close(r, [1.0 / math.sqrt(1.25)], 1e-15, "ln rstd (biased variance)")
+    _close(y, [[(v - 2.5) / math.sqrt(1.25) for v in (1, 2, 3, 4)]], 1e-15, "ln([1,2,3,4])")
+    # constant row -> exactly 0
+    y, mu, r = O.layernorm_rows(np.full((2, 6), -3.5), 1e-5)
+    _close(y, np.zeros((2, 6)), 0.0, "ln(const)")
+    _close(mu, [-3.5, -3.5], 0.0, "ln mean const")
+
+
+def check_layernorm_bruteforce(O):
+    rng = _rng(21)
+    x = rng.standard_normal((6, 5)) * 2.0 + 0.7
+    y, mu, r = O.layernorm_rows(x, 1e-2)
+    by, bmu, br = bf_layernorm(x.tolist(), 1e-2)
+    _close(y, by, 1e-13, "ln vs brute force")
+    _close(mu, bmu, 1e-13, "ln mean vs brute force")
+    _close(r, br, 1e-13, "ln rstd vs brute force")
+
+
+def check_layernorm_invariants(O):
+    rng = _rng(22)
+    x = rng.standard_normal((40, 64)) * 3.0 + 5.0
+    eps = 1e-5
+    y, mu, r = O.layernorm_rows(x, eps)
+    v = np.var(x, axis=1)
+    _close(np.mean(y, axis=1), np.zeros(40), 1e-12, "ln output mean")
+    _close(np.mean(y * y, axis=1), v / (v + eps), 1e-12, "ln output variance")
+    y0, _, _ = O.layernorm_rows(x, 0.0)
+    y1, _, _ = O.layernorm_rows(x * 4.25 - 11.0, 0.0)
+    _close(y0, y1, 1e-11, "ln affine invariance")
+
+
+def check_layernorm_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(23)
+    x = rng.standard_normal((31, 80)) * 1.5 - 0.5
+    ref = F.layer_norm(torch.from_numpy(x), (80,), eps=1e-5).numpy()
+    y, _, _ = O.layernorm_rows(x, 1e-5)
+    _close(y, ref, 1e-12, "ln vs torch F.layer_norm fp64")
+
+
+# ---------------------------------------------------------------------------
+# norm + GEMM
+# ---------------------------------------------------------------------------
+
+def check_prenorm_gemm_bruteforce(O):
+    rng = _rng(31)
+    M, K, N = 4, 6, 3
+    x = rng.standard_normal((M, K)) * 1.7
+    w = rng.standard_normal((K, N))
+    g = rng.standard_normal(K)
+    for gamma in (None, g):
+        y, r = O.prenorm_rms_gemm(x, w, 1e-4, gamma)
+        xn, br = bf_rmsnorm(x.tolist(), 1e-4, None if gamma is None else gamma.tolist())
+        _close(y, bf_matmul(xn, w.tolist()), 1e-13, "prenorm gemm vs brute force")
+        _close(r, br, 1e-13, "prenorm rstd vs brute force")
+
+
+def check_prenorm_gemm_identities(O):
+    rng = _rng(32)
+    M, K, N = 9, 16, 5
+    x = rng.standard_normal((M, K)) * rng.lognormal(0.0, 1.0, (M, 1))
+    w = rng.standard_normal((K, N))
+    eps = 1e-6
+    y, r = O.prenorm_rms_gemm(x, w, eps)
+    # lazy form: (diag(rstd) X) W = diag(rstd) (X W), rstd from brute force
+    _, br = bf_rmsnorm(x.tolist(), eps)
+    lazy = np.array(bf_matmul(x.tolist(), w.tolist())) * np.array(br)[:, None]
+    _close(y, lazy, 1e-12, "lazy pre-norm identity")
+    # W = I reduces to rmsnorm(X)
+    yi, _ = O.prenorm_rms_gemm(x, np.eye(K), eps)
+    xn, _ = bf_rmsnorm(x.tolist(), eps)
+    _close(yi, xn, 1e-13, "prenorm with W = I")
+    # row permutation equivariance
+    p = rng.permutation(M)
+    yp, _ = O.prenorm_rms_gemm(x[p], w, eps)
+    _close(yp, y[p], 1e-13, "prenorm row permutation")
+
+
+def check_prenorm_gemm_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(33)
+    x = rng.standard_normal((20, 64)) * 2.0
+    w = rng.standard_normal((64, 24)) / 8.0
+    g = 1.0 + 0.3 * rng.standard_normal(64)
+    ref = (F.rms_norm(torch.from_numpy(x), (64,), torch.from_numpy(g), eps=1e-6)
+           @ torch.from_numpy(w)).numpy()
+    y, _ = O.prenorm_rms_gemm(x, w, 1e-6, g)
+    _close(y, ref, 1e-12, "prenorm gemm vs torch fp64")
+
+
+def check_postnorm_bruteforce(O):
+    rng = _rng(41)
+    M, K, N = 3, 5, 6
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((K, N))
+    z = bf_matmul(x.tolist(), w.tolist())
+    y, mu, r = O.gemm_postnorm(x, w, 1e-3, "ln")
+    by, bmu, br = bf_layernorm(z, 1e-3)
+    _close(y, by, 1e-13, "post-LN gemm vs brute force")
+    _close(mu, bmu, 1e-13, "post-LN mean vs brute force")
+    _close(r, br, 1e-13, "post-LN rstd vs brute force")
+    y, mu, r = O.gemm_postnorm(x, w, 1e-3, "rms")
+    by, br = bf_rmsnorm(z, 1e-3)
+    assert mu is None
+    _close(y, by, 1e-13, "post-RMS gemm vs brute force")
+    _close(r, br, 1e-13, "post-RMS rstd vs brute force")
+
+
+def check_postnorm_identities(O):
+    rng = _rng(42)
+    M, K, N = 12, 32, 48
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((K, N)) / math.sqrt(K)
+    # W = I (K = N) reduces to the row norm of X
+    xs = rng.standard_normal((M, N)) * 2.0 + 1.0
+    yi, _, _ = O.gemm_postnorm(xs, np.eye(N), 1e-5, "ln")
+    bi, _, _ = bf_layernorm(xs.tolist(), 1e-5)
+    _close(yi, bi, 1e-13, "post-LN with W = I")
+    yi, _, _ = O.gemm_postnorm(xs, np.eye(N), 1e-6, "rms")
+    bi, _ = bf_rmsnorm(xs.tolist(), 1e-6)
+    _close(yi, bi, 1e-13, "post-RMS with W = I")
+    # output invariants over N
+    y, _, _ = O.gemm_postnorm(x, w, 0.0, "ln")
+    _close(np.mean(y, axis=1), np.zeros(M), 1e-12, "post-LN row mean")
+    _close(np.mean(y * y, axis=1), np.ones(M), 1e-12, "post-LN row variance")
+    y, _, _ = O.gemm_postnorm(x, w, 0.0, "rms")
+    _close(np.mean(y * y, axis=1), np.ones(M), 1e-12, "post-RMS row rms")
+    p = rng.permutation(M)
+    ya, _, _ = O.gemm_postnorm(x, w, 1e-6, "rms")
+    yb, _, _ = O.gemm_postnorm(x[p], w, 1e-6, "rms")
+    _close(yb, ya[p], 1e-13, "post-norm row permutation")
+
+
+def check_postnorm_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(43)
+    x = rng.standard_normal((17, 40))
+    w = rng.standard_normal((40, 72)) / 6.0
+    z = torch.from_numpy(x) @ torch.from_numpy(w)
+    y, _, _ = O.gemm_postnorm(x, w, 1e-5, "ln")
+    _close(y, F.layer_norm(z, (72,), eps=1e-5).numpy(), 1e-12, "post-LN vs torch fp64")
+    y, _, _ = O.gemm_postnorm(x, w, 1e-6, "rms")
+    _close(y, F.rms_norm(z, (72,), eps=1e-6).numpy(), 1e-12, "post-RMS vs torch fp64")
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def check_attention_bruteforce(O):
+    rng = _rng(51)
+    B, Sq, Skv, H, D = 1, 3, 4, 2, 5
+    q = rng.standard_normal((B, Sq, H, D)) * 1.3 + 0.2
+    k = rng.standard_normal((B, Skv, H, D))
+    v = rng.standard_normal((B, Skv, H, D))
+    out, _, _, _ = O.norm_attention(q, k, v, 1e-5, 1e-6, 0.7)
+    ref = bf_norm_attention(q.tolist(), k.tolist(), v.tolist(), 1e-5, 1e-6, 0.7)
+    _close(out, ref, 1e-12, "norm attention vs brute force")
+
+
+def check_attention_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(52)
+    B, Sq, Skv, H, D = 2, 9, 13, 3, 16
+    q = rng.standard_normal((B, Sq, H, D)) * 2.0 - 1.0
+    k = rng.standard_normal((B, Skv, H, D))
+    v = rng.standard_normal((B, Skv, H, D))
+    scale = 1.0 / math.sqrt(D)
+    tq = F.layer_norm(torch.from_numpy(q), (D,), eps=1e-5).permute(0, 2, 1, 3).contiguous()
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).contiguous()
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).contiguous()
+    o = F.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    ref = F.rms_norm(o, (D,), eps=1e-6).permute(0, 2, 1, 3).numpy()
+    out, mu, r1, r2 = O.norm_attention(q, k, v, 1e-5, 1e-6, scale)
+    _close(out, ref, 1e-12, "norm attention vs torch fp64 sdpa")
+    # plain attention against sdpa too
+    o2 = F.scaled_dot_product_attention(torch.from_numpy(q).permute(0, 2, 1, 3).contiguous(),
+                                        tk, tv, scale=scale).permute(0, 2, 1, 3).numpy()
+    _close(O.attention(q, k, v, scale), o2, 1e-12, "attention vs torch fp64 sdpa")
+    _close(mu, np.mean(q, axis=-1), 1e-13, "ln mean output")
+    _close(r1, 1.0 / np.sqrt(np.var(q, axis=-1) + 1e-5), 1e-12, "ln rstd output")
+
+
+def check_attention_closed_forms(O):
+    rng = _rng(53)
+    B, Sq, H, D = 2, 5, 3, 8
+    q = rng.standard_normal((B, Sq, H, D))
+    # one key: weights are 1, out = rmsnorm(v) for every query
+    k1 = rng.standard_normal((B, 1, H, D))
+    v1 = rng.standard_normal((B, 1, H, D))
+    out, _, _, _ = O.norm_attention(q, k1, v1, 1e-5, 1e-6, 0.3)
+    want, _ = bf_rmsnorm(v1.reshape(-1, D).tolist(), 1e-6)
+    want = np.array(want).reshape(B, 1, H, D)
+    _close(out, np.broadcast_to(want, out.shape), 1e-13, "single key -> rmsnorm(v)")
+    # K = 0: uniform weights, out = rmsnorm(mean_t v)
+    Skv = 7
+    k0 = np.zeros((B, Skv, H, D))
+    v = rng.standard_normal((B, Skv, H, D))
+    out, _, _, _ = O.norm_attention(q, k0, v, 1e-5, 1e-6, 0.3)
+    mv = np.mean(v, axis=1)
+    want, _ = bf_rmsnorm(mv.reshape(-1, D).tolist(), 1e-6)
+    want = np.array(want).reshape(B, 1, H, D)
+    _close(out, np.broadcast_to(want, out.shape), 1e-13, "K = 0 -> uniform weights")
+    # constant query rows: layernorm gives 0 -> uniform weights for any K
+    qc = np.full((B, Sq, H, D), 4.0)
+    k = rng.standard_normal((B, Skv, H, D))
+    out, _, _, _ = O.norm_attention(qc, k, v, 1e-5, 1e-6, 0.3)
+    _close(out, np.broadcast_to(want, out.shape), 1e-13, "constant q -> uniform weights")
+    # jointly permuting keys and values leaves the output unchanged
+    qq = rng.standard_normal((B, Sq, H, D))
+    o1, _, _, _ = O.norm_attention(qq, k, v, 1e-5, 1e-6, 0.3)
+    p = rng.permutation(Skv)
+    o2, _, _, _ = O.norm_attention(qq, k[:, p], v[:, p], 1e-5, 1e-6, 0.3)
+    _close(o1, o2, 1e-13, "kv permutation invariance")
+    # output rows have rms ms/(ms+eps) -> ~1
+    _close(np.mean(o1 * o1, axis=-1), np.ones(o1.shape[:-1]), 1e-3, "output row rms")
+
+
+def check_compare(O):
+    e = O.compare(np.array([1.0, 2.0]), np.array([1.0, 3.0]))
+    assert abs(e["normwise_rel"] - 1.0 / 3.0) < 1e-15, e
+    assert abs(e["mae"] - 0.5) < 1e-15, e
+    assert abs(e["max_abs"] - 1.0) < 1e-15, e
+
+
+ALL_CHECKS = [
+    check_bf16_decode,
+    check_rmsnorm_closed_form,
+    check_rmsnorm_bruteforce,
+    check_rmsnorm_invariants,
+    check_rmsnorm_torch,
+    check_layernorm_closed_form,
+    check_layernorm_bruteforce,
+    check_layernorm_invariants,
+    check_layernorm_torch,
+    check_prenorm_gemm_bruteforce,
+    check_prenorm_gemm_identities,
+    check_prenorm_gemm_torch,
+    check_postnorm_bruteforce,
+    check_postnorm_identities,
+    check_postnorm_torch,
+    check_attention_bruteforce,
+    check_attention_torch,
+    check_attention_closed_forms,
+    check_compare,
+]
+
+
+def failing_checks(O):
+    """Names of the checks that fail for oracle module/namespace O."""
+    bad = []
+    for chk in ALL_CHECKS:
+        try:
+            chk(O)
+        except AssertionError:
+            bad.append(chk.__name__)
+        except Exception:  # a mutant may crash a check outright: also a catch
+            bad.append(chk.__name__)
+    return bad

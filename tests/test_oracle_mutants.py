@@ -1,0 +1,192 @@
+"""Planted mistakes in copies of the oracle (CPU only): each must fail a pin.
+
+This shows the pins are strong enough that a plausible slip anywhere in the
+oracle (a dropped term, a wrong axis or sign, a transposed operand, eps in the
+wrong place, a biased/unbiased mix-up) does not go unnoticed.  The mistakes
+live only in these in-memory copies; the real oracle is untouched.
+"""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import fng_oracle as F
+
+
+def _ns(**over):
+    ns = types.SimpleNamespace(**{n: getattr(F, n) for n in dir(F) if not n.startswith("_")})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    # rebind the composite functions so they use the mutated pieces
+    def prenorm_rms_gemm(x, w, eps, gamma=None):
+        xn, r = ns.rmsnorm_rows(x, eps, gamma)
+        return xn @ np.asarray(w, dtype=np.float64), r
+
+    def gemm_postnorm(x, w, eps, kind):
+        z = ns.gemm(x, w)
+        if kind == "ln":
+            return ns.layernorm_rows(z, eps)
+        y, r = ns.rmsnorm_rows(z, eps)
+        return y, None, r
+
+    def norm_attention(q, k, v, eps_ln, eps_rms, sm_scale):
+        q = np.asarray(q, dtype=np.float64)
+        B, Sq, H, D = q.shape
+        out = np.empty((B, Sq, H, np.shape(v)[-1]))
+        mu_a = np.empty((B, Sq, H)); r1_a = np.empty((B, Sq, H)); r2_a = np.empty((B, Sq, H))
+        for b in range(B):
+            for h in range(H):
+                qn, mu, r1 = ns.layernorm_rows(q[b, :, h, :], eps_ln)
+                s = (qn @ np.asarray(k)[b, :, h, :].T) * sm_scale
+                o = ns.softmax_rows(s) @ np.asarray(v)[b, :, h, :]
+                y, r2 = ns.rmsnorm_rows(o, eps_rms)
+                out[b, :, h, :] = y
+                mu_a[b, :, h] = mu; r1_a[b, :, h] = r1; r2_a[b, :, h] = r2
+        return out, mu_a, r1_a, r2_a
+
+    for name, fn in (("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
+                     ("norm_attention", norm_attention)):
+        if name not in over:
+            setattr(ns, name, fn)
+    return ns
+
+
+def _rms_eps_outside(x, eps, gamma=None):
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / (np.sqrt(np.mean(x * x, axis=-1)) + eps)
+    y = x * r[..., None]
+    return (y * gamma if gamma is not None else y), r
+
+
+def _rms_sum_not_mean(x, eps, gamma=None):
+    x = np.asarray(x, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.sum(x * x, axis=-1) / max(x.shape[-1] - 1, 1) + eps)
+    y = x * r[..., None]
+    return (y * gamma if gamma is not None else y), r
+
+
+def _rms_gamma_in_stats(x, eps, gamma=None):
+    x = np.asarray(x, dtype=np.float64)
+    if gamma is not None:
+        x = x * gamma
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+    return x * r[..., None], r
+
+
+def _ln_unbiased(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.mean(x, axis=-1)
+    d = x - mu[..., None]
+    var = np.sum(d * d, axis=-1) / (x.shape[-1] - 1)
+    r = 1.0 / np.sqrt(var + eps)
+    return d * r[..., None], mu, r
+
+
+def _ln_eps_outside(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.mean(x, axis=-1)
+    d = x - mu[..., None]
+    r = 1.0 / (np.sqrt(np.mean(d * d, axis=-1)) + eps)
+    return d * r[..., None], mu, r
+
+
+def _ln_no_center(x, eps):
+    x = np.asarray(x, dtype=np.float64)
+    mu = np.mean(x, axis=-1)
+    d = x - mu[..., None]
+    r = 1.0 / np.sqrt(np.mean(d * d, axis=-1) + eps)
+    return x * r[..., None], mu, r
+
+
+def _gemm_transposed(x, w):
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def _softmax_wrong_axis(s):
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - np.max(s, axis=0, keepdims=True))
+    return e / np.sum(e, axis=0, keepdims=True)
+
+
+def _softmax_no_norm(s):
+    s = np.asarray(s, dtype=np.float64)
+    return np.exp(s - np.max(s, axis=-1, keepdims=True))
+
+
+def _decode_wrong(bits):
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(15)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _compare_wrong(y, ref):
+    err = np.abs(np.asarray(y, np.float64) - np.asarray(ref, np.float64))
+    return {"normwise_rel": float(np.max(err)), "mae": float(np.max(err)), "max_abs": float(np.max(err))}
+
+
+def _attn_scale_divided(base):
+    def f(q, k, v, eps_ln, eps_rms, sm_scale):
+        return base(q, k, v, eps_ln, eps_rms, 1.0 / sm_scale)
+    return f
+
+
+def _attn_norm_k(q, k, v, eps_ln, eps_rms, sm_scale):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    out = np.empty(q.shape[:3] + (np.shape(v)[-1],))
+    z = np.zeros((B, Sq, H))
+    for b in range(B):
+        for h in range(H):
+            kn, _, _ = F.layernorm_rows(k[b, :, h, :], eps_ln)
+            s = (q[b, :, h, :] @ kn.T) * sm_scale
+            o = F.softmax_rows(s) @ np.asarray(v)[b, :, h, :]
+            out[b, :, h, :], _ = F.rmsnorm_rows(o, eps_rms)
+    return out, z, z, z
+
+
+def _attn_no_out_norm(q, k, v, eps_ln, eps_rms, sm_scale):
+    q = np.asarray(q, dtype=np.float64)
+    B, Sq, H, D = q.shape
+    out = np.empty(q.shape[:3] + (np.shape(v)[-1],))
+    z = np.zeros((B, Sq, H))
+    for b in range(B):
+        for h in range(H):
+            qn, _, _ = F.layernorm_rows(q[b, :, h, :], eps_ln)
+            s = (qn @ np.asarray(k)[b, :, h, :].T) * sm_scale
+            out[b, :, h, :] = F.softmax_rows(s) @ np.asarray(v)[b, :, h, :]
+    return out, z, z, z
+
+
+MUTANTS = {
+    "rms_eps_outside_sqrt": dict(rmsnorm_rows=_rms_eps_outside),
+    "rms_divides_by_n_minus_1": dict(rmsnorm_rows=_rms_sum_not_mean),
+    "rms_gamma_before_stats": dict(rmsnorm_rows=_rms_gamma_in_stats),
+    "ln_unbiased_variance": dict(layernorm_rows=_ln_unbiased),
+    "ln_eps_outside_sqrt": dict(layernorm_rows=_ln_eps_outside),
+    "ln_missing_centering": dict(layernorm_rows=_ln_no_center),
+    "gemm_transposed_w": dict(gemm=_gemm_transposed,
+                              prenorm_rms_gemm=lambda x, w, eps, gamma=None: (
+                                  F.rmsnorm_rows(x, eps, gamma)[0] @ np.asarray(w).T,
+                                  F.rms_rstd(x, eps))),
+    "softmax_over_queries": dict(softmax_rows=_softmax_wrong_axis),
+    "softmax_unnormalised": dict(softmax_rows=_softmax_no_norm),
+    "bf16_decode_shift": dict(bf16_to_f64=_decode_wrong),
+    "compare_mae_is_max": dict(compare=_compare_wrong),
+    "attn_scale_inverted": dict(norm_attention=_attn_scale_divided(F.norm_attention)),
+    "attn_normalises_k": dict(norm_attention=_attn_norm_k),
+    "attn_missing_out_rmsnorm": dict(norm_attention=_attn_no_out_norm),
+}
+
+
+def test_unmutated_copy_passes():
+    assert oracle_pins.failing_checks(_ns()) == []
+    assert oracle_pins.failing_checks(oracle) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    bad = oracle_pins.failing_checks(_ns(**MUTANTS[name]))
+    assert bad, f"planted mistake {name} passed every pin"
