@@ -1,0 +1,232 @@
+// C ABI of libfng.so: argument validation and dispatch to the HIP kernels.
+// Every entry point validates before touching the HIP runtime, so a rejected
+// call enqueues nothing.  Semantics and conventions are documented in
+// include/fng.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fng_internal.h"
+
+#define FNG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using fng::GemmCall;
+
+constexpr int kVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// common GEMM validation; returns FNG_OK or the error
+int check_gemm(const void* X, const void* W, const void* Y, int64_t M, int64_t N, int64_t K, float eps,
+               bool need_eps) {
+  if (M < 0 || N < 0 || K < 1) return FNG_ERR_INVALID_ARG;
+  if (need_eps && !(eps > 0.f && isfinite(eps))) return FNG_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FNG_OK;
+  if (!X || !W || !Y) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return FNG_ERR_MISALIGNED;
+  if (K % 8 != 0 || N % 8 != 0) return FNG_ERR_MISALIGNED;
+  // 32-bit index and buffer-range limits of the kernels
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FNG_ERR_UNSUPPORTED;
+  if ((K + 256) * N * 2 >= (int64_t)UINT32_MAX) return FNG_ERR_UNSUPPORTED;  // W rows incl. K-tile overrun
+  if (256 * K * 2 >= (int64_t)UINT32_MAX) return FNG_ERR_UNSUPPORTED;        // one X row block
+  if (M * N >= ((int64_t)1 << 46)) return FNG_ERR_UNSUPPORTED;
+  return FNG_OK;
+}
+
+bool m_or_n_empty(int64_t M, int64_t N) { return M == 0 || N == 0; }
+
+struct Workspace {
+  float* part;
+  uint32_t* cnt;
+  uint32_t* done;
+  uint32_t* status;
+  size_t bytes;
+};
+
+// layout: [status (256 B)] [cnt: tiles_m u32] [done: tiles_m u32] (256-B aligned) [partials]
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Workspace layout(void* base, int64_t M, int64_t N) {
+  const int64_t tm = fng::splitn_tiles_m(M), tn = fng::splitn_tiles_n(N), bm = fng::splitn_bm();
+  char* b = static_cast<char*>(base);
+  Workspace w{};
+  size_t off = 0;
+  w.status = reinterpret_cast<uint32_t*>(b + off);
+  off += 256;
+  w.cnt = reinterpret_cast<uint32_t*>(b + off);
+  off += align256((size_t)tm * 4);
+  w.done = reinterpret_cast<uint32_t*>(b + off);
+  off += align256((size_t)tm * 4);
+  w.part = reinterpret_cast<float*>(b + off);
+  off += (size_t)tm * tn * bm * 2 * sizeof(float);
+  w.bytes = off;
+  return w;
+}
+
+int resolve_path(int path, int64_t M, int64_t N) {
+  if (path == FNG_PATH_AUTO) {
+    if (N <= fng::fulln_max_n()) return FNG_PATH_FULLN;
+    if (fng::splitn_feasible(M, N)) return FNG_PATH_SPLITN;
+    return FNG_PATH_TWOPASS;
+  }
+  return path;
+}
+
+int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, float* rstd_out, int64_t M,
+             int64_t N, int64_t K, float eps, void* workspace, size_t workspace_bytes, int path,
+             void* stream) {
+  int st = check_gemm(X, W, Y, M, N, K, eps, true);
+  if (st != FNG_OK) return st;
+  if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
+  if (m_or_n_empty(M, N)) return FNG_OK;
+  if ((mean_out && !aligned16(mean_out)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
+  path = resolve_path(path, M, N);
+  GemmCall c{X, W, nullptr, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
+  if (path == FNG_PATH_FULLN) {
+    if (N > fng::fulln_max_n()) return FNG_ERR_UNSUPPORTED;
+    return fng::launch_postnorm_fulln(c, ln, as_stream(stream));
+  }
+  const size_t need = fng_gemm_postnorm_workspace_bytes(M, N, K, path);
+  if (!workspace || workspace_bytes < need) return FNG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
+  Workspace w = layout(workspace, M, N);
+  c.part = w.part;
+  c.cnt = w.cnt;
+  c.done = w.done;
+  c.status = w.status;
+  if (path == FNG_PATH_SPLITN) {
+    if (!fng::splitn_feasible(M, N)) return FNG_ERR_UNSUPPORTED;
+    return fng::launch_postnorm_splitn(c, ln, as_stream(stream));
+  }
+  st = fng::launch_postnorm_partial(c, ln, as_stream(stream));
+  if (st != FNG_OK) return st;
+  return fng::launch_postnorm_finalize(Y, w.part, mean_out, rstd_out, M, N, fng::splitn_tiles_n(N),
+                                       fng::splitn_bm(), 256, eps, ln, as_stream(stream));
+}
+
+int check_attn(const void* Q, const void* K, const void* V, const void* O, int64_t B, int64_t Sq,
+               int64_t Skv, int64_t H, int64_t D) {
+  if (B < 0 || Sq < 0 || H < 0 || Skv < 1 || D < 1) return FNG_ERR_INVALID_ARG;
+  if (D != 128) return FNG_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0 || H == 0) return FNG_OK;
+  if (!Q || !K || !V || !O) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FNG_ERR_MISALIGNED;
+  // per-batch 32-bit buffer ranges (with one tile of overrun) and the grid size
+  if ((Sq + 128) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if ((Skv + 64) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if (B * H * ((Sq + 127) / 128) >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  return FNG_OK;
+}
+
+}  // namespace
+
+FNG_EXPORT int fng_version(void) { return kVersion; }
+
+FNG_EXPORT const char* fng_status_string(int status) {
+  switch (status) {
+    case FNG_OK: return "ok";
+    case FNG_ERR_INVALID_ARG: return "invalid argument";
+    case FNG_ERR_UNSUPPORTED: return "unsupported shape or path";
+    case FNG_ERR_MISALIGNED: return "misaligned pointer or dimension";
+    case FNG_ERR_WORKSPACE: return "workspace missing or too small";
+    case FNG_ERR_HIP: return "HIP runtime error";
+    case FNG_ERR_TIMEOUT: return "split-N exchange wait timed out";
+    default: return "unknown status";
+  }
+}
+
+FNG_EXPORT int64_t fng_fulln_max_n(void) { return fng::fulln_max_n(); }
+
+FNG_EXPORT size_t fng_gemm_postnorm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path) {
+  (void)K;
+  if (M <= 0 || N <= 0) return 0;
+  if (path == FNG_PATH_FULLN) return 0;
+  if (path == FNG_PATH_AUTO && N <= fng::fulln_max_n()) return 0;
+  return layout(nullptr, M, N).bytes;
+}
+
+FNG_EXPORT int fng_prenorm_rms_gemm(const void* X, const void* W, const void* gamma, void* Y,
+                                    float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
+                                    void* stream) {
+  const int st = check_gemm(X, W, Y, M, N, K, eps, true);
+  if (st != FNG_OK || m_or_n_empty(M, N)) return st;
+  if ((gamma && !aligned16(gamma)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
+  GemmCall c{X, W, gamma, Y, nullptr, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
+  return fng::launch_prenorm(c, as_stream(stream));
+}
+
+FNG_EXPORT int fng_gemm_postnorm_ln(const void* X, const void* W, void* Y, float* mean_out, float* rstd_out,
+                                    int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                                    size_t workspace_bytes, int path, void* stream) {
+  return postnorm(true, X, W, Y, mean_out, rstd_out, M, N, K, eps, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, float* rstd_out, int64_t M,
+                                     int64_t N, int64_t K, float eps, void* workspace,
+                                     size_t workspace_bytes, int path, void* stream) {
+  return postnorm(false, X, W, Y, nullptr, rstd_out, M, N, K, eps, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < 256) return FNG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, as_stream(stream)) != hipSuccess)
+    return FNG_ERR_HIP;
+  if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return FNG_ERR_HIP;
+  return word ? FNG_ERR_TIMEOUT : FNG_OK;
+}
+
+FNG_EXPORT int fng_norm_attention(const void* Q, const void* K, const void* V, void* out, float* ln_mean_out,
+                                  float* ln_rstd_out, float* rms_rstd_out, int64_t B, int64_t Sq, int64_t Skv,
+                                  int64_t H, int64_t D, float sm_scale, float eps_ln, float eps_rms,
+                                  void* stream) {
+  if (!(eps_ln > 0.f && isfinite(eps_ln)) || !(eps_rms > 0.f && isfinite(eps_rms))) return FNG_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
+  const int st = check_attn(Q, K, V, out, B, Sq, Skv, H, D);
+  if (st != FNG_OK || B == 0 || Sq == 0 || H == 0) return st;
+  fng::AttnCall c{Q, K, V, out, ln_mean_out, ln_rstd_out, rms_rstd_out, B, Sq, Skv, H, D,
+                  sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), eps_ln, eps_rms};
+  return fng::launch_attention(c, true, as_stream(stream));
+}
+
+FNG_EXPORT int fng_rmsnorm(const void* X, const void* gamma, void* Y, float* rstd_out, int64_t M, int64_t N,
+                           float eps, void* stream) {
+  if (M < 0 || N < 1 || !(eps > 0.f && isfinite(eps))) return FNG_ERR_INVALID_ARG;
+  if (M == 0) return FNG_OK;
+  if (!X || !Y) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y) || (gamma && !aligned16(gamma)) || N % 8 != 0) return FNG_ERR_MISALIGNED;
+  if (N > INT32_MAX / 4 || M > INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  return fng::launch_rownorm(X, gamma, Y, nullptr, rstd_out, M, N, eps, false, as_stream(stream));
+}
+
+FNG_EXPORT int fng_layernorm(const void* X, void* Y, float* mean_out, float* rstd_out, int64_t M, int64_t N,
+                             float eps, void* stream) {
+  if (M < 0 || N < 1 || !(eps > 0.f && isfinite(eps))) return FNG_ERR_INVALID_ARG;
+  if (M == 0) return FNG_OK;
+  if (!X || !Y) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Y) || N % 8 != 0) return FNG_ERR_MISALIGNED;
+  if (N > INT32_MAX / 4 || M > INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  return fng::launch_rownorm(X, nullptr, Y, mean_out, rstd_out, M, N, eps, true, as_stream(stream));
+}
+
+FNG_EXPORT int fng_gemm(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K, void* stream) {
+  const int st = check_gemm(X, W, Y, M, N, K, 1.f, false);
+  if (st != FNG_OK || m_or_n_empty(M, N)) return st;
+  GemmCall c{X, W, nullptr, Y, nullptr, nullptr, M, N, K, 0.f, nullptr, nullptr, nullptr, nullptr};
+  return fng::launch_gemm(c, as_stream(stream));
+}
+
+FNG_EXPORT int fng_attention(const void* Q, const void* K, const void* V, void* out, int64_t B, int64_t Sq,
+                             int64_t Skv, int64_t H, int64_t D, float sm_scale, void* stream) {
+  if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
+  const int st = check_attn(Q, K, V, out, B, Sq, Skv, H, D);
+  if (st != FNG_OK || B == 0 || Sq == 0 || H == 0) return st;
+  fng::AttnCall c{Q, K, V, out, nullptr, nullptr, nullptr, B, Sq, Skv, H, D,
+                  sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), 1e-5f, 1e-6f};
+  return fng::launch_attention(c, false, as_stream(stream));
+}

@@ -1,0 +1,130 @@
+// Device-side building blocks shared by the fng kernels (gfx950 / CDNA4).
+//
+// MFMA lane layouts used throughout (v_mfma_f32_32x32x16_{bf16,f16}):
+//   operand A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + j], j = 0..7
+//   operand B (16 x 32): lane l holds B[8 * (l / 32) + j][l % 32], j = 0..7
+//   result  D (32 x 32): lane l, register r holds
+//                        D[8 * (r / 4) + 4 * (l / 32) + (r % 4)][l % 32]
+// ds_read_b64_tr_b16: in each group of 16 lanes, lanes 4r..4r+3 address row r
+// (4 consecutive 16-bit elements each, 16 columns in total); lane i of the
+// group receives column i of rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fng {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define FNG_LDS __attribute__((address_space(3)))
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// buffer resources: hardware range checking turns out-of-range loads into 0
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword3 0x00020000: raw (untyped) 32-bit data format, as used for gfx9 buffers.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ u32x2_t buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// two fp32 -> packed fp16x2, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2_t v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// packed bf16x2 word -> packed fp16x2 word (exact for |x| in fp16 normal range)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(bf16lo(w), bf16hi(w));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_f16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// sum of squares of 8 bf16 held in a 16-byte vector, accumulated into acc with
+// fp32 FMAs (bf16 -> fp32 is exact).  The packed bf16 dot instruction is not
+// used: measured on gfx950 it does not return the fp32-accurate sum.
+__device__ __forceinline__ float sumsq_bf16x8(u32x4_t v, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = bf16lo(v[i]), b = bf16hi(v[i]);
+    acc = fmaf(a, a, acc);
+    acc = fmaf(b, b, acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// LDS access
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t lds_read16(const FNG_LDS char* p) {
+  return *reinterpret_cast<const FNG_LDS u32x4_t*>(p);
+}
+__device__ __forceinline__ void lds_write16(FNG_LDS char* p, u32x4_t v) {
+  *reinterpret_cast<FNG_LDS u32x4_t*>(p) = v;
+}
+// transposing read of 4 x 16-bit (see header comment)
+__device__ __forceinline__ u32x2_t lds_read_tr16(const FNG_LDS char* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<FNG_LDS s16x4_t*>(const_cast<FNG_LDS char*>(p)));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask); }
+__device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
+
+// ---------------------------------------------------------------------------
+// workgroup -> tile remap so that consecutive logical tiles run on one XCD.
+// Workgroups are dispatched round-robin over the 8 XCDs; slot s of XCD x
+// receives logical index x * (G / 8) + s.  A bijection on [0, G).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t wg, uint32_t G) {
+  const uint32_t per = G / 8u;
+  if (wg < per * 8u) return (wg % 8u) * per + wg / 8u;
+  return wg;
+}
+
+}  // namespace fng

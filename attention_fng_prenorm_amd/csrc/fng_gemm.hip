@@ -1,0 +1,569 @@
+// bf16 GEMM Y[M,N] = X[M,K] @ W[K,N] on gfx950 MFMA, with the normalization
+// epilogues of "Towards Free Normalization: Fusing Normalization into GEMM and
+// Attention Kernels":
+//   EPI_PLAIN    the unfused GEMM baseline
+//   EPI_PRENORM  section 2, Lazy Pre-Norm: the sum of squares of the raw X rows
+//                is accumulated beside the K loop from the X fragments already
+//                in registers for the MFMA, and rstd = 1/sqrt(ss/K + eps) is
+//                applied as a row scale in the epilogue (the row-scale
+//                commutation identity of that section).  An optional gain
+//                gamma[k] is folded into the X fragments after the statistic.
+//   EPI_FULLN    section 1, naive fusion: one workgroup's tile spans all N, the
+//                row statistics come straight from the fp32 accumulators.
+//   EPI_SPLITN   section 3, multi-CTA norm without clusters: each workgroup
+//                publishes per-row partial statistics of its N slice, the
+//                workgroups of one row block (all co-resident: persistent,
+//                cooperative launch) wait for each other, merge the partials
+//                in a fixed order and normalize their accumulators in place.
+//   EPI_PARTIAL  first kernel of the two-pass fallback: un-normalized bf16 Y
+//                plus the same per-row partials; fng_norm.hip finishes it.
+//
+// Block: 64 * WAVES_M * WAVES_N threads (4 or 8 waves).  Each wave owns a
+// (BM/WAVES_M) x (BN/WAVES_N) sub-tile built from 32x32 MFMA tiles.  The MFMA
+// is issued as D = W_frag * X_frag, so D is the transposed tile: lane l holds
+// output row m = l % 32 and 16 columns, which keeps every row reduction of the
+// norm epilogues inside a lane plus one lane-pair exchange.
+//
+// Staging: X and W tiles go HBM -> VGPR (buffer loads, out-of-range rows read
+// as 0) -> LDS, double-buffered with one barrier per K tile.  X is kept
+// [m][k] (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as
+// in memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte
+// chunks are XOR-swizzled per row so fragment reads are bank-conflict free.
+#include "fng_device.h"
+#include "fng_internal.h"
+
+namespace fng {
+
+enum : int { EPI_PLAIN = 0, EPI_PRENORM = 1, EPI_FULLN = 2, EPI_SPLITN = 3, EPI_PARTIAL = 4 };
+
+struct GemmParams {
+  const uint16_t* X;
+  const uint16_t* W;
+  const uint16_t* gamma;
+  uint16_t* Y;
+  float* mean_out;
+  float* rstd_out;
+  float* part;       // [tiles_m][tiles_n][BM][2] per-row partials (split-N, two-pass)
+  uint32_t* cnt;     // [tiles_m] arrivals (split-N)
+  uint32_t* done;    // [tiles_m] finished readers (split-N)
+  uint32_t* status;  // split-N timeout flag
+  int M, N, K;
+  float eps;
+  int tiles_m, tiles_n, total_tiles;
+  int group_m;       // row blocks per tile group (L2 locality of the tile order)
+  uint32_t spin_limit;
+};
+
+template <int BM, int BN, int BK>
+struct Smem {
+  static constexpr int A_STAGE = BM * BK * 2;
+  static constexpr int B_STAGE = BK * BN * 2;
+  static constexpr int BYTES = 2 * (A_STAGE + B_STAGE);
+};
+
+// swizzles of the 16-byte chunk index inside one LDS row
+__device__ __forceinline__ int swz_a(int row) { return row & 7; }
+__device__ __forceinline__ int swz_b(int krow) { return (krow & 3) << 1; }
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams p) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int NWAVES = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M;
+  constexpr int WN = BN / WAVES_N;
+  constexpr int FM = WM / 32;
+  constexpr int FN = WN / 32;
+  constexpr int KC = BK / 8;    // 16-byte chunks per X row of a K tile
+  constexpr int NC = BN / 8;    // 16-byte chunks per W row of a K tile
+  constexpr int A_CH = BM * KC / NT;
+  constexpr int B_CH = BK * NC / NT;
+  static_assert(NWAVES == 4 || NWAVES == 8, "4 or 8 waves per workgroup");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
+  static_assert(BK % 16 == 0 && KC <= 8, "BK in {16,32,64}");
+  static_assert(BM * KC % NT == 0 && BK * NC % NT == 0, "whole chunks per thread");
+  static_assert(NC >= 8, "BN >= 64 for the W swizzle");
+  using S = Smem<BM, BN, BK>;
+
+  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+  FNG_LDS char* lds = (FNG_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const int M = p.M, N = p.N, K = p.K;
+  const int ktiles = (K + BK - 1) / BK;
+
+  // persistent loop for split-N, one tile per workgroup otherwise
+  const uint32_t G = gridDim.x;
+  const uint32_t slot = xcd_remap(blockIdx.x, G);
+  for (int t = (int)slot; t < p.total_tiles; t += (int)G) {
+    int tm, tn;
+    if constexpr (EPI == EPI_SPLITN) {
+      tm = t / p.tiles_n;
+      tn = t % p.tiles_n;
+    } else {
+      const int per_group = p.group_m * p.tiles_n;
+      const int g = t / per_group;
+      const int first_m = g * p.group_m;
+      const int gsize = min(p.group_m, p.tiles_m - first_m);
+      const int r = t - g * per_group;
+      tm = first_m + r % gsize;
+      tn = r / gsize;
+    }
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const uint32_t xbytes = (uint32_t)min<int64_t>((int64_t)(M - m0) * K * 2, 0xffffffffLL);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X + (size_t)m0 * K, xbytes);
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(p.W + n0, (uint32_t)((int64_t)K * N * 2 - (int64_t)n0 * 2));
+    __amdgpu_buffer_rsrc_t gr;
+    if constexpr (GAMMA) gr = make_rsrc(p.gamma, (uint32_t)K * 2);
+
+    // ---- staging helpers -------------------------------------------------
+    u32x4_t ra[A_CH], rb[B_CH];
+    auto gload = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + NT * i;
+        const int row = c / KC, kc = c % KC;
+        const int k = kt * BK + kc * 8;
+        u32x4_t v = buffer_load16(xr, (uint32_t)(row * K + k) * 2u);
+        ra[i] = (k < K) ? v : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + NT * i;
+        const int krow = c / NC, nc = c % NC;
+        const int k = kt * BK + krow;
+        u32x4_t v = buffer_load16(wr, (uint32_t)(k * N + nc * 8) * 2u);
+        rb[i] = (n0 + nc * 8 < N) ? v : u32x4_t{0, 0, 0, 0};
+      }
+    };
+    auto sstore = [&](int stage) {
+      FNG_LDS char* as = lds + stage * S::A_STAGE;
+      FNG_LDS char* bs = lds + 2 * S::A_STAGE + stage * S::B_STAGE;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + NT * i;
+        const int row = c / KC, kc = c % KC;
+        lds_write16(as + row * (BK * 2) + ((kc ^ swz_a(row)) & (KC - 1)) * 16, ra[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + NT * i;
+        const int krow = c / NC, nc = c % NC;
+        lds_write16(bs + krow * (BN * 2) + (nc ^ swz_b(krow)) * 16, rb[i]);
+      }
+    };
+
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    float ss[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ss[i] = 0.f;
+
+    __syncthreads();  // previous tile's epilogue may still read LDS
+    gload(0);
+    sstore(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const int stage = kt & 1;
+      const bool more = kt + 1 < ktiles;
+      if (more) gload(kt + 1);
+      const FNG_LDS char* as = lds + stage * S::A_STAGE;
+      const FNG_LDS char* bs = lds + 2 * S::A_STAGE + stage * S::B_STAGE;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        u32x4_t xf[FM], wf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = wm * WM + 32 * i + l32;
+          const int kc = 2 * kk + hi;
+          xf[i] = lds_read16(as + row * (BK * 2) + ((kc ^ swz_a(row)) & (KC - 1)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int g = lane >> 4, li = lane & 15;
+          const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (li & 3);
+          const int nc = n >> 3, nb = (n & 7) * 2;
+          const int k0 = kk * 16 + 8 * (g >> 1) + (li >> 2);
+          const u32x2_t lo = lds_read_tr16(bs + k0 * (BN * 2) + (nc ^ swz_b(k0)) * 16 + nb);
+          const int k1 = k0 + 4;
+          const u32x2_t hi2 = lds_read_tr16(bs + k1 * (BN * 2) + (nc ^ swz_b(k1)) * 16 + nb);
+          wf[j] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+        }
+        if constexpr (EPI == EPI_PRENORM) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) ss[i] = sumsq_bf16x8(xf[i], ss[i]);
+        }
+        if constexpr (GAMMA) {
+          const int k = kt * BK + kk * 16 + 8 * hi;
+          const u32x4_t gv = buffer_load16(gr, (uint32_t)k * 2u);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              xf[i][e] = pack_bf16(bf16lo(xf[i][e]) * bf16lo(gv[e]),
+                                   bf16hi(xf[i][e]) * bf16hi(gv[e]));
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
+      }
+      if (more) sstore(stage ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogues -------------------------------------------------------
+    // lane l of wave (wm, wn) holds rows  wm*WM + 32*i + l32          (i < FM)
+    // and columns                         wn*WN + 32*j + 8*(r/4) + 4*hi + r%4
+    auto col_of = [&](int j, int r4) { return n0 + wn * WN + 32 * j + 8 * r4 + 4 * hi; };
+    auto row_of = [&](int i) { return m0 + wm * WM + 32 * i + l32; };
+
+    float rs_mean[FM], rs_rstd[FM];
+    if constexpr (EPI == EPI_PRENORM) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const float tot = xor_sum(ss[i], 32);
+        rs_mean[i] = 0.f;
+        rs_rstd[i] = __builtin_amdgcn_rsqf(tot / (float)K + p.eps);
+      }
+    }
+
+    if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN || EPI == EPI_PARTIAL) {
+      // per-row statistics of this tile's valid columns, fp32 accumulators
+      // red: [WAVES_N][BM] floats in LDS (the stage buffers are free now)
+      FNG_LDS float* red = (FNG_LDS float*)lds;
+      const int nvalid = min(BN, N - n0);
+      auto row_reduce = [&](float (&v)[FM], float (&out)[FM]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const float s = xor_sum(v[i], 32);
+          if (hi == 0) red[wn * BM + wm * WM + 32 * i + l32] = s;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < WAVES_N; ++w) s += red[w * BM + wm * WM + 32 * i + l32];
+          out[i] = s;
+        }
+        __syncthreads();
+      };
+      float part[FM], s1[FM], s2[FM];
+      if constexpr (LN) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              if (col_of(j, r4) < N)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += acc[i][j][4 * r4 + e];
+          part[i] = s;
+        }
+        row_reduce(part, s1);  // tile row sums
+        float tmean[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) tmean[i] = s1[i] / (float)nvalid;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              if (col_of(j, r4) < N)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float d = acc[i][j][4 * r4 + e] - tmean[i];
+                  s += d * d;
+                }
+          part[i] = s;
+        }
+        row_reduce(part, s2);  // tile M2 about the tile mean
+#pragma unroll
+        for (int i = 0; i < FM; ++i) s1[i] = tmean[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float s = 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              if (col_of(j, r4) < N)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s += acc[i][j][4 * r4 + e] * acc[i][j][4 * r4 + e];
+          part[i] = s;
+        }
+        row_reduce(part, s2);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) s1[i] = 0.f;
+      }
+      // s1 = tile mean (LN) / 0 (RMS); s2 = tile M2 (LN) / tile sum of squares (RMS)
+
+      if constexpr (EPI == EPI_FULLN) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          rs_mean[i] = s1[i];
+          rs_rstd[i] = __builtin_amdgcn_rsqf(s2[i] / (float)N + p.eps);
+        }
+      } else {
+        // publish partials: part[tm][tn][row][2]
+        if constexpr (EPI == EPI_PARTIAL) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) rs_mean[i] = s1[i];
+        }
+        float* pp = p.part + ((size_t)tm * p.tiles_n + tn) * (BM * 2);
+        if (wn == 0 && hi == 0) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + 32 * i + l32;
+            pp[row * 2 + 0] = s1[i];
+            pp[row * 2 + 1] = s2[i];
+          }
+        }
+        if constexpr (EPI == EPI_SPLITN) {
+          // the waves with wn == 0 wrote; each of them arrives once (release)
+          const uint32_t writers = WAVES_M;
+          if (wn == 0 && lane == 0)
+            __hip_atomic_fetch_add(p.cnt + tm, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t target = writers * (uint32_t)p.tiles_n;
+          uint32_t spins = 0;
+          while (__hip_atomic_load(p.cnt + tm, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > p.spin_limit) {
+              if (lane == 0)
+                __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+          // merge all N slices of my rows in a fixed order
+          const float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2);
+          const int nt = p.tiles_n;
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int row = wm * WM + 32 * i + l32;
+            if constexpr (LN) {
+              // Chan et al. pairwise merge of (count, mean, M2)
+              float cn = 0.f, mean = 0.f, m2 = 0.f;
+              for (int q = 0; q < nt; ++q) {
+                const float nb = (float)min(BN, N - q * BN);
+                const float mb = pb[(size_t)q * BM * 2 + row * 2 + 0];
+                const float m2b = pb[(size_t)q * BM * 2 + row * 2 + 1];
+                const float tot = cn + nb;
+                const float d = mb - mean;
+                mean += d * (nb / tot);
+                m2 += m2b + d * d * (cn * nb / tot);
+                cn = tot;
+              }
+              rs_mean[i] = mean;
+              rs_rstd[i] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
+            } else {
+              float s = 0.f;
+              for (int q = 0; q < nt; ++q) s += pb[(size_t)q * BM * 2 + row * 2 + 1];
+              rs_mean[i] = 0.f;
+              rs_rstd[i] = __builtin_amdgcn_rsqf(s / (float)N + p.eps);
+            }
+          }
+          // every wave has read; the last one resets the counters for the next call
+          if (lane == 0) {
+            const uint32_t prev =
+                __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == (uint32_t)NWAVES * (uint32_t)p.tiles_n - 1u) {
+              __hip_atomic_store(p.cnt + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+    }
+
+    // statistics outputs (one writer per row)
+    if constexpr (EPI == EPI_PRENORM || EPI == EPI_FULLN || EPI == EPI_SPLITN) {
+      if (tn == 0 && wn == 0 && hi == 0) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int m = row_of(i);
+          if (m < M) {
+            if (p.rstd_out) p.rstd_out[m] = rs_rstd[i];
+            if constexpr (LN)
+              if (p.mean_out) p.mean_out[m] = rs_mean[i];
+          }
+        }
+      }
+    }
+
+    // ---- store bf16 -----------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = row_of(i);
+      if (m >= M) continue;
+      uint16_t* yrow = p.Y + (size_t)m * N;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int n = col_of(j, r4);
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float a = acc[i][j][4 * r4 + e];
+            if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
+            if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
+            // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
+            // mean, so rows whose mean dwarfs their spread keep their precision
+            if constexpr (EPI == EPI_PARTIAL && LN) a -= rs_mean[i];
+            v[e] = a;
+          }
+          *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side: configurations and launch
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
+int launch(const GemmParams& p0, int grid, bool cooperative, hipStream_t stream) {
+  GemmParams p = p0;
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;
+  p.total_tiles = p.tiles_m * p.tiles_n;
+  auto kern = gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, EPI, LN, GAMMA>;
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  if (grid <= 0) grid = p.total_tiles;
+  if (cooperative) {
+    void* args[] = {&p};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(NT), args, 0,
+                                   stream) != hipSuccess)
+      return FNG_ERR_HIP;
+  } else {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, stream, p);
+  }
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
+int max_coresident_grid() {
+  int per_cu = 0, dev = 0, cus = 0;
+  auto kern = gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, EPI, LN, GAMMA>;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                   64 * WAVES_M * WAVES_N, 0) !=
+      hipSuccess)
+    return -1;
+  return per_cu * cus;
+}
+
+GemmParams base_params(const GemmCall& c) {
+  GemmParams p{};
+  p.X = static_cast<const uint16_t*>(c.X);
+  p.W = static_cast<const uint16_t*>(c.W);
+  p.gamma = static_cast<const uint16_t*>(c.gamma);
+  p.Y = static_cast<uint16_t*>(c.Y);
+  p.mean_out = c.mean_out;
+  p.rstd_out = c.rstd_out;
+  p.M = (int)c.M;
+  p.N = (int)c.N;
+  p.K = (int)c.K;
+  p.eps = c.eps;
+  p.group_m = 4;
+  p.spin_limit = 1u << 22;
+  return p;
+}
+
+// tile choice for the MFMA-bound mainloop (large M and N)
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigWM = 2, kBigWN = 4;
+
+bool small_problem(const GemmCall& c) { return c.M * c.N <= 256LL * 256 * 64; }
+
+}  // namespace
+
+// split-N geometry shared with the workspace size computation
+int64_t splitn_tiles_m(int64_t M) { return (M + kBigBM - 1) / kBigBM; }
+int64_t splitn_tiles_n(int64_t N) { return (N + kBigBN - 1) / kBigBN; }
+int64_t splitn_bm() { return kBigBM; }
+int64_t fulln_max_n() { return 256; }
+
+int launch_gemm(const GemmCall& c, hipStream_t s) {
+  GemmParams p = base_params(c);
+  if (small_problem(c)) return launch<64, 64, 64, 2, 2, EPI_PLAIN, false, false>(p, 0, false, s);
+  return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PLAIN, false, false>(p, 0, false, s);
+}
+
+int launch_prenorm(const GemmCall& c, hipStream_t s) {
+  GemmParams p = base_params(c);
+  const bool g = c.gamma != nullptr;
+  if (small_problem(c)) {
+    return g ? launch<64, 64, 64, 2, 2, EPI_PRENORM, false, true>(p, 0, false, s)
+             : launch<64, 64, 64, 2, 2, EPI_PRENORM, false, false>(p, 0, false, s);
+  }
+  return g ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, true>(p, 0, false, s)
+           : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, false>(p, 0, false, s);
+}
+
+int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
+  GemmParams p = base_params(c);
+  // one workgroup spans all N (<= 256): 32 rows x 256 columns, waves side by side along N
+  return ln ? launch<32, 256, 64, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
+            : launch<32, 256, 64, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
+}
+
+int splitn_feasible(int64_t M, int64_t N) {
+  const int cap = max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>();
+  if (cap <= 0) return 0;
+  return splitn_tiles_n(N) <= cap ? 1 : 0;
+}
+
+int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
+  GemmParams p = base_params(c);
+  p.part = static_cast<float*>(c.part);
+  p.cnt = c.cnt;
+  p.done = c.done;
+  p.status = c.status;
+  const int cap = ln ? max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>()
+                     : max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>();
+  const int tn = (int)splitn_tiles_n(c.N);
+  const int total = (int)(splitn_tiles_m(c.M) * tn);
+  if (cap <= 0 || tn > cap) return FNG_ERR_UNSUPPORTED;
+  // a whole number of row blocks per round, so every wait is on a co-resident peer
+  int grid = (cap / tn) * tn;
+  if (grid > total) grid = total;
+  return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>(p, grid, true, s)
+            : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>(p, grid, true, s);
+}
+
+int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s) {
+  GemmParams p = base_params(c);
+  p.part = static_cast<float*>(c.part);
+  return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PARTIAL, true, false>(p, 0, false, s)
+            : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PARTIAL, false, false>(p, 0, false, s);
+}
+
+}  // namespace fng

@@ -1,0 +1,61 @@
+// Internal interface between the C ABI (fng_api.cpp) and the kernel files.
+// Arguments reaching these launchers have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fng.h"
+
+namespace fng {
+
+struct GemmCall {
+  const void* X;
+  const void* W;
+  const void* gamma;  // bf16 [K] or nullptr
+  void* Y;
+  float* mean_out;
+  float* rstd_out;
+  int64_t M, N, K;
+  float eps;
+  void* part;         // split-N / two-pass partials
+  uint32_t* cnt;
+  uint32_t* done;
+  uint32_t* status;
+};
+
+// fng_gemm.hip
+int launch_gemm(const GemmCall& c, hipStream_t s);
+int launch_prenorm(const GemmCall& c, hipStream_t s);
+int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s);
+int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s);
+int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s);
+int splitn_feasible(int64_t M, int64_t N);
+int64_t splitn_tiles_m(int64_t M);
+int64_t splitn_tiles_n(int64_t N);
+int64_t splitn_bm();
+int64_t fulln_max_n();
+
+// fng_norm.hip
+int launch_rownorm(const void* X, const void* gamma, void* Y, float* mean_out, float* rstd_out,
+                   int64_t M, int64_t N, float eps, bool ln, hipStream_t s);
+// second pass of the two-pass post-norm: merge per-tile partials, normalize Y in place
+int launch_postnorm_finalize(void* Y, const void* part, float* mean_out, float* rstd_out,
+                             int64_t M, int64_t N, int64_t tiles_n, int64_t bm, int64_t bn,
+                             float eps, bool ln, hipStream_t s);
+
+// fng_attention.hip
+struct AttnCall {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* ln_mean_out;
+  float* ln_rstd_out;
+  float* rms_rstd_out;
+  int64_t B, Sq, Skv, H, D;
+  float sm_scale, eps_ln, eps_rms;
+};
+int launch_attention(const AttnCall& c, bool norm, hipStream_t s);
+
+}  // namespace fng

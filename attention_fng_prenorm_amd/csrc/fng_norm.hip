@@ -1,0 +1,273 @@
+// Standalone row normalizations (the unfused baseline the fusions replace) and
+// the second kernel of the two-pass post-norm fallback.
+//
+// "Towards Free Normalization: Fusing Normalization into GEMM and Attention
+// Kernels", section 1: a norm kernel tiles only the outer dimension and loads
+// whole rows.  Here a group of LPR lanes owns one row, each lane holding CPL
+// 16-byte chunks in registers, so the row is read from HBM once and written
+// once.  Statistics are fp32; LayerNorm is two-pass over the registers
+// (mean, then the sum of squared deviations), RMSNorm divides the sum of
+// squares by the row length; eps is inside the square root.
+#include "fng_device.h"
+#include "fng_internal.h"
+
+namespace fng {
+
+struct RowNormParams {
+  const uint16_t* X;
+  const uint16_t* gamma;
+  uint16_t* Y;
+  float* mean_out;
+  float* rstd_out;
+  int64_t M;
+  int N;
+  float eps;
+};
+
+template <int LPR, int CPL, bool LN, bool GAMMA>
+__global__ __launch_bounds__(256) void rownorm_kernel(RowNormParams p) {
+  constexpr int RPB = 256 / LPR;  // rows per block
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const bool valid = row < p.M;
+  const int N = p.N;
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(p.X + (valid ? row : 0) * (int64_t)N, valid ? (uint32_t)N * 2u : 0u);
+
+  u32x4_t v[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) v[c] = buffer_load16(xr, (uint32_t)((c * LPR + sub) * 16));
+
+  float s = 0.f;
+  float mean = 0.f;
+  if constexpr (LN) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += bf16lo(v[c][e]) + bf16hi(v[c][e]);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) s = xor_sum(s, m);
+    mean = s / (float)N;
+    s = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      if ((c * LPR + sub) * 8 < N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16lo(v[c][e]) - mean, b = bf16hi(v[c][e]) - mean;
+          s += a * a + b * b;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s = sumsq_bf16x8(v[c], s);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) s = xor_sum(s, m);
+  const float rstd = __builtin_amdgcn_rsqf(s / (float)N + p.eps);
+
+  if (!valid) return;
+  if (sub == 0) {
+    if (p.rstd_out) p.rstd_out[row] = rstd;
+    if constexpr (LN)
+      if (p.mean_out) p.mean_out[row] = mean;
+  }
+  __amdgpu_buffer_rsrc_t gr;
+  if constexpr (GAMMA) gr = make_rsrc(p.gamma, (uint32_t)N * 2u);
+  uint16_t* y = p.Y + row * (int64_t)N;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int col = (c * LPR + sub) * 8;
+    if (col >= N) continue;
+    u32x4_t o;
+    u32x4_t g;
+    if constexpr (GAMMA) g = buffer_load16(gr, (uint32_t)col * 2u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float a = (bf16lo(v[c][e]) - mean) * rstd;
+      float b = (bf16hi(v[c][e]) - mean) * rstd;
+      if constexpr (GAMMA) {
+        a *= bf16lo(g[e]);
+        b *= bf16hi(g[e]);
+      }
+      o[e] = pack_bf16(a, b);
+    }
+    *reinterpret_cast<u32x4_t*>(y + col) = o;
+  }
+}
+
+// rows longer than the register-resident variants: one block per row, the row
+// is read twice (statistics, then normalize)
+template <bool LN, bool GAMMA>
+__global__ __launch_bounds__(256) void rownorm_long_kernel(RowNormParams p) {
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int N = p.N;
+  const uint16_t* x = p.X + row * (int64_t)N;
+  uint16_t* y = p.Y + row * (int64_t)N;
+  __shared__ float red[4];
+  auto block_sum = [&](float v) {
+    for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+  };
+  float mean = 0.f;
+  if constexpr (LN) {
+    float s = 0.f;
+    for (int col = tid * 8; col < N; col += 256 * 8) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + col);
+      for (int e = 0; e < 4; ++e) s += bf16lo(v[e]) + bf16hi(v[e]);
+    }
+    mean = block_sum(s) / (float)N;
+  }
+  float s = 0.f;
+  for (int col = tid * 8; col < N; col += 256 * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + col);
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16lo(v[e]) - mean, b = bf16hi(v[e]) - mean;
+      s += a * a + b * b;
+    }
+  }
+  const float rstd = __builtin_amdgcn_rsqf(block_sum(s) / (float)N + p.eps);
+  if (tid == 0) {
+    if (p.rstd_out) p.rstd_out[row] = rstd;
+    if constexpr (LN)
+      if (p.mean_out) p.mean_out[row] = mean;
+  }
+  // all reads of this row finish before any write (Y may alias X)
+  __syncthreads();
+  for (int col = tid * 8; col < N; col += 256 * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + col);
+    u32x4_t g = {0, 0, 0, 0};
+    if constexpr (GAMMA) g = *reinterpret_cast<const u32x4_t*>(p.gamma + col);
+    u32x4_t o;
+    for (int e = 0; e < 4; ++e) {
+      float a = (bf16lo(v[e]) - mean) * rstd, b = (bf16hi(v[e]) - mean) * rstd;
+      if constexpr (GAMMA) {
+        a *= bf16lo(g[e]);
+        b *= bf16hi(g[e]);
+      }
+      o[e] = pack_bf16(a, b);
+    }
+    *reinterpret_cast<u32x4_t*>(y + col) = o;
+  }
+}
+
+namespace {
+
+template <int LPR, int CPL, bool LN>
+int go(const RowNormParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / LPR;
+  const int64_t grid = (p.M + RPB - 1) / RPB;
+  if (p.gamma)
+    hipLaunchKernelGGL((rownorm_kernel<LPR, CPL, LN, true>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((rownorm_kernel<LPR, CPL, LN, false>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+template <bool LN>
+int dispatch(const RowNormParams& p, hipStream_t s) {
+  const int N = p.N;
+  if (N <= 128) return go<16, 1, LN>(p, s);
+  if (N <= 256) return go<32, 1, LN>(p, s);
+  if (N <= 512) return go<64, 1, LN>(p, s);
+  if (N <= 1024) return go<64, 2, LN>(p, s);
+  if (N <= 2048) return go<64, 4, LN>(p, s);
+  if (N <= 4096) return go<64, 8, LN>(p, s);
+  if (N <= 8192) return go<64, 16, LN>(p, s);
+  if (p.gamma)
+    hipLaunchKernelGGL((rownorm_long_kernel<LN, true>), dim3((unsigned)p.M), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((rownorm_long_kernel<LN, false>), dim3((unsigned)p.M), dim3(256), 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_rownorm(const void* X, const void* gamma, void* Y, float* mean_out, float* rstd_out,
+                   int64_t M, int64_t N, float eps, bool ln, hipStream_t s) {
+  RowNormParams p{static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(gamma),
+                  static_cast<uint16_t*>(Y), mean_out, rstd_out, M, (int)N, eps};
+  return ln ? dispatch<true>(p, s) : dispatch<false>(p, s);
+}
+
+// ---------------------------------------------------------------------------
+// two-pass post-norm, second kernel: one wave per row merges the per-tile
+// partials (fixed order; Chan et al. pairwise (count, mean, M2) merge for
+// LayerNorm, plain sum of squares for RMSNorm) and normalizes the row of Y
+// in place.
+// ---------------------------------------------------------------------------
+struct FinalizeParams {
+  uint16_t* Y;
+  const float* part;  // [tiles_m][tiles_n][bm][2]
+  float* mean_out;
+  float* rstd_out;
+  int64_t M;
+  int N, tiles_n, bm, bn;
+  float eps;
+};
+
+template <bool LN>
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.M) return;
+  const int64_t tm = row / p.bm;
+  const int r = (int)(row % p.bm);
+  const float* pb = p.part + (size_t)tm * p.tiles_n * p.bm * 2;
+  float mean = 0.f, rstd;
+  if constexpr (LN) {
+    float cn = 0.f, m2 = 0.f;
+    for (int q = 0; q < p.tiles_n; ++q) {
+      const float nb = (float)min(p.bn, p.N - q * p.bn);
+      const float mb = pb[((size_t)q * p.bm + r) * 2 + 0];
+      const float m2b = pb[((size_t)q * p.bm + r) * 2 + 1];
+      const float tot = cn + nb;
+      const float d = mb - mean;
+      mean += d * (nb / tot);
+      m2 += m2b + d * d * (cn * nb / tot);
+      cn = tot;
+    }
+    rstd = __builtin_amdgcn_rsqf(m2 / (float)p.N + p.eps);
+  } else {
+    float s = 0.f;
+    for (int q = 0; q < p.tiles_n; ++q) s += pb[((size_t)q * p.bm + r) * 2 + 1];
+    rstd = __builtin_amdgcn_rsqf(s / (float)p.N + p.eps);
+  }
+  if (lane == 0) {
+    if (p.rstd_out) p.rstd_out[row] = rstd;
+    if constexpr (LN)
+      if (p.mean_out) p.mean_out[row] = mean;
+  }
+  uint16_t* y = p.Y + row * (int64_t)p.N;
+  for (int col = lane * 8; col < p.N; col += 64 * 8) {
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + col);
+    // LayerNorm intermediates were stored minus their tile mean
+    float shift = -mean;
+    if constexpr (LN) shift = pb[((size_t)(col / p.bn) * p.bm + r) * 2 + 0] - mean;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = pack_bf16((bf16lo(v[e]) + shift) * rstd, (bf16hi(v[e]) + shift) * rstd);
+    *reinterpret_cast<u32x4_t*>(y + col) = v;
+  }
+}
+
+int launch_postnorm_finalize(void* Y, const void* part, float* mean_out, float* rstd_out, int64_t M,
+                             int64_t N, int64_t tiles_n, int64_t bm, int64_t bn, float eps, bool ln,
+                             hipStream_t s) {
+  FinalizeParams p{static_cast<uint16_t*>(Y), static_cast<const float*>(part), mean_out, rstd_out, M,
+                   (int)N, (int)tiles_n, (int)bm, (int)bn, eps};
+  const int64_t grid = (M + 3) / 4;
+  if (ln)
+    hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(finalize_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+}  // namespace fng

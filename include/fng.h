@@ -1,0 +1,162 @@
+/*
+ * fng.h - C ABI of libfng.so: normalization fused into bf16 GEMM and attention
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "Towards Free Normalization: Fusing Normalization into
+ * GEMM and Attention Kernels" (PyTorch blog):
+ *   - section 2 (Lazy Pre-Norm): C = rmsnorm(A) @ B with the row statistic
+ *     accumulated during the K loop and applied as an epilogue row scale;
+ *   - sections 1 and 3 (naive full-N fusion, multi-CTA norm): C = norm(A @ B),
+ *     LayerNorm or RMSNorm over each output row;
+ *   - section 4 (FlashNormAttention): LayerNorm of the queries before the
+ *     attention product and RMSNorm of its output after it.
+ * Plus the unfused baselines those fusions replace (row norms, plain GEMM,
+ * plain attention).
+ *
+ * Conventions for every entry point
+ *   - Tensors are caller-owned device memory on the current HIP device,
+ *     row-major and contiguous.  bf16 tensors are raw 16-bit bfloat16 bit
+ *     patterns.  Statistics outputs are fp32.
+ *   - Matrices: X is [M, K], W is [K, N] (N contiguous), Y is [M, N].
+ *   - Attention tensors are [B, S, H, D] (D contiguous).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; no call synchronizes except fng_get_kernel_status.
+ *   - Every call validates its arguments first and returns a status.  No call
+ *     throws, prints, aborts or allocates device memory.  A failed validation
+ *     enqueues nothing.
+ *   - Inputs are never written.  Outputs are fully overwritten.  Outputs must
+ *     not alias inputs, except Y == X for fng_rmsnorm / fng_layernorm.
+ *   - Preconditions (checked): base pointers 16-byte aligned; for GEMM entry
+ *     points K % 8 == 0 and N % 8 == 0 (rows are whole 16-byte vectors), K >= 1;
+ *     for attention D == 128 and Skv >= 1; eps > 0.  M, N (GEMM) and B, Sq, H
+ *     (attention) may be 0, which enqueues nothing and returns FNG_OK.  Tile
+ *     tails in M, N, K and Sq, Skv are masked inside the kernels.
+ *   - Optional outputs (rstd_out, mean_out, ...) may be NULL.
+ *   - Accumulation and statistics are fp32; outputs are rounded to bf16 with
+ *     round-to-nearest-even.
+ */
+#ifndef FNG_H
+#define FNG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FNG_OK = 0,
+  FNG_ERR_INVALID_ARG = 1, /* NULL required pointer, negative size, eps <= 0, ... */
+  FNG_ERR_UNSUPPORTED = 2, /* shape outside what the kernels implement (e.g. D != 128) */
+  FNG_ERR_MISALIGNED = 3,  /* pointer not 16-byte aligned, or K/N not a multiple of 8 */
+  FNG_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than *_workspace_bytes() */
+  FNG_ERR_HIP = 5,         /* the HIP runtime reported an error for a launch */
+  FNG_ERR_TIMEOUT = 6      /* a split-N exchange wait hit its bound (see below) */
+} fng_status;
+
+/* How a post-norm GEMM reduces statistics over N. */
+typedef enum {
+  FNG_PATH_AUTO = 0,    /* FULLN when N fits one workgroup, else SPLITN, else TWOPASS */
+  FNG_PATH_FULLN = 1,   /* one workgroup owns whole output rows (section 1's naive
+                           fusion); requires N <= fng_fulln_max_n() */
+  FNG_PATH_SPLITN = 2,  /* N split over co-resident workgroups that exchange per-row
+                           partial statistics through the workspace (section 3's
+                           multi-CTA norm, without clusters) */
+  FNG_PATH_TWOPASS = 3  /* GEMM kernel stores un-normalized bf16 Y plus partial
+                           statistics, a second kernel normalizes Y in place
+                           (the unfused IO the fusion removes; comparison/fallback) */
+} fng_path;
+
+/* ---------------------------------------------------------------------------
+ * Lazy pre-RMSNorm GEMM (section 2, "Lazy Pre-Norm", the kernel pseudocode and
+ * the row-scale commutation identity):
+ *   rstd[m] = 1 / sqrt(mean_k X[m,k]^2 + eps)
+ *   Y[m,n]  = rstd[m] * sum_k X[m,k] * gamma[k] * W[k,n]
+ * i.e. Y = rmsnorm(X) * gamma @ W.  The statistic uses the raw X; gamma (bf16,
+ * [K], optional: NULL means no affine) multiplies along K inside the product.
+ * rstd_out: optional fp32 [M].
+ * ------------------------------------------------------------------------- */
+int fng_prenorm_rms_gemm(const void* X, const void* W, const void* gamma, void* Y,
+                         float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * GEMM + post-norm (section 1 naive fusion and section 3 multi-CTA norm):
+ *   Z = X @ W  (fp32 accumulation);  Y = norm(Z) over each row of N,
+ * LayerNorm: Y = (Z - mean) / sqrt(var + eps), biased variance, no affine;
+ * RMSNorm:   Y = Z / sqrt(mean(Z^2) + eps), no affine.
+ * Statistics come from the fp32 accumulator, before the bf16 rounding.
+ * mean_out (LN only) and rstd_out: optional fp32 [M].
+ *
+ * workspace: caller-owned device memory of at least
+ * fng_gemm_postnorm_workspace_bytes(M, N, K, path) bytes, zero-filled ONCE
+ * when allocated; the kernels leave it zeroed again for the next call.  It may
+ * be NULL only when that size is 0.  Calls sharing one workspace must be
+ * ordered (same stream).  If a call reports FNG_ERR_TIMEOUT through
+ * fng_get_kernel_status, its Y is invalid and the workspace must be
+ * zero-filled again.
+ * ------------------------------------------------------------------------- */
+size_t fng_gemm_postnorm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path);
+int64_t fng_fulln_max_n(void);
+
+int fng_gemm_postnorm_ln(const void* X, const void* W, void* Y, float* mean_out,
+                         float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
+                         void* workspace, size_t workspace_bytes, int path, void* stream);
+
+int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, float* rstd_out,
+                          int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                          size_t workspace_bytes, int path, void* stream);
+
+/* Reads the status word a split-N call leaves in `workspace` (synchronizes
+ * `stream`).  Returns FNG_OK, FNG_ERR_TIMEOUT, or a validation/HIP error. */
+int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Norm-sandwiched attention (section 4, FlashNormAttention, in its per-head,
+ * softmax, no-residual form):
+ *   for each (b, h):  q^ = layernorm(Q[b,:,h,:]) over D   (eps_ln, no affine)
+ *                     P  = softmax(q^ K[b,:,h,:]^T * sm_scale) over all keys
+ *                     O  = P V[b,:,h,:]
+ *                     out[b,:,h,:] = rmsnorm(O) over D    (eps_rms, no affine)
+ * Q, out: [B, Sq, H, D]; K, V: [B, Skv, H, D]; D must be 128.  Non-causal.
+ * sm_scale <= 0 selects 1/sqrt(D).  Optional fp32 [B, Sq, H] statistics outputs.
+ * K and V magnitudes must be below 65504 (the kernel multiplies in fp16 with
+ * fp32 accumulation; bf16 inputs in that range convert to fp16 exactly down to
+ * 2^-14).
+ * ------------------------------------------------------------------------- */
+int fng_norm_attention(const void* Q, const void* K, const void* V, void* out,
+                       float* ln_mean_out, float* ln_rstd_out, float* rms_rstd_out,
+                       int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                       float sm_scale, float eps_ln, float eps_rms, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Unfused baselines (the separate kernels the fusions replace; section 1
+ * describes the standalone row norm that loads whole rows).
+ * ------------------------------------------------------------------------- */
+/* Y = rmsnorm(X) * gamma over rows of length N; gamma bf16 [N] or NULL. */
+int fng_rmsnorm(const void* X, const void* gamma, void* Y, float* rstd_out, int64_t M,
+                int64_t N, float eps, void* stream);
+/* Y = layernorm(X) over rows of length N (biased variance, no affine). */
+int fng_layernorm(const void* X, void* Y, float* mean_out, float* rstd_out, int64_t M,
+                  int64_t N, float eps, void* stream);
+/* Y = X @ W in bf16 with fp32 accumulation (same mainloop as the fused GEMMs). */
+int fng_gemm(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
+             void* stream);
+/* out = softmax(Q K^T * sm_scale) V, BSHD, D == 128, same kernel as
+ * fng_norm_attention without the two norms. */
+int fng_attention(const void* Q, const void* K, const void* V, void* out, int64_t B,
+                  int64_t Sq, int64_t Skv, int64_t H, int64_t D, float sm_scale,
+                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Misc.
+ * ------------------------------------------------------------------------- */
+const char* fng_status_string(int status);
+int fng_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FNG_H */

@@ -1,0 +1,152 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/fng.h declares, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_fng_prenorm_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fng.h")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fng_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for must in ("fng_prenorm_rms_gemm", "fng_gemm_postnorm_ln", "fng_gemm_postnorm_rms",
+                 "fng_norm_attention", "fng_rmsnorm", "fng_layernorm", "fng_gemm", "fng_attention"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), f"{name} not exported"
+    # and the binding wraps each of them under the same name
+    assert sorted(B.SIGNATURES) == declared_symbols()
+    for name in declared_symbols():
+        assert callable(getattr(B, name))
+
+
+def test_only_fng_symbols_are_exported():
+    # the dynamic symbol table should not leak internal C++ names
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    funcs = [ln.split()[-1] for ln in out.splitlines() if " T " in ln]
+    assert funcs, "no exported functions"
+    leaked = [f for f in funcs if not f.startswith("fng_") and not f.startswith("_init")
+              and not f.startswith("_fini")]
+    assert not leaked, leaked[:10]
+
+
+def test_version_and_status_strings():
+    assert B.fng_version() >= 1
+    assert B.fng_status_string(0) == "ok"
+    for s in range(1, 7):
+        assert B.fng_status_string(s) not in ("ok", "unknown status")
+    assert B.fng_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert B.fng_gemm_postnorm_workspace_bytes(8192, 256, 256, B.FNG_PATH_AUTO) == 0
+    assert B.fng_gemm_postnorm_workspace_bytes(8192, 256, 256, B.FNG_PATH_FULLN) == 0
+    n = B.fng_gemm_postnorm_workspace_bytes(16384, 4096, 1024, B.FNG_PATH_SPLITN)
+    # status + two counter arrays + 64 row blocks x 16 slices x 256 rows x 2 floats
+    assert n >= 64 * 16 * 256 * 2 * 4
+    assert B.fng_gemm_postnorm_workspace_bytes(0, 4096, 1024, B.FNG_PATH_SPLITN) == 0
+    assert B.fng_fulln_max_n() >= 256
+
+
+# raw C calls with arguments that validation must reject -------------------
+L = None
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+MIS = 0x10008   # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.lib()
+
+
+def test_prenorm_validation(lib):
+    f = lib.fng_prenorm_rms_gemm
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 0, 1e-6, None) == B.FNG_ERR_INVALID_ARG   # K = 0
+    assert f(FAKE, FAKE, None, FAKE, None, -1, 8, 8, 1e-6, None) == B.FNG_ERR_INVALID_ARG  # M < 0
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 8, 0.0, None) == B.FNG_ERR_INVALID_ARG    # eps = 0
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 8, float("nan"), None) == B.FNG_ERR_INVALID_ARG
+    assert f(None, FAKE, None, FAKE, None, 4, 8, 8, 1e-6, None) == B.FNG_ERR_INVALID_ARG   # NULL X
+    assert f(MIS, FAKE, None, FAKE, None, 4, 8, 8, 1e-6, None) == B.FNG_ERR_MISALIGNED
+    assert f(FAKE, FAKE, MIS, FAKE, None, 4, 8, 8, 1e-6, None) == B.FNG_ERR_MISALIGNED     # gamma
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 12, 1e-6, None) == B.FNG_ERR_MISALIGNED   # K % 8
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 12, 8, 1e-6, None) == B.FNG_ERR_MISALIGNED   # N % 8
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 1 << 20, 1 << 14, 1e-6, None) == B.FNG_ERR_UNSUPPORTED
+    # empty problems are a successful no-op (nothing is enqueued)
+    assert f(None, None, None, None, None, 0, 8, 8, 1e-6, None) == B.FNG_OK
+    assert f(None, None, None, None, None, 4, 0, 8, 1e-6, None) == B.FNG_OK
+
+
+def test_postnorm_validation(lib):
+    for f, ln in ((lib.fng_gemm_postnorm_ln, True), (lib.fng_gemm_postnorm_rms, False)):
+        def call(X, W, Y, M, N, K, eps, ws, wsb, path):
+            if ln:
+                return f(X, W, Y, None, None, M, N, K, eps, ws, wsb, path, None)
+            return f(X, W, Y, None, M, N, K, eps, ws, wsb, path, None)
+        assert call(FAKE, FAKE, FAKE, 4, 8, 8, -1.0, None, 0, 0) == B.FNG_ERR_INVALID_ARG
+        assert call(FAKE, FAKE, FAKE, 4, 8, 8, 1e-5, None, 0, 7) == B.FNG_ERR_INVALID_ARG     # bad path
+        assert call(FAKE, FAKE, FAKE, 4, 8, 10, 1e-5, None, 0, 0) == B.FNG_ERR_MISALIGNED
+        # full-N path cannot take N above its limit
+        assert call(FAKE, FAKE, FAKE, 4, 4096, 8, 1e-5, None, 0, B.FNG_PATH_FULLN) == B.FNG_ERR_UNSUPPORTED
+        # two-pass and split-N need the workspace
+        assert call(FAKE, FAKE, FAKE, 4, 4096, 8, 1e-5, None, 0, B.FNG_PATH_TWOPASS) == B.FNG_ERR_WORKSPACE
+        assert call(FAKE, FAKE, FAKE, 4, 4096, 8, 1e-5, FAKE, 64, B.FNG_PATH_TWOPASS) == B.FNG_ERR_WORKSPACE
+        assert call(FAKE, FAKE, FAKE, 4, 4096, 8, 1e-5, MIS, 1 << 30, B.FNG_PATH_TWOPASS) == B.FNG_ERR_MISALIGNED
+        assert call(None, None, None, 0, 4096, 8, 1e-5, None, 0, B.FNG_PATH_SPLITN) == B.FNG_OK
+
+
+def test_attention_validation(lib):
+    na = lib.fng_norm_attention
+    a = lib.fng_attention
+    args = (FAKE, FAKE, FAKE, FAKE)
+    assert na(*args, None, None, None, 1, 8, 8, 2, 64, 0.0, 1e-5, 1e-6, None) == B.FNG_ERR_UNSUPPORTED
+    assert na(*args, None, None, None, 1, 8, 0, 2, 128, 0.0, 1e-5, 1e-6, None) == B.FNG_ERR_INVALID_ARG
+    assert na(*args, None, None, None, 1, 8, 8, 2, 128, 0.0, 0.0, 1e-6, None) == B.FNG_ERR_INVALID_ARG
+    assert na(*args, None, None, None, 1, 8, 8, 2, 128, float("inf"), 1e-5, 1e-6, None) == B.FNG_ERR_INVALID_ARG
+    assert na(MIS, FAKE, FAKE, FAKE, None, None, None, 1, 8, 8, 2, 128, 0.0, 1e-5, 1e-6, None) == B.FNG_ERR_MISALIGNED
+    assert na(None, FAKE, FAKE, FAKE, None, None, None, 1, 8, 8, 2, 128, 0.0, 1e-5, 1e-6, None) == B.FNG_ERR_INVALID_ARG
+    assert na(None, None, None, None, None, None, None, 0, 8, 8, 2, 128, 0.0, 1e-5, 1e-6, None) == B.FNG_OK
+    assert a(*args, 1, 8, 8, 2, 96, 0.0, None) == B.FNG_ERR_UNSUPPORTED
+    assert a(*args, 1, 1 << 22, 8, 64, 128, 0.0, None) == B.FNG_ERR_UNSUPPORTED
+    assert a(None, None, None, None, 2, 0, 8, 2, 128, 0.0, None) == B.FNG_OK
+
+
+def test_norm_and_gemm_validation(lib):
+    assert lib.fng_rmsnorm(FAKE, None, FAKE, None, 4, 12, 1e-6, None) == B.FNG_ERR_MISALIGNED
+    assert lib.fng_rmsnorm(FAKE, None, FAKE, None, 4, 0, 1e-6, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_rmsnorm(FAKE, None, FAKE, None, 4, 8, 0.0, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_rmsnorm(None, None, None, None, 0, 8, 1e-6, None) == B.FNG_OK
+    assert lib.fng_layernorm(MIS, FAKE, None, None, 4, 8, 1e-5, None) == B.FNG_ERR_MISALIGNED
+    assert lib.fng_layernorm(None, FAKE, None, None, 4, 8, 1e-5, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_gemm(FAKE, FAKE, FAKE, 4, 8, 0, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_gemm(FAKE, FAKE, MIS, 4, 8, 8, None) == B.FNG_ERR_MISALIGNED
+    assert lib.fng_gemm(None, None, None, 0, 8, 8, None) == B.FNG_OK
+
+
+def test_get_kernel_status_validation(lib):
+    assert lib.fng_get_kernel_status(None, 0, None) == B.FNG_ERR_WORKSPACE
+    assert lib.fng_get_kernel_status(FAKE, 16, None) == B.FNG_ERR_WORKSPACE
+    assert lib.fng_get_kernel_status(MIS, 4096, None) == B.FNG_ERR_MISALIGNED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.fng_gemm(x, torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(4, 8, dtype=torch.bfloat16))
