@@ -54,20 +54,67 @@ struct GemmParams {
   uint32_t spin_limit;
 };
 
-template <int BM, int BN, int BK>
+template <int BM, int BN, int BK, int STAGES, bool GAMMA>
 struct Smem {
   static constexpr int A_STAGE = BM * BK * 2;
   static constexpr int B_STAGE = BK * BN * 2;
-  static constexpr int BYTES = 2 * (A_STAGE + B_STAGE);
+  static constexpr int G_STAGE = GAMMA ? 256 : 0;  // gamma slice of the K tile
+  static constexpr int STAGE = A_STAGE + B_STAGE + G_STAGE;
+  static constexpr int BYTES = STAGES * STAGE;
 };
 
 // swizzles of the 16-byte chunk index inside one LDS row
-__device__ __forceinline__ int swz_a(int row) { return row & 7; }
+//   X rows (BK*2 bytes): XOR with row bits so that 8 consecutive rows read by a
+//   fragment load land in distinct banks;
+//   W rows (BN*2 bytes): XOR with 2*(k % 4) so the 4 rows of a transposing read
+//   land in distinct 32-byte slots.
+template <int KC>
+__device__ __forceinline__ int swz_a(int row) {
+  if constexpr (KC >= 8) return row & 7;
+  else return ((row >> 1) ^ row) & (KC - 1);
+}
 __device__ __forceinline__ int swz_b(int krow) { return (krow & 3) << 1; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only (global copies are waited for explicitly with wait_vmcnt), and is a
+// compiler memory barrier
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
+// writes LDS bytes [base + 16 l, +16).  Written as inline asm so that the
+// compiler does not model the LDS write: it would otherwise wait for every
+// copy in flight before each LDS read.  The ring's explicit vmcnt waits and
+// barriers are the synchronization.  The descriptor words and the LDS base
+// are wave-uniform scalars.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                 (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffff),
+                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4_t rsrc, const FNG_LDS char* lds_wave_base, uint32_t off) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer range: DMA writes zeros
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams p) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
@@ -75,21 +122,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   constexpr int FN = WN / 32;
   constexpr int KC = BK / 8;    // 16-byte chunks per X row of a K tile
   constexpr int NC = BN / 8;    // 16-byte chunks per W row of a K tile
-  constexpr int A_CH = BM * KC / NT;
-  constexpr int B_CH = BK * NC / NT;
+  constexpr int STAGES = 4;
+  // HBM -> LDS copies: one wave instruction moves 64 lanes x 16 B = 1 KB
+  constexpr int A_PER_WAVE = BM * BK * 2 / 1024 / NWAVES;
+  constexpr int B_PER_WAVE = BK * BN * 2 / 1024 / NWAVES;
+  constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;  // per wave per stage (wave 0: +1 with gamma)
+  constexpr int SS_SLOTS = (FM + WAVES_N - 1) / WAVES_N;
   static_assert(NWAVES == 4 || NWAVES == 8, "4 or 8 waves per workgroup");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
-  static_assert(BK % 16 == 0 && KC <= 8, "BK in {16,32,64}");
-  static_assert(BM * KC % NT == 0 && BK * NC % NT == 0, "whole chunks per thread");
+  static_assert(BK == 32 || BK == 64, "BK in {32, 64}");
+  static_assert(A_PER_WAVE >= 1 && B_PER_WAVE >= 1, "whole 1 KB copies per wave");
+  static_assert(A_PER_WAVE * NWAVES * 1024 == BM * BK * 2 && B_PER_WAVE * NWAVES * 1024 == BK * BN * 2,
+                "tile bytes split evenly over the waves");
   static_assert(NC >= 8, "BN >= 64 for the W swizzle");
-  using S = Smem<BM, BN, BK>;
+  using S = Smem<BM, BN, BK, STAGES, GAMMA>;
+  static_assert(S::BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES == 4, "the ring below is written out for 4 stages");
 
-  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
-  FNG_LDS char* lds = (FNG_LDS char*)smem;
+  // one LDS object per ring stage: the compiler can then see that the copies
+  // in flight into the other stages never alias the stage being read
+  __shared__ __attribute__((aligned(1024))) char sm0[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm1[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm2[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char sm3[S::STAGE];
+  FNG_LDS char* lds = (FNG_LDS char*)sm0;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int l32 = lane & 31;
@@ -118,47 +178,53 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
-    const uint32_t xbytes = (uint32_t)min<int64_t>((int64_t)(M - m0) * K * 2, 0xffffffffLL);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.X + (size_t)m0 * K, xbytes);
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.W + n0, (uint32_t)((int64_t)K * N * 2 - (int64_t)n0 * 2));
-    __amdgpu_buffer_rsrc_t gr;
-    if constexpr (GAMMA) gr = make_rsrc(p.gamma, (uint32_t)K * 2);
+    // rows of X past M and K/N tails of W read as zero; X's range is capped
+    // below kOOB so that kOOB offsets are always out of range
+    const int64_t xrem = (int64_t)(M - m0) * K * 2;
+    const uint32_t xbytes = xrem > 0x7ffffff0LL ? 0x7ffffff0u : (uint32_t)xrem;
+    const i32x4_t xr = dma_rsrc(p.X + (size_t)m0 * K, xbytes);
+    const i32x4_t wr = dma_rsrc(p.W + n0, (uint32_t)((int64_t)K * N * 2 - (int64_t)n0 * 2));
+    i32x4_t gr;
+    if constexpr (GAMMA) gr = dma_rsrc(p.gamma, (uint32_t)K * 2);
 
-    // ---- staging helpers -------------------------------------------------
-    u32x4_t ra[A_CH], rb[B_CH];
-    auto gload = [&](int kt) {
+    // ---- this lane's share of each K tile's copies ------------------------
+    // X: copy i of this wave fills LDS bytes [(wave*A_PER_WAVE + i) KB, +1 KB)
+    //    of the stage; lane l writes the 16 B at +16 l, i.e. row r, physical
+    //    chunk pc, which holds logical chunk pc ^ swz(r).
+    uint32_t a_off[A_PER_WAVE];
+    int a_k[A_PER_WAVE];
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + NT * i;
-        const int row = c / KC, kc = c % KC;
-        const int k = kt * BK + kc * 8;
-        u32x4_t v = buffer_load16(xr, (uint32_t)(row * K + k) * 2u);
-        ra[i] = (k < K) ? v : u32x4_t{0, 0, 0, 0};
+    for (int i = 0; i < A_PER_WAVE; ++i) {
+      const int idx = (wave * A_PER_WAVE + i) * 1024 + lane * 16;
+      const int row = idx / (BK * 2), pc = (idx % (BK * 2)) / 16;
+      const int kc = pc ^ swz_a<KC>(row);
+      a_k[i] = kc * 8;
+      a_off[i] = (uint32_t)(row * K + kc * 8) * 2u;
+    }
+    uint32_t b_off[B_PER_WAVE];
+    bool b_ok[B_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) {
+      const int idx = (wave * B_PER_WAVE + i) * 1024 + lane * 16;
+      const int krow = idx / (BN * 2), pc = (idx % (BN * 2)) / 16;
+      const int nc = pc ^ swz_b(krow);
+      b_ok[i] = n0 + nc * 8 < N;
+      b_off[i] = (uint32_t)(krow * N + nc * 8) * 2u;
+    }
+    auto issue = [&](int kt, FNG_LDS char* sb) {
+#pragma unroll
+      for (int i = 0; i < A_PER_WAVE; ++i) {
+        const uint32_t off = (kt * BK + a_k[i] < K) ? a_off[i] + (uint32_t)(kt * BK * 2) : kOOB;
+        dma16(xr, sb + (wave * A_PER_WAVE + i) * 1024, off);
       }
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + NT * i;
-        const int krow = c / NC, nc = c % NC;
-        const int k = kt * BK + krow;
-        u32x4_t v = buffer_load16(wr, (uint32_t)(k * N + nc * 8) * 2u);
-        rb[i] = (n0 + nc * 8 < N) ? v : u32x4_t{0, 0, 0, 0};
+      for (int i = 0; i < B_PER_WAVE; ++i) {
+        const uint32_t off = (b_ok[i] && kt < ktiles) ? b_off[i] + (uint32_t)(kt * BK) * (uint32_t)N * 2u : kOOB;
+        dma16(wr, sb + S::A_STAGE + (wave * B_PER_WAVE + i) * 1024, off);
       }
-    };
-    auto sstore = [&](int stage) {
-      FNG_LDS char* as = lds + stage * S::A_STAGE;
-      FNG_LDS char* bs = lds + 2 * S::A_STAGE + stage * S::B_STAGE;
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + NT * i;
-        const int row = c / KC, kc = c % KC;
-        lds_write16(as + row * (BK * 2) + ((kc ^ swz_a(row)) & (KC - 1)) * 16, ra[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + NT * i;
-        const int krow = c / NC, nc = c % NC;
-        lds_write16(bs + krow * (BN * 2) + (nc ^ swz_b(krow)) * 16, rb[i]);
+      if constexpr (GAMMA) {
+        if (wave == 0 && lane < KC)
+          dma16(gr, sb + S::A_STAGE + S::B_STAGE, kt < ktiles ? (uint32_t)(kt * BK + lane * 8) * 2u : kOOB);
       }
     };
 
@@ -169,21 +235,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    float ss[FM];
+    // lazy pre-norm: this wave accumulates the sum of squares of the X
+    // fragments f = s * WAVES_N + wn (the waves sharing rows split them)
+    float ss[SS_SLOTS];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ss[i] = 0.f;
+    for (int s = 0; s < SS_SLOTS; ++s) ss[s] = 0.f;
 
-    __syncthreads();  // previous tile's epilogue may still read LDS
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int stage = kt & 1;
-      const bool more = kt + 1 < ktiles;
-      if (more) gload(kt + 1);
-      const FNG_LDS char* as = lds + stage * S::A_STAGE;
-      const FNG_LDS char* bs = lds + 2 * S::A_STAGE + stage * S::B_STAGE;
+    auto compute = [&](const FNG_LDS char* as) {
+      const FNG_LDS char* bs = as + S::A_STAGE;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         u32x4_t xf[FM], wf[FN];
@@ -191,7 +250,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         for (int i = 0; i < FM; ++i) {
           const int row = wm * WM + 32 * i + l32;
           const int kc = 2 * kk + hi;
-          xf[i] = lds_read16(as + row * (BK * 2) + ((kc ^ swz_a(row)) & (KC - 1)) * 16);
+          xf[i] = lds_read16(as + row * (BK * 2) + (kc ^ swz_a<KC>(row)) * 16);
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -206,11 +265,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         }
         if constexpr (EPI == EPI_PRENORM) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i) ss[i] = sumsq_bf16x8(xf[i], ss[i]);
+          for (int s = 0; s < SS_SLOTS; ++s) {
+            const int f = s * WAVES_N + wn;
+            u32x4_t v = xf[0];
+#pragma unroll
+            for (int q = 1; q < FM; ++q) v = (f == q) ? xf[q] : v;
+            if (f < FM) ss[s] = sumsq_bf16x8(v, ss[s]);
+          }
         }
         if constexpr (GAMMA) {
-          const int k = kt * BK + kk * 16 + 8 * hi;
-          const u32x4_t gv = buffer_load16(gr, (uint32_t)k * 2u);
+          const u32x4_t gv = lds_read16(bs + S::B_STAGE + kk * 32 + hi * 16);
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -225,9 +289,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
       }
-      if (more) sstore(stage ^ 1);
-      __syncthreads();
+    };
+
+    // ---- mainloop: 4-deep ring, one barrier per K tile --------------------
+    // step kt: wait for this wave's copies of tile kt (at most the copies of
+    // the two tiles issued after it may still be in flight), barrier (every
+    // wave's copies landed, and every wave is done reading tile kt-1), refill
+    // the freed stage with tile kt+3, multiply tile kt.
+    // The refill is issued unconditionally: past the last K tile its offsets
+    // are all out of range (it writes zeros into a stage nobody reads), which
+    // keeps the number of copies in flight the same at every step.
+    auto step = [&](int kt, const FNG_LDS char* cur, FNG_LDS char* refill) {
+      wait_vmcnt<(STAGES - 2) * LOADS>();
+      lds_barrier();
+      issue(kt + STAGES - 1, refill);
+      compute(cur);
+    };
+    __syncthreads();  // the previous tile's epilogue may still read LDS
+    issue(0, (FNG_LDS char*)sm0);
+    issue(1, (FNG_LDS char*)sm1);
+    issue(2, (FNG_LDS char*)sm2);
+    for (int kt = 0; kt < ktiles; kt += 4) {
+      step(kt, (FNG_LDS char*)sm0, (FNG_LDS char*)sm3);
+      if (kt + 1 < ktiles) step(kt + 1, (FNG_LDS char*)sm1, (FNG_LDS char*)sm0);
+      if (kt + 2 < ktiles) step(kt + 2, (FNG_LDS char*)sm2, (FNG_LDS char*)sm1);
+      if (kt + 3 < ktiles) step(kt + 3, (FNG_LDS char*)sm3, (FNG_LDS char*)sm2);
     }
+    // drain the trailing zero-fill copies before the epilogue reuses the LDS
+    wait_vmcnt<0>();
+    __syncthreads();
 
     // ---- epilogues -------------------------------------------------------
     // lane l of wave (wm, wn) holds rows  wm*WM + 32*i + l32          (i < FM)
@@ -237,11 +327,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 
     float rs_mean[FM], rs_rstd[FM];
     if constexpr (EPI == EPI_PRENORM) {
+      FNG_LDS float* red = (FNG_LDS float*)lds;
+#pragma unroll
+      for (int s = 0; s < SS_SLOTS; ++s) {
+        const int f = s * WAVES_N + wn;
+        const float tot = xor_sum(ss[s], 32);
+        if (f < FM && hi == 0) red[wm * WM + 32 * f + l32] = tot;
+      }
+      __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const float tot = xor_sum(ss[i], 32);
         rs_mean[i] = 0.f;
-        rs_rstd[i] = __builtin_amdgcn_rsqf(tot / (float)K + p.eps);
+        rs_rstd[i] = __builtin_amdgcn_rsqf(red[wm * WM + 32 * i + l32] / (float)K + p.eps);
       }
     }
 
