@@ -31,8 +31,8 @@ int check_gemm(const void* X, const void* W, const void* Y, int64_t M, int64_t N
   if (K % 8 != 0 || N % 8 != 0) return FNG_ERR_MISALIGNED;
   // 32-bit index and buffer-range limits of the kernels
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FNG_ERR_UNSUPPORTED;
-  if ((K + 256) * N * 2 >= (int64_t)UINT32_MAX) return FNG_ERR_UNSUPPORTED;  // W rows incl. K-tile overrun
-  if (256 * K * 2 >= (int64_t)UINT32_MAX) return FNG_ERR_UNSUPPORTED;        // one X row block
+  if ((K + 256) * N * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;   // W (+ K-tile overrun) below 2 GiB
+  if ((256 + 1) * K * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;  // one X row block below 2 GiB
   if (M * N >= ((int64_t)1 << 46)) return FNG_ERR_UNSUPPORTED;
   return FNG_OK;
 }

@@ -48,8 +48,11 @@ constexpr int kBQ = 128;  // query rows per workgroup
 constexpr int kBK = 64;   // keys per tile
 constexpr int kTileBytes = kBK * kD * 2;
 
-__device__ __forceinline__ int swz_k(int key) { return key & 7; }
-__device__ __forceinline__ int swz_v(int key) { return (key & 3) << 1; }
+// LDS chunk swizzles (16-byte chunks, 16 per 256-byte row, 64 banks of 4 B):
+// a K fragment read covers 16 consecutive keys at one chunk; a transposing V
+// read covers keys k..k+3 and four consecutive chunks.
+__device__ __forceinline__ int swz_k(int key) { return key & 15; }
+__device__ __forceinline__ int swz_v(int key) { return (key & 3) << 2; }
 
 template <bool NORM>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {

@@ -54,26 +54,40 @@ struct GemmParams {
   uint32_t spin_limit;
 };
 
+// LDS layout: the W parts of all ring stages, then the X parts, then the
+// gamma slices.  A fragment address is one lane-dependent base register plus
+// a compile-time (stage, k16 slice) offset in the instruction's 16-bit offset
+// field.
 template <int BM, int BN, int BK, int STAGES, bool GAMMA>
 struct Smem {
   static constexpr int A_STAGE = BM * BK * 2;
   static constexpr int B_STAGE = BK * BN * 2;
-  static constexpr int G_STAGE = GAMMA ? 256 : 0;  // gamma slice of the K tile
-  static constexpr int STAGE = A_STAGE + B_STAGE + G_STAGE;
-  static constexpr int BYTES = STAGES * STAGE;
+  static constexpr int B_OFF = 0;
+  static constexpr int A_OFF = STAGES * B_STAGE;
+  static constexpr int G_OFF = A_OFF + STAGES * A_STAGE;
+  static constexpr int BYTES = G_OFF + (GAMMA ? STAGES * 256 : 0);
+  static constexpr int a(int s) { return A_OFF + s * A_STAGE; }
+  static constexpr int b(int s) { return B_OFF + s * B_STAGE; }
+  static constexpr int gm(int s) { return G_OFF + s * 256; }
 };
 
-// swizzles of the 16-byte chunk index inside one LDS row
-//   X rows (BK*2 bytes): XOR with row bits so that 8 consecutive rows read by a
-//   fragment load land in distinct banks;
-//   W rows (BN*2 bytes): XOR with 2*(k % 4) so the 4 rows of a transposing read
-//   land in distinct 32-byte slots.
+// swizzles of the 16-byte chunk index inside one LDS row.  The LDS serves
+// 256 B per cycle (64 banks of 4 B): a ds_read_b128 is served 16 lanes per
+// cycle, a ds_read_b64_tr_b16 32 lanes per cycle, and each group must touch
+// 64 distinct banks.
+//   X rows (BK*2 bytes; a fragment read covers 16 consecutive rows at one
+//   logical chunk): XOR the chunk with the row's index among the rows that
+//   share a 256 B bank window, so the 16 rows land on distinct units.
+//   W rows (BN*2 bytes; a transposing read covers rows k..k+3 and four
+//   consecutive chunks): XOR with 4*(k % 4) moves each row to its own
+//   quarter of the window.
 template <int KC>
 __device__ __forceinline__ int swz_a(int row) {
-  if constexpr (KC >= 8) return row & 7;
-  else return ((row >> 1) ^ row) & (KC - 1);
+  constexpr int ROWS_PER_WINDOW = 256 / (KC * 16);
+  return (row / ROWS_PER_WINDOW) & (KC - 1);
 }
-__device__ __forceinline__ int swz_b(int krow) { return (krow & 3) << 1; }
+template <int NC>
+__device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) << 2) & (NC - 1); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
 template <int N>
@@ -127,7 +141,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   constexpr int A_PER_WAVE = BM * BK * 2 / 1024 / NWAVES;
   constexpr int B_PER_WAVE = BK * BN * 2 / 1024 / NWAVES;
   constexpr int LOADS = A_PER_WAVE + B_PER_WAVE;  // per wave per stage (wave 0: +1 with gamma)
-  constexpr int SS_SLOTS = (FM + WAVES_N - 1) / WAVES_N;
+  // lazy pre-norm: the WAVES_N waves that share rows split the sums of squares.
+  // Each wave visits its X fragments in a rotated order so that the ones it
+  // sums are its first SS_SLOTS register slots (no run-time indexing).
+  constexpr int SS_SLOTS = FM >= WAVES_N ? FM / WAVES_N : 1;
+  static_assert(FM < WAVES_N || FM % WAVES_N == 0, "row fragments split evenly");
   static_assert(NWAVES == 4 || NWAVES == 8, "4 or 8 waves per workgroup");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
   static_assert(BK == 32 || BK == 64, "BK in {32, 64}");
@@ -139,13 +157,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   static_assert(S::BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES == 4, "the ring below is written out for 4 stages");
 
-  // one LDS object per ring stage: the compiler can then see that the copies
-  // in flight into the other stages never alias the stage being read
-  __shared__ __attribute__((aligned(1024))) char sm0[S::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm1[S::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm2[S::STAGE];
-  __shared__ __attribute__((aligned(1024))) char sm3[S::STAGE];
-  FNG_LDS char* lds = (FNG_LDS char*)sm0;
+  __shared__ __attribute__((aligned(1024))) char smem[S::BYTES];
+  FNG_LDS char* lds = (FNG_LDS char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,6 +167,43 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   const int wn = wave % WAVES_N;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int rot = FM >= WAVES_N ? wn * SS_SLOTS : wn;
+  const bool ss_owner = FM >= WAVES_N || wn < FM;
+  // row (within the tile) of this lane's fragment slot i
+  auto lrow = [&](int i) { return wm * WM + 32 * ((i + rot) % FM) + l32; };
+
+  // Lane-dependent LDS base addresses of the fragment reads; every other part
+  // of an address (ring stage, k16 slice, second transposed half) is a
+  // compile-time offset.  The empty asm keeps each base in one register so
+  // the compiler does not fold the large region offsets into per-stage copies.
+  //   X slot i, k16 slice kk: row lrow(i), logical chunk 2*kk + hi, swizzled
+  //   (an XOR, so one base per slot and slice).
+  //   W column block j: rows kk*16 + 8*(g/2) + (li/4) (+4 for the second
+  //   half), columns 16*(g%2) + 4*(li%4) of the block; the row swizzle only
+  //   depends on li/4, so slices and halves are plain offsets.
+  FNG_LDS char* xaddr[FM][BK / 16];
+  FNG_LDS char* waddr[FN];
+  {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < BK / 16; ++q) {
+        const int row = lrow(i);
+        const int kc = 2 * q + hi;
+        uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + row * (BK * 2) + (kc ^ swz_a<KC>(row)) * 16);
+        asm volatile("" : "+v"(a));
+        xaddr[i][q] = reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a));
+      }
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (li & 3);
+      const int k0 = 8 * (g >> 1) + (li >> 2);
+      uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(lds + k0 * (BN * 2) + ((n >> 3) ^ swz_b<NC>(k0)) * 16 + (n & 7) * 2);
+      asm volatile("" : "+v"(a));
+      waddr[j] = reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a));
+    }
+  }
 
   const int M = p.M, N = p.N, K = p.K;
   const int ktiles = (K + BK - 1) / BK;
@@ -207,24 +257,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     for (int i = 0; i < B_PER_WAVE; ++i) {
       const int idx = (wave * B_PER_WAVE + i) * 1024 + lane * 16;
       const int krow = idx / (BN * 2), pc = (idx % (BN * 2)) / 16;
-      const int nc = pc ^ swz_b(krow);
+      const int nc = pc ^ swz_b<NC>(krow);
       b_ok[i] = n0 + nc * 8 < N;
       b_off[i] = (uint32_t)(krow * N + nc * 8) * 2u;
     }
-    auto issue = [&](int kt, FNG_LDS char* sb) {
+    // Out-of-range copies (K tail, N tail, tiles past the end) set bit 31 of
+    // the offset: both descriptors' ranges are below 2^31, so they read zeros.
+    auto issue = [&](int kt, int s) {
+      const uint32_t kt_live = kt < ktiles ? 0u : kOOB;
 #pragma unroll
       for (int i = 0; i < A_PER_WAVE; ++i) {
-        const uint32_t off = (kt * BK + a_k[i] < K) ? a_off[i] + (uint32_t)(kt * BK * 2) : kOOB;
-        dma16(xr, sb + (wave * A_PER_WAVE + i) * 1024, off);
+        const uint32_t dead = (kt * BK + a_k[i] < K) ? kt_live : kOOB;
+        dma16(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, (a_off[i] + (uint32_t)(kt * BK * 2)) | dead);
       }
 #pragma unroll
       for (int i = 0; i < B_PER_WAVE; ++i) {
-        const uint32_t off = (b_ok[i] && kt < ktiles) ? b_off[i] + (uint32_t)(kt * BK) * (uint32_t)N * 2u : kOOB;
-        dma16(wr, sb + S::A_STAGE + (wave * B_PER_WAVE + i) * 1024, off);
+        const uint32_t dead = b_ok[i] ? kt_live : kOOB;
+        dma16(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024,
+              (b_off[i] + (uint32_t)(kt * BK) * (uint32_t)N * 2u) | dead);
       }
       if constexpr (GAMMA) {
         if (wave == 0 && lane < KC)
-          dma16(gr, sb + S::A_STAGE + S::B_STAGE, kt < ktiles ? (uint32_t)(kt * BK + lane * 8) * 2u : kOOB);
+          dma16(gr, lds + S::gm(s), ((uint32_t)(kt * BK + lane * 8) * 2u) | kt_live);
       }
     };
 
@@ -235,85 +289,94 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    // lazy pre-norm: this wave accumulates the sum of squares of the X
-    // fragments f = s * WAVES_N + wn (the waves sharing rows split them)
     float ss[SS_SLOTS];
 #pragma unroll
     for (int s = 0; s < SS_SLOTS; ++s) ss[s] = 0.f;
 
-    auto compute = [&](const FNG_LDS char* as) {
-      const FNG_LDS char* bs = as + S::A_STAGE;
+    // one k16 slice of fragments: X rows of this wave, W columns of this wave
+    // (and the matching gamma slice)
+    struct Frags {
+      u32x4_t x[FM];
+      u32x4_t w[FN];
+      u32x4_t g;
+    };
+    auto load = [&](int s, int kk, Frags& f) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        u32x4_t xf[FM], wf[FN];
+      for (int i = 0; i < FM; ++i) f.x[i] = lds_read16(xaddr[i][kk] + (S::a(s) - S::A_OFF));
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int row = wm * WM + 32 * i + l32;
-          const int kc = 2 * kk + hi;
-          xf[i] = lds_read16(as + row * (BK * 2) + (kc ^ swz_a<KC>(row)) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int g = lane >> 4, li = lane & 15;
-          const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (li & 3);
-          const int nc = n >> 3, nb = (n & 7) * 2;
-          const int k0 = kk * 16 + 8 * (g >> 1) + (li >> 2);
-          const u32x2_t lo = lds_read_tr16(bs + k0 * (BN * 2) + (nc ^ swz_b(k0)) * 16 + nb);
-          const int k1 = k0 + 4;
-          const u32x2_t hi2 = lds_read_tr16(bs + k1 * (BN * 2) + (nc ^ swz_b(k1)) * 16 + nb);
-          wf[j] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
-        }
-        if constexpr (EPI == EPI_PRENORM) {
-#pragma unroll
-          for (int s = 0; s < SS_SLOTS; ++s) {
-            const int f = s * WAVES_N + wn;
-            u32x4_t v = xf[0];
-#pragma unroll
-            for (int q = 1; q < FM; ++q) v = (f == q) ? xf[q] : v;
-            if (f < FM) ss[s] = sumsq_bf16x8(v, ss[s]);
-          }
-        }
-        if constexpr (GAMMA) {
-          const u32x4_t gv = lds_read16(bs + S::B_STAGE + kk * 32 + hi * 16);
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              xf[i][e] = pack_bf16(bf16lo(xf[i][e]) * bf16lo(gv[e]),
-                                   bf16hi(xf[i][e]) * bf16hi(gv[e]));
-            }
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(wf[j], xf[i], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        const FNG_LDS char* wa = waddr[j] + S::b(s) + kk * 16 * (BN * 2);
+        const u32x2_t lo = lds_read_tr16(wa);
+        const u32x2_t hi2 = lds_read_tr16(wa + 4 * (BN * 2));
+        f.w[j] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
       }
+      if constexpr (GAMMA) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
+    };
+    auto mma = [&](Frags& f) {
+      if constexpr (EPI == EPI_PRENORM) {
+        if (ss_owner) {
+#pragma unroll
+          for (int s = 0; s < SS_SLOTS; ++s) ss[s] = sumsq_bf16x8(f.x[s], ss[s]);
+        }
+      }
+      if constexpr (GAMMA) {
+        // the gain multiplies along K; the lane's 8 W values and its 8 X
+        // values share the same k, so it is folded into the W fragments
+        // (the statistic above used the raw X)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f.w[j][e] = pack_bf16(bf16lo(f.w[j][e]) * bf16lo(f.g[e]), bf16hi(f.w[j][e]) * bf16hi(f.g[e]));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(f.w[j], f.x[i], acc[i][j]);
     };
 
-    // ---- mainloop: 4-deep ring, one barrier per K tile --------------------
-    // step kt: wait for this wave's copies of tile kt (at most the copies of
-    // the two tiles issued after it may still be in flight), barrier (every
-    // wave's copies landed, and every wave is done reading tile kt-1), refill
-    // the freed stage with tile kt+3, multiply tile kt.
-    // The refill is issued unconditionally: past the last K tile its offsets
-    // are all out of range (it writes zeros into a stage nobody reads), which
-    // keeps the number of copies in flight the same at every step.
-    auto step = [&](int kt, const FNG_LDS char* cur, FNG_LDS char* refill) {
-      wait_vmcnt<(STAGES - 2) * LOADS>();
+    // ---- mainloop: 4-deep ring of K tiles, one barrier per tile ------------
+    // Step kt (its first k16 fragments already in registers): read the rest of
+    // tile kt's fragments, multiply all but the last slice, then wait for this
+    // wave's copies of tile kt+1 (at most those of tiles kt+2, kt+3 may still
+    // be in flight) and barrier: every wave has finished reading tile kt and
+    // tile kt+1 has landed.  Refill tile kt's stage with tile kt+4, read the
+    // first fragments of tile kt+1, and only then multiply the last slice of
+    // tile kt, which covers the latency of those reads.  The refill is issued
+    // unconditionally (past the last tile it writes zeros nobody reads), so
+    // the number of copies in flight is the same at every step.
+    constexpr int KK = BK / 16;
+    // sched_barrier(0) fences keep the compiler from sinking the next slice's
+    // fragment reads down to their consumers: each slice's reads are issued
+    // as a block ahead of the previous slice's MFMAs, which cover their latency.
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](int kt, int cur, int next, Frags& fa) {
+      Frags fb;
+#pragma unroll
+      for (int kk = 1; kk < KK; ++kk) {
+        if (kk % 2 == 1) { load(cur, kk, fb); fence(); mma(fa); fence(); }
+        else { load(cur, kk, fa); fence(); mma(fb); fence(); }
+      }
+      wait_vmcnt<2 * LOADS>();
       lds_barrier();
-      issue(kt + STAGES - 1, refill);
-      compute(cur);
+      issue(kt + STAGES, cur);
+      if constexpr (KK % 2 == 0) { load(next, 0, fa); fence(); mma(fb); fence(); }
+      else { Frags fc; load(next, 0, fc); fence(); mma(fa); fence(); fa = fc; }
     };
     __syncthreads();  // the previous tile's epilogue may still read LDS
-    issue(0, (FNG_LDS char*)sm0);
-    issue(1, (FNG_LDS char*)sm1);
-    issue(2, (FNG_LDS char*)sm2);
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    issue(3, 3);
+    wait_vmcnt<3 * LOADS>();
+    lds_barrier();
+    Frags fr;
+    load(0, 0, fr);
     for (int kt = 0; kt < ktiles; kt += 4) {
-      step(kt, (FNG_LDS char*)sm0, (FNG_LDS char*)sm3);
-      if (kt + 1 < ktiles) step(kt + 1, (FNG_LDS char*)sm1, (FNG_LDS char*)sm0);
-      if (kt + 2 < ktiles) step(kt + 2, (FNG_LDS char*)sm2, (FNG_LDS char*)sm1);
-      if (kt + 3 < ktiles) step(kt + 3, (FNG_LDS char*)sm3, (FNG_LDS char*)sm2);
+      step(kt, 0, 1, fr);
+      if (kt + 1 < ktiles) step(kt + 1, 1, 2, fr);
+      if (kt + 2 < ktiles) step(kt + 2, 2, 3, fr);
+      if (kt + 3 < ktiles) step(kt + 3, 3, 0, fr);
     }
     // drain the trailing zero-fill copies before the epilogue reuses the LDS
     wait_vmcnt<0>();
@@ -323,22 +386,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     // lane l of wave (wm, wn) holds rows  wm*WM + 32*i + l32          (i < FM)
     // and columns                         wn*WN + 32*j + 8*(r/4) + 4*hi + r%4
     auto col_of = [&](int j, int r4) { return n0 + wn * WN + 32 * j + 8 * r4 + 4 * hi; };
-    auto row_of = [&](int i) { return m0 + wm * WM + 32 * i + l32; };
+    auto row_of = [&](int i) { return m0 + lrow(i); };
 
     float rs_mean[FM], rs_rstd[FM];
     if constexpr (EPI == EPI_PRENORM) {
       FNG_LDS float* red = (FNG_LDS float*)lds;
 #pragma unroll
       for (int s = 0; s < SS_SLOTS; ++s) {
-        const int f = s * WAVES_N + wn;
         const float tot = xor_sum(ss[s], 32);
-        if (f < FM && hi == 0) red[wm * WM + 32 * f + l32] = tot;
+        if (ss_owner && hi == 0) red[lrow(s)] = tot;
       }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         rs_mean[i] = 0.f;
-        rs_rstd[i] = __builtin_amdgcn_rsqf(red[wm * WM + 32 * i + l32] / (float)K + p.eps);
+        rs_rstd[i] = __builtin_amdgcn_rsqf(red[lrow(i)] / (float)K + p.eps);
       }
     }
 
@@ -351,14 +413,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const float s = xor_sum(v[i], 32);
-          if (hi == 0) red[wn * BM + wm * WM + 32 * i + l32] = s;
+          if (hi == 0) red[wn * BM + lrow(i)] = s;
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           float s = 0.f;
 #pragma unroll
-          for (int w = 0; w < WAVES_N; ++w) s += red[w * BM + wm * WM + 32 * i + l32];
+          for (int w = 0; w < WAVES_N; ++w) s += red[w * BM + lrow(i)];
           out[i] = s;
         }
         __syncthreads();
@@ -434,62 +496,86 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         if (wn == 0 && hi == 0) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const int row = wm * WM + 32 * i + l32;
-            pp[row * 2 + 0] = s1[i];
-            pp[row * 2 + 1] = s2[i];
+            const int row = lrow(i);
+            if constexpr (EPI == EPI_SPLITN) {
+              // device-scope stores: written through to the device-coherent
+              // level, visible to every XCD without a cache-wide write-back
+              __hip_atomic_store(pp + row * 2 + 0, s1[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(pp + row * 2 + 1, s2[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              pp[row * 2 + 0] = s1[i];
+              pp[row * 2 + 1] = s2[i];
+            }
           }
         }
         if constexpr (EPI == EPI_SPLITN) {
-          // the waves with wn == 0 wrote; each of them arrives once (release)
-          const uint32_t writers = WAVES_M;
-          if (wn == 0 && lane == 0)
-            __hip_atomic_fetch_add(p.cnt + tm, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-          const uint32_t target = writers * (uint32_t)p.tiles_n;
-          uint32_t spins = 0;
-          while (__hip_atomic_load(p.cnt + tm, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > p.spin_limit) {
-              if (lane == 0)
+          // Exchange (section 3's multi-CTA reduction, without clusters).
+          // Every access to the exchanged data is a device-scope atomic, which
+          // the hardware performs at the device-coherent level (past the
+          // per-XCD L2s), so no cache-wide release/acquire fence is needed:
+          //  - each writer wave waits until its partial stores are acknowledged
+          //    (vmcnt 0) before the workgroup barrier;
+          //  - one thread then arrives on the row block's counter and polls it;
+          //  - after a second barrier all threads read the partials with
+          //    device-scope loads, issued only once the poll has returned.
+          wait_vmcnt<0>();
+          __syncthreads();
+          FNG_LDS float* stats = (FNG_LDS float*)lds;  // [BM][2]: mean, rstd
+          if (tid == 0) {
+            __hip_atomic_fetch_add(p.cnt + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t target = (uint32_t)p.tiles_n;
+            uint32_t spins = 0;
+            while (__hip_atomic_load(p.cnt + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+              __builtin_amdgcn_s_sleep(1);
+              if (++spins > p.spin_limit) {
                 __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
+                break;
+              }
+            }
+            // every workgroup of the row block has finished waiting once the
+            // last one arrives here: it resets the counters for the next call
+            const uint32_t prev =
+                __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == target - 1u) {
+              __hip_atomic_store(p.cnt + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
-          // merge all N slices of my rows in a fixed order
-          const float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2);
-          const int nt = p.tiles_n;
-#pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = wm * WM + 32 * i + l32;
+          __syncthreads();
+          // merge the tiles_n slices of row tid in a fixed order
+          if (tid < BM) {
+            float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
+            const int nt = p.tiles_n;
+            auto ld = [&](int q, int c) {
+              return __hip_atomic_load(pb + (size_t)q * BM * 2 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
             if constexpr (LN) {
               // Chan et al. pairwise merge of (count, mean, M2)
               float cn = 0.f, mean = 0.f, m2 = 0.f;
               for (int q = 0; q < nt; ++q) {
                 const float nb = (float)min(BN, N - q * BN);
-                const float mb = pb[(size_t)q * BM * 2 + row * 2 + 0];
-                const float m2b = pb[(size_t)q * BM * 2 + row * 2 + 1];
+                const float mb = ld(q, 0);
+                const float m2b = ld(q, 1);
                 const float tot = cn + nb;
                 const float d = mb - mean;
                 mean += d * (nb / tot);
                 m2 += m2b + d * d * (cn * nb / tot);
                 cn = tot;
               }
-              rs_mean[i] = mean;
-              rs_rstd[i] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
+              stats[tid * 2 + 0] = mean;
+              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
             } else {
               float s = 0.f;
-              for (int q = 0; q < nt; ++q) s += pb[(size_t)q * BM * 2 + row * 2 + 1];
-              rs_mean[i] = 0.f;
-              rs_rstd[i] = __builtin_amdgcn_rsqf(s / (float)N + p.eps);
+              for (int q = 0; q < nt; ++q) s += ld(q, 1);
+              stats[tid * 2 + 0] = 0.f;
+              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(s / (float)N + p.eps);
             }
           }
-          // every wave has read; the last one resets the counters for the next call
-          if (lane == 0) {
-            const uint32_t prev =
-                __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            if (prev == (uint32_t)NWAVES * (uint32_t)p.tiles_n - 1u) {
-              __hip_atomic_store(p.cnt + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            rs_mean[i] = stats[lrow(i) * 2 + 0];
+            rs_rstd[i] = stats[lrow(i) * 2 + 1];
           }
         }
       }
@@ -510,31 +596,47 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       }
     }
 
-    // ---- store bf16 -----------------------------------------------------
+    // ---- store bf16 through LDS: fragments -> swizzled LDS tile -> full rows
+    // A lane holds 4 consecutive columns of one row per register quad; lanes l
+    // and l + 32 hold the two halves of one 16-byte chunk.  The tile is staged
+    // in LDS (chunk index XOR-ed with the row so the 32 rows of one write land
+    // on distinct banks) and written back with 16-byte stores along rows.
+    {
+      static_assert(BM * BN * 2 <= S::BYTES, "output tile fits in the ring");
+      constexpr int NCH = BN / 8;  // 16-byte chunks per tile row
+      __syncthreads();             // statistics in LDS have been read
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = row_of(i);
-      if (m >= M) continue;
-      uint16_t* yrow = p.Y + (size_t)m * N;
+      for (int i = 0; i < FM; ++i) {
+        const int row = lrow(i);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = col_of(j, r4);
-          if (n >= N) continue;
-          float v[4];
+          for (int r4 = 0; r4 < 4; ++r4) {
+            float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float a = acc[i][j][4 * r4 + e];
-            if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
-            if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
-            // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
-            // mean, so rows whose mean dwarfs their spread keep their precision
-            if constexpr (EPI == EPI_PARTIAL && LN) a -= rs_mean[i];
-            v[e] = a;
+            for (int e = 0; e < 4; ++e) {
+              float a = acc[i][j][4 * r4 + e];
+              if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
+              if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
+              // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
+              // mean, so rows whose mean dwarfs their spread keep their precision
+              if constexpr (EPI == EPI_PARTIAL && LN) a -= rs_mean[i];
+              v[e] = a;
+            }
+            const int ch = (wn * WN + 32 * j + 8 * r4) / 8;
+            *reinterpret_cast<FNG_LDS u32x2_t*>(lds + row * (BN * 2) + ((ch ^ row) & (NCH - 1)) * 16 + hi * 8) =
+                u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
           }
-          *reinterpret_cast<u32x2_t*>(yrow + n) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
         }
+      }
+      __syncthreads();
+      constexpr int NT = 64 * NWAVES;
+#pragma unroll 4
+      for (int c = tid; c < BM * NCH; c += NT) {
+        const int row = c / NCH, ch = c % NCH;
+        const int m = m0 + row, n = n0 + ch * 8;
+        const u32x4_t v = lds_read16(lds + row * (BN * 2) + ((ch ^ row) & (NCH - 1)) * 16);
+        if (m < M && n < N) *reinterpret_cast<u32x4_t*>(p.Y + (size_t)m * N + n) = v;
       }
     }
   }

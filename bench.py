@@ -45,8 +45,8 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--reps", type=int, default=5, help="interleaved rounds per kernel comparison")
     ap.add_argument("--batch", type=int, default=10, help="launches per timed batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
