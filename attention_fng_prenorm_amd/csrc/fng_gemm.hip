@@ -542,33 +542,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
             }
           }
           __syncthreads();
-          // merge the tiles_n slices of row tid in a fixed order
+          // merge the tiles_n slices of row tid in a fixed order; the
+          // device-scope loads are issued in batches of 16 independent loads
+          // (one at a time they would be serialized memory round trips)
           if (tid < BM) {
             float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
             const int nt = p.tiles_n;
-            auto ld = [&](int q, int c) {
-              return __hip_atomic_load(pb + (size_t)q * BM * 2 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            };
-            if constexpr (LN) {
-              // Chan et al. pairwise merge of (count, mean, M2)
-              float cn = 0.f, mean = 0.f, m2 = 0.f;
-              for (int q = 0; q < nt; ++q) {
-                const float nb = (float)min(BN, N - q * BN);
-                const float mb = ld(q, 0);
-                const float m2b = ld(q, 1);
-                const float tot = cn + nb;
-                const float d = mb - mean;
-                mean += d * (nb / tot);
-                m2 += m2b + d * d * (cn * nb / tot);
-                cn = tot;
+            constexpr int BATCH = 16;
+            float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f;
+            for (int q0 = 0; q0 < nt; q0 += BATCH) {
+              float mb[BATCH], vb[BATCH];
+#pragma unroll
+              for (int u = 0; u < BATCH; ++u) {
+                const int q = min(q0 + u, nt - 1);  // clamped: always a valid slice
+                float* a = pb + (size_t)q * BM * 2;
+                if constexpr (LN) mb[u] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                vb[u] = __hip_atomic_load(a + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
+#pragma unroll
+              for (int u = 0; u < BATCH; ++u) {
+                if (q0 + u >= nt) break;
+                if constexpr (LN) {
+                  // Chan et al. pairwise merge of (count, mean, M2)
+                  const float nb = (float)min(BN, N - (q0 + u) * BN);
+                  const float tot = cn + nb;
+                  const float d = mb[u] - mean;
+                  mean += d * (nb / tot);
+                  m2 += vb[u] + d * d * (cn * nb / tot);
+                  cn = tot;
+                } else {
+                  ssum += vb[u];
+                }
+              }
+            }
+            if constexpr (LN) {
               stats[tid * 2 + 0] = mean;
               stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
             } else {
-              float s = 0.f;
-              for (int q = 0; q < nt; ++q) s += ld(q, 1);
               stats[tid * 2 + 0] = 0.f;
-              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(s / (float)N + p.eps);
+              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(ssum / (float)N + p.eps);
             }
           }
           __syncthreads();
