@@ -18,7 +18,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention]
+       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|copy]
 """
 
 import argparse
@@ -92,6 +92,17 @@ def main():
         return {k: float(np.median(v)) for k, v in res.items()}
 
     kernels = {}
+
+    if args.only == "copy":
+        # calibration for the HBM byte counters: a plain device copy of known size
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 3}), flush=True)
+        return
 
     # ---------------- headline: lazy pre-RMSNorm GEMM, LLM-MLP shape ---------------
     spec, d = inputs.make_inputs("prenorm_rms_mlp")
@@ -236,7 +247,8 @@ def main():
                    "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": profiled_traffic("prenorm")},
         "kernels": kernels,
     }
     if "prenorm_rms_mlp" in kernels:
@@ -245,6 +257,24 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, spec)
     print(json.dumps(out), flush=True)
+
+
+def profiled_traffic(workload):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the copy calibration), or None when the GEMM
+    source changed since those counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            t = json.load(f)
+        src = b"".join(open(os.path.join(ROOT, "attention_fng_prenorm_amd", "csrc", n), "rb").read()
+                       for n in ("fng_gemm.hip", "fng_device.h"))
+        if hashlib.sha256(src).hexdigest() != t["gemm_source_sha256"]:
+            return None
+        w = t["workloads"][workload]
+        return round(w["fetch_bytes"] + w["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def summarize(t, flops, norm_bytes, fused_bytes=None):
