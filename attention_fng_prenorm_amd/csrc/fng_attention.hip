@@ -6,16 +6,18 @@
 // softmax is the activation; there are no residual adds.  NORM=false gives the
 // plain attention baseline from the same code.
 //
-// Work split: one workgroup = 4 waves = 128 query rows of one (batch, head);
-// each wave owns 32 query rows for the whole kernel and loops over the keys in
-// tiles of 64 with an online (running max / running sum) softmax.
+// Work split: one workgroup = 8 waves (two per SIMD, so one wave's softmax
+// can issue while the other's MFMAs run) = 256 query rows of one (batch,
+// head); each wave owns 32 query rows for the whole kernel and loops over the
+// keys in tiles of 64 with an online (running max / running sum) softmax.
 //
 // Orientation: the score MFMA is issued as S^T = K * Q^T and the output MFMA as
 // O^T = V^T * P^T, so lane l always holds query row l % 32: the softmax row
 // max/sum, the LayerNorm and the RMSNorm are all in-lane sums plus one
 // exchange with lane l ^ 32.  The probabilities P stay in registers between
-// the two MFMAs: the key order in which a lane holds them is matched by the
-// rows the V fragment is read from (ds_read_b64_tr_b16 on V kept [key][d]).
+// the two MFMAs: the score MFMA's rows are loaded in a permuted key order so
+// that a lane holds them in the order the output MFMA consumes them, and V is
+// staged transposed so its fragments are plain row reads.
 //
 // Precision: MFMA operands are fp16 (K and V converted from bf16 while staged
 // into LDS, the normalized queries and the probabilities rounded to fp16),
@@ -44,19 +46,40 @@ struct AttnParams {
 };
 
 constexpr int kD = 128;
-constexpr int kBQ = 128;  // query rows per workgroup
-constexpr int kBK = 64;   // keys per tile
-constexpr int kTileBytes = kBK * kD * 2;
+constexpr int kWaves = 8;              // 2 per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBQ = 32 * kWaves;       // query rows per workgroup, 32 per wave
+constexpr int kBK = 64;                // keys per tile
+constexpr int kRowK = kD * 2 + 16;     // bytes per K row ([key][d]) in LDS, padded
+constexpr int kRowV = kBK * 2 + 16;    // bytes per V^T row ([d][key]) in LDS, padded
+constexpr int kTileK = kBK * kRowK;
+constexpr int kTileV = kD * kRowV;
+constexpr int kOffV = 2 * kTileK;      // LDS: K buffers 0/1, then V^T buffers 0/1
+constexpr int kChunks = kBK * kD / 8 / kThreads;  // 16-byte chunks per thread per tile
+// The running max of a row is only moved when a tile's max exceeds it by more
+// than this (log2 domain), so most tiles skip the accumulator rescale; the
+// probabilities stay below 2^kLazy, well inside fp16.
+constexpr float kLazy = 8.0f;
 
-// LDS chunk swizzles (16-byte chunks, 16 per 256-byte row, 64 banks of 4 B):
-// a K fragment read covers 16 consecutive keys at one chunk; a transposing V
-// read covers keys k..k+3 and four consecutive chunks.
-__device__ __forceinline__ int swz_k(int key) { return key & 15; }
-__device__ __forceinline__ int swz_v(int key) { return (key & 3) << 2; }
+// LDS layouts (64 banks of 4 B).  K is kept [key][d] and V transposed,
+// [d][key], both in fp16 and with every row padded by 16 bytes: a fragment
+// read (16 lanes on 16 consecutive rows at one 16-byte column) then covers all
+// banks, and a lane's offsets for the different fragments differ by constants.
+//
+// Key order: the score MFMA's A operand row m is loaded with key kappa(m)
+// (bits 2 and 3 of m swapped), which leaves lane (q, hi) of S^T holding, in
+// registers 8i..8i+7 of key block w, the eight consecutive keys
+// 32w + 16i + 8hi + (0..7): exactly the k-slots the output MFMA takes its
+// P^T operand in, so the probabilities go from one MFMA to the next without a
+// shuffle and V^T fragments are plain 16-byte row reads.
+__device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <bool B>
+using flag = std::integral_constant<bool, B>;
 
 template <bool NORM>
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K, V x 2 stages
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kTileK + 2 * kTileV];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -65,9 +88,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const uint32_t t = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = (int)(t % (uint32_t)p.tiles_q);
-  const int bh = (int)(t / (uint32_t)p.tiles_q);
+  const uint32_t t0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = (int)(t0 % (uint32_t)p.tiles_q);
+  const int bh = (int)(t0 / (uint32_t)p.tiles_q);
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int H = p.H, Sq = p.Sq, Skv = p.Skv;
@@ -79,175 +102,263 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.K + kbase, (uint32_t)((size_t)Skv * H * kD * 2));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.V + kbase, (uint32_t)((size_t)Skv * H * kD * 2));
 
-  // ---- queries: lane holds d = 16*kk + 8*hi + e of query row q -------------
+  // ---- queries: lane holds d = 16*kk + 8*hi + e of query row q, normalized
+  // (NORM) and pre-multiplied by sm_scale * log2(e) ---------------------------
   const int q = qt * kBQ + wave * 32 + l32;
-  const uint32_t qoff = (uint32_t)(((size_t)q * H + h) * kD * 2);
   u32x4_t qf[8];
   {
+    const uint32_t qoff = (uint32_t)(((size_t)q * H + h) * kD * 2);
     u32x4_t raw[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) raw[kk] = buffer_load16(qr, qoff + (uint32_t)(16 * kk + 8 * hi) * 2u);
+    float shift = 0.f, mul = p.scale_log2;
     if constexpr (NORM) {
       float s = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s += bf16lo(raw[kk][e]) + bf16hi(raw[kk][e]);
-      const float mean = xor_sum(s, 32) * (1.0f / kD);
+      const float mean = half_swap_sum(s) * (1.0f / kD);
       float s2 = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float a = bf16lo(raw[kk][e]) - mean, c = bf16hi(raw[kk][e]) - mean;
-          s2 += a * a + c * c;
+          const float x0 = bf16lo(raw[kk][e]) - mean, x1 = bf16hi(raw[kk][e]) - mean;
+          s2 += x0 * x0 + x1 * x1;
         }
-      const float rstd = __builtin_amdgcn_rsqf(xor_sum(s2, 32) * (1.0f / kD) + p.eps_ln);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          qf[kk][e] = pack_f16((bf16lo(raw[kk][e]) - mean) * rstd, (bf16hi(raw[kk][e]) - mean) * rstd);
+      const float rstd = __builtin_amdgcn_rsqf(half_swap_sum(s2) * (1.0f / kD) + p.eps_ln);
+      shift = mean;
+      mul = rstd * p.scale_log2;
       if (hi == 0 && q < Sq) {
         const size_t si = ((size_t)b * Sq + q) * H + h;
         if (p.ln_mean_out) p.ln_mean_out[si] = mean;
         if (p.ln_rstd_out) p.ln_rstd_out[si] = rstd;
       }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[kk][e] = bf16x2_to_f16x2(raw[kk][e]);
     }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qf[kk][e] = pack_f16((bf16lo(raw[kk][e]) - shift) * mul, (bf16hi(raw[kk][e]) - shift) * mul);
   }
 
-  // ---- K/V staging: 1024 chunks of 8 elements per tile, 4 per thread --------
-  u32x4_t rk[4], rv[4];
-  auto gload = [&](int kt) {
+  // ---- lane-constant LDS offsets -------------------------------------------
+  // K fragment (kk, w): key 32w + kappa(l32), d = 16kk + 8hi + (0..7)
+  const int koff = kappa(l32) * kRowK + hi * 16;
+  // V^T fragment (c, dt): d = 32dt + l32, keys 16c + 8hi + (0..7)
+  const int voff = l32 * kRowV + hi * 16;
+
+  // ---- K/V staging: 1024 chunks of 8 elements per tile and tensor ---------
+  // K: chunk c = tid + 512i is key c/16, d 8(c%16)..+7, stored as it is.
+  // V: thread holds keys 2p, 2p+1 (p = tid%32) at d 8(tid/32)..+7 and writes
+  // the transposed pairs, one 4-byte word per d row.
+  u32x4_t rk[kChunks], rv[kChunks];
+  auto gload_k = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + kThreads * i;
       const int key = kt * kBK + (c >> 4), dc = c & 15;
-      const uint32_t off = (uint32_t)((((size_t)key * H + h) * kD + dc * 8) * 2);
-      rk[i] = buffer_load16(kr, off);
-      rv[i] = buffer_load16(vr, off);
+      rk[i] = buffer_load16(kr, (uint32_t)((((size_t)key * H + h) * kD + dc * 8) * 2));
     }
   };
-  auto sstore = [&](int stage) {
-    FNG_LDS char* ks = lds + stage * (2 * kTileBytes);
-    FNG_LDS char* vs = ks + kTileBytes;
+  auto gload_v = [&](int kt) __attribute__((always_inline)) {
+    const int key = kt * kBK + 2 * (tid & 31), dc = tid >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c >> 4, dc = c & 15;
-      u32x4_t k16, v16;
+    for (int i = 0; i < 2; ++i)
+      rv[i] = buffer_load16(vr, (uint32_t)((((size_t)(key + i) * H + h) * kD + dc * 8) * 2));
+  };
+  auto sstore_k = [&](int buf) __attribute__((always_inline)) {
+    FNG_LDS char* dst = lds + buf * kTileK;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k16[e] = bf16x2_to_f16x2(rk[i][e]);
-        v16[e] = bf16x2_to_f16x2(rv[i][e]);
-      }
-      lds_write16(ks + key * (kD * 2) + ((dc ^ swz_k(key)) & 15) * 16, k16);
-      lds_write16(vs + key * (kD * 2) + ((dc ^ swz_v(key)) & 15) * 16, v16);
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = tid + kThreads * i;
+      u32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(rk[i][e]);
+      lds_write16(dst + (c >> 4) * kRowK + (c & 15) * 16, v);
+    }
+  };
+  auto sstore_v = [&](int buf) __attribute__((always_inline)) {
+    FNG_LDS char* dst = lds + kOffV + buf * kTileV + (tid >> 5) * 8 * kRowV + (tid & 31) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<FNG_LDS uint32_t*>(dst + (2 * e) * kRowV) = pack_f16(bf16lo(rv[0][e]), bf16lo(rv[1][e]));
+      *reinterpret_cast<FNG_LDS uint32_t*>(dst + (2 * e + 1) * kRowV) = pack_f16(bf16hi(rv[0][e]), bf16hi(rv[1][e]));
     }
   };
 
+  // ---- running state -------------------------------------------------------
   f32x16_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float mrun = -INFINITY;  // running max (log2 domain) of query row q
+  float mrun = -INFINITY;  // running max (log2 domain) of row q
   float lrun = 0.f;        // this lane's share of the running sum
 
-  const int ntiles = (Skv + kBK - 1) / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) gload(kt + 1);
-    const FNG_LDS char* ks = lds + stage * (2 * kTileBytes);
-    const FNG_LDS char* vs = ks + kTileBytes;
-
-    // S^T for keys 32*u + (0..31): register r <-> key 32u + 8(r/4) + 4hi + r%4
-    f32x16_t s[2];
+  // S^T = K Q^T for keys 32w + (0..31): register r <-> key 32w + 16(r/8) + 8hi + r%8.
+  // Fragment i = 2kk + w; reads run kPre fragments ahead of the MFMAs.
+  constexpr int kPre = 4;
+  auto qk = [&](int t, f32x16_t(&s)[2]) __attribute__((always_inline)) {
+    const FNG_LDS char* kb = lds + (t & 1) * kTileK + koff;
+    auto rd = [&](int i) { return lds_read16(kb + (i >> 1) * 32 + (i & 1) * 32 * kRowK); };
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int w = 0; w < 2; ++w)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[u][r] = 0.f;
-      const int key = 32 * u + l32;
+      for (int r = 0; r < 16; ++r) s[w][r] = 0.f;
+    u32x4_t kf[kPre];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int dc = 2 * kk + hi;
-        const u32x4_t kf = lds_read16(ks + key * (kD * 2) + ((dc ^ swz_k(key)) & 15) * 16);
-        s[u] = mfma_f16(kf, qf[kk], s[u]);
-      }
+    for (int i = 0; i < kPre; ++i) kf[i] = rd(i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i & 1] = mfma_f16(kf[i % kPre], qf[i >> 1], s[i & 1]);
+      if (i + kPre < 16) kf[i % kPre] = rd(i + kPre);
     }
-
-    // online softmax in the log2 domain
-    const int kvalid = Skv - kt * kBK;  // >= 1
-    float mx = -INFINITY;
+  };
+  // O^T += V^T P^T; fragment i = 4c + dt, read kPre fragments ahead
+  auto pv = [&](int t, const u32x4_t(&pf)[4]) __attribute__((always_inline)) {
+    const FNG_LDS char* vb = lds + kOffV + (t & 1) * kTileV + voff;
+    auto rd = [&](int i) { return lds_read16(vb + (i >> 2) * 32 + (i & 3) * 32 * kRowV); };
+    u32x4_t vf[kPre];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < kPre; ++i) vf[i] = rd(i);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * u + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float v = s[u][r] * p.scale_log2;
-        if (key >= kvalid) v = -INFINITY;
-        s[u][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = xor_max(mx, 32);
-    const float mnew = fmaxf(mrun, mx);
-    const float alpha = exp2f(mrun - mnew);
+    for (int i = 0; i < 16; ++i) {
+      o[i & 3] = mfma_f16(vf[i % kPre], pf[i >> 2], o[i & 3]);
+      if (i + kPre < 16) vf[i % kPre] = rd(i + kPre);
+    }
+  };
+  // softmax, first half: mask the keys past the end, row max, running max
+  // update, rescale of l and o when the max moved
+  auto sm_max = [&](f32x16_t(&s)[2], int t, bool mask) __attribute__((always_inline)) {
+    if (mask) {
+      const int kvalid = Skv - t * kBK;
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * w + 16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) s[w][r] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[w][r]);
+    mx = half_swap_max(mx);
+    const float mold = mrun;
+    const float mnew = mx > mold + kLazy ? mx : mold;
+    const float alpha = (mnew == mold || mold == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mold - mnew);
     mrun = mnew;
-    float ls = 0.f;
+    lrun *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    }
+  };
+  // softmax, second half: probabilities relative to the running max, row sum,
+  // fp16 pack as the B operand: k16 step c holds keys 16c + 8hi + (0..7)
+  auto sm_exp = [&](f32x16_t(&s)[2], u32x4_t(&pf)[4]) __attribute__((always_inline)) {
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[u][r] - mnew);
-        s[u][r] = e;
-        ls += e;
+        const float e = __builtin_amdgcn_exp2f(s[w][r] - mrun);
+        s[w][r] = e;
+        ls[r & 3] += e;
       }
-    lrun = lrun * alpha + ls;
+    lrun += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    for (int c = 0; c < 4; ++c) {
+      const int w = c >> 1, r0 = 8 * (c & 1);
+      pf[c] = u32x4_t{pack_f16(s[w][r0 + 0], s[w][r0 + 1]), pack_f16(s[w][r0 + 2], s[w][r0 + 3]),
+                      pack_f16(s[w][r0 + 4], s[w][r0 + 5]), pack_f16(s[w][r0 + 6], s[w][r0 + 7])};
+    }
+  };
 
-    // P^T as the B operand: k16 step c holds keys 16c + 4hi + (0..3) in slots
-    // 0..3 and 16c + 8 + 4hi + (0..3) in slots 4..7
-    u32x4_t pf[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int u = c >> 1, r0 = 8 * (c & 1);
-      pf[c] = u32x4_t{pack_f16(s[u][r0 + 0], s[u][r0 + 1]), pack_f16(s[u][r0 + 2], s[u][r0 + 3]),
-                      pack_f16(s[u][r0 + 4], s[u][r0 + 5]), pack_f16(s[u][r0 + 6], s[u][r0 + 7])};
+  const int ntiles = (Skv + kBK - 1) / kBK;
+  const bool ragged = (Skv % kBK) != 0;
+
+  // Software pipeline over key tiles: iteration t computes the scores of tile
+  // t and the softmax and output update of tile t - 1.  K(t) and V(t - 1) are
+  // resident together; K(t + 1) and V(t) are staged during iteration t into
+  // the buffers freed by iteration t - 1.
+  //
+  // The two waves that share a SIMD (w and w + 4) run the iteration's phases
+  // in different orders, so that while one is in its VALU-heavy softmax the
+  // other issues MFMAs:
+  //   waves 0-3: softmax(t - 1), O += V(t - 1) P(t - 1), S(t) = K(t) Q^T
+  //   waves 4-7: S(t) = K(t) Q^T, softmax(t - 1), O += V(t - 1) P(t - 1)
+  // (next_known: tile t + 1 is known to exist.)
+  f32x16_t sa[2], sb[2];
+  u32x4_t pf[4];
+  auto iter = [&](auto order_a, auto has_prev, auto has_cur, auto maskable, auto next_known, int t,
+                  f32x16_t(&s_prev)[2], f32x16_t(&s_cur)[2]) __attribute__((always_inline)) {
+    constexpr bool A = decltype(order_a)::value;
+    constexpr bool PREV = decltype(has_prev)::value;
+    constexpr bool CUR = decltype(has_cur)::value;
+    constexpr bool MASKABLE = decltype(maskable)::value;
+    const bool next_k = decltype(next_known)::value || (CUR && t + 1 < ntiles);
+    const bool mask_prev = MASKABLE && ragged && t - 1 == ntiles - 1;
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    if (next_k) gload_k(t + 1);
+    if constexpr (CUR) gload_v(t);
+    if constexpr (!A && CUR) {
+      qk(t, s_cur);
+      fence();
     }
-    // O^T += V^T P^T; V fragment rows are the same keys, read transposed
-    const int g = lane >> 4, li = lane & 15;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int key0 = 16 * c + 4 * (g >> 1) + (li >> 2);
-      const int key1 = key0 + 8;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = 32 * dt + 16 * (g & 1) + 4 * (li & 3);
-        const int dc = d >> 3, db = (d & 7) * 2;
-        const u32x2_t a = lds_read_tr16(vs + key0 * (kD * 2) + ((dc ^ swz_v(key0)) & 15) * 16 + db);
-        const u32x2_t bb = lds_read_tr16(vs + key1 * (kD * 2) + ((dc ^ swz_v(key1)) & 15) * 16 + db);
-        o[dt] = mfma_f16(u32x4_t{a[0], a[1], bb[0], bb[1]}, pf[c], o[dt]);
-      }
+    if constexpr (PREV) {
+      sm_max(s_prev, t - 1, mask_prev);
+      sm_exp(s_prev, pf);
+      fence();
+      pv(t - 1, pf);
+      fence();
     }
-    if (more) sstore(stage ^ 1);
-    __syncthreads();
-  }
+    if constexpr (A && CUR) {
+      qk(t, s_cur);
+      fence();
+    }
+    if constexpr (CUR) {
+      if (next_k) sstore_k((t + 1) & 1);
+      sstore_v(t & 1);
+      __syncthreads();
+    }
+  };
+
+  auto pipeline = [&](auto order_a) __attribute__((always_inline)) {
+    iter(order_a, flag<false>{}, flag<true>{}, flag<true>{}, flag<false>{}, 0, sb, sa);
+    int t = 1;
+    for (; t + 1 < ntiles - 1; t += 2) {
+      iter(order_a, flag<true>{}, flag<true>{}, flag<false>{}, flag<true>{}, t, sa, sb);
+      iter(order_a, flag<true>{}, flag<true>{}, flag<false>{}, flag<true>{}, t + 1, sb, sa);
+    }
+    if (t < ntiles - 1) {
+      iter(order_a, flag<true>{}, flag<true>{}, flag<false>{}, flag<true>{}, t, sa, sb);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) sa[w] = sb[w];
+      ++t;
+    }
+    if (t == ntiles - 1) {
+      iter(order_a, flag<true>{}, flag<true>{}, flag<true>{}, flag<false>{}, t, sa, sb);
+      iter(order_a, flag<true>{}, flag<false>{}, flag<true>{}, flag<false>{}, t + 1, sb, sa);
+    } else {  // a single key tile: its scores are in sa
+      iter(order_a, flag<true>{}, flag<false>{}, flag<true>{}, flag<false>{}, t, sa, sb);
+    }
+  };
+
+  gload_k(0);
+  sstore_k(0);
+  __syncthreads();
+  if (wave < 4)
+    pipeline(flag<true>{});
+  else
+    pipeline(flag<false>{});
 
   // ---- epilogue: 1/l, RMSNorm over d, bf16 store -------------------------
-  const float inv = 1.0f / xor_sum(lrun, 32);
+  const float inv = 1.0f / half_swap_sum(lrun);
   float rstd = 1.f;
   if constexpr (NORM) {
     float ss = 0.f;
@@ -258,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {
         const float v = o[i][r] * inv;
         ss += v * v;
       }
-    rstd = __builtin_amdgcn_rsqf(xor_sum(ss, 32) * (1.0f / kD) + p.eps_rms);
+    rstd = __builtin_amdgcn_rsqf(half_swap_sum(ss) * (1.0f / kD) + p.eps_rms);
     if (hi == 0 && q < Sq && p.rms_rstd_out) p.rms_rstd_out[((size_t)b * Sq + q) * H + h] = rstd;
   }
   if (q >= Sq) return;
@@ -270,10 +381,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnParams p) {
       const int d = 32 * dt + 8 * r4 + 4 * hi;
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = o[dt][4 * r4 + e] * inv;
-        if constexpr (NORM) v[e] = (v[e]) * rstd;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * r4 + e] * inv * rstd;
       *reinterpret_cast<u32x2_t*>(orow + d) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
 }
@@ -297,9 +405,9 @@ int launch_attention(const AttnCall& c, bool norm, hipStream_t s) {
   p.tiles_q = (p.Sq + kBQ - 1) / kBQ;
   p.total = p.tiles_q * p.H * p.B;
   if (norm)
-    hipLaunchKernelGGL(attention_kernel<true>, dim3(p.total), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attention_kernel<true>, dim3(p.total), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(attention_kernel<false>, dim3(p.total), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attention_kernel<false>, dim3(p.total), dim3(kThreads), 0, s, p);
   return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
 }
 

@@ -127,6 +127,19 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const FNG_LDS char* p) {
 __device__ __forceinline__ float xor_sum(float v, int mask) { return v + __shfl_xor(v, mask); }
 __device__ __forceinline__ float xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
 
+// combine lane l with lane l ^ 32 without going through LDS
+// (v_permlane32_swap exchanges the upper half of one operand with the lower
+// half of the other; with both operands equal, the two results hold v[l] and
+// v[l ^ 32], so both lanes of a pair get the same combined value)
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------------------------
 // workgroup -> tile remap so that consecutive logical tiles run on one XCD.
 // Workgroups are dispatched round-robin over the 8 XCDs; slot s of XCD x
