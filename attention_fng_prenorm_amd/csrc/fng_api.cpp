@@ -115,10 +115,11 @@ int check_attn(const void* Q, const void* K, const void* V, const void* O, int64
   if (B == 0 || Sq == 0 || H == 0) return FNG_OK;
   if (!Q || !K || !V || !O) return FNG_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FNG_ERR_MISALIGNED;
-  // per-batch 32-bit buffer ranges (with one tile of overrun) and the grid size
-  if ((Sq + 128) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  // per-batch 32-bit buffer ranges (with one tile of overrun: 256 query rows,
+  // 64 key rows) and the grid size
+  if ((Sq + 256) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
   if ((Skv + 64) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
-  if (B * H * ((Sq + 127) / 128) >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if (B * H * ((Sq + 255) / 256) >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
   return FNG_OK;
 }
 

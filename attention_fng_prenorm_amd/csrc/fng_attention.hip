@@ -261,22 +261,23 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   // softmax, second half: probabilities relative to the running max, row sum,
   // fp16 pack as the B operand: k16 step c holds keys 16c + 8hi + (0..7)
   auto sm_exp = [&](f32x16_t(&s)[2], u32x4_t(&pf)[4]) __attribute__((always_inline)) {
+    // row sum over the fp16 probabilities the output MFMA consumes, two per
+    // v_dot2 (the operand is taken from the fp16 pair itself, not re-read out
+    // of the packed vector)
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < 2; ++w)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[w][r] - mrun);
-        s[w][r] = e;
-        ls[r & 3] += e;
-      }
-    lrun += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int w = c >> 1, r0 = 8 * (c & 1);
-      pf[c] = u32x4_t{pack_f16(s[w][r0 + 0], s[w][r0 + 1]), pack_f16(s[w][r0 + 2], s[w][r0 + 3]),
-                      pack_f16(s[w][r0 + 4], s[w][r0 + 5]), pack_f16(s[w][r0 + 6], s[w][r0 + 7])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2_t h2 = {(_Float16)__builtin_amdgcn_exp2f(s[w][r0 + 2 * e] - mrun),
+                            (_Float16)__builtin_amdgcn_exp2f(s[w][r0 + 2 * e + 1] - mrun)};
+        pf[c][e] = __builtin_bit_cast(uint32_t, h2);
+        ls[e] = __builtin_amdgcn_fdot2(h2, ones, ls[e], false);
+      }
     }
+    lrun += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   const int ntiles = (Skv + kBK - 1) / kBK;

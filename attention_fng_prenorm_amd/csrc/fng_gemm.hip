@@ -24,11 +24,12 @@
 // output row m = l % 32 and 16 columns, which keeps every row reduction of the
 // norm epilogues inside a lane plus one lane-pair exchange.
 //
-// Staging: X and W tiles go HBM -> VGPR (buffer loads, out-of-range rows read
-// as 0) -> LDS, double-buffered with one barrier per K tile.  X is kept
-// [m][k] (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as
-// in memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte
-// chunks are XOR-swizzled per row so fragment reads are bank-conflict free.
+// Staging: X and W tiles are copied HBM -> LDS directly (buffer_load ... lds,
+// out-of-range rows and tails read as 0) through a 4-stage ring with one
+// barrier per K tile.  X is kept [m][k] (k contiguous) and read with
+// ds_read_b128; W is kept [k][n] exactly as in memory and read k-contiguous per
+// lane with ds_read_b64_tr_b16.  16-byte chunks are XOR-swizzled per row so
+// fragment reads are bank-conflict free.
 #include "fng_device.h"
 #include "fng_internal.h"
 

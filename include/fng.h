@@ -123,7 +123,8 @@ int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* s
  * sm_scale <= 0 selects 1/sqrt(D).  Optional fp32 [B, Sq, H] statistics outputs.
  * K and V magnitudes must be below 65504 (the kernel multiplies in fp16 with
  * fp32 accumulation; bf16 inputs in that range convert to fp16 exactly down to
- * 2^-14).
+ * 2^-14).  The normalized queries are pre-multiplied by sm_scale * log2(e)
+ * before their fp16 rounding.
  * ------------------------------------------------------------------------- */
 int fng_norm_attention(const void* Q, const void* K, const void* V, void* out,
                        float* ln_mean_out, float* ln_rstd_out, float* rms_rstd_out,
@@ -144,7 +145,8 @@ int fng_layernorm(const void* X, void* Y, float* mean_out, float* rstd_out, int6
 int fng_gemm(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
              void* stream);
 /* out = softmax(Q K^T * sm_scale) V, BSHD, D == 128, same kernel as
- * fng_norm_attention without the two norms. */
+ * fng_norm_attention without the two norms.  Q * sm_scale * log2(e), K and V
+ * must stay below 65504 in magnitude (fp16 MFMA operands). */
 int fng_attention(const void* Q, const void* K, const void* V, void* out, int64_t B,
                   int64_t Sq, int64_t Skv, int64_t H, int64_t D, float sm_scale,
                   void* stream);
