@@ -92,17 +92,31 @@ __device__ __forceinline__ f32x16_t mfma_f16(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// sum of squares of 8 bf16 held in a 16-byte vector, accumulated into acc with
-// fp32 FMAs (bf16 -> fp32 is exact).  The packed bf16 dot instruction is not
-// used: measured on gfx950 it does not return the fp32-accurate sum.
+// sum of squares of 8 bf16 held in a 16-byte vector, accumulated into acc:
+// one v_dot2_f32_bf16 per pair (products exact in fp32, fp32 accumulation;
+// measured on gfx950 to agree with an fp32 FMA chain to 3e-6 relative over
+// 4096 terms).  Each word is first copied to a scalar: a bit-cast applied
+// directly to an element of the vector was compiled as element 0 for every
+// element (this toolchain), which silently drops 3/4 of the sum.
 __device__ __forceinline__ float sumsq_bf16x8(u32x4_t v, float acc) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = bf16lo(v[i]), b = bf16hi(v[i]);
-    acc = fmaf(a, a, acc);
-    acc = fmaf(b, b, acc);
+    const uint32_t w = v[i];
+    const bf16x2_t p = __builtin_bit_cast(bf16x2_t, w);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
   }
   return acc;
+}
+
+// the same into two accumulators (words 0, 2 -> a0; 1, 3 -> a1)
+__device__ __forceinline__ void sumsq_bf16x8_2(u32x4_t v, float& a0, float& a1) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    const bf16x2_t p = __builtin_bit_cast(bf16x2_t, w);
+    if (i % 2 == 0) a0 = __builtin_amdgcn_fdot2_f32_bf16(p, p, a0, false);
+    else a1 = __builtin_amdgcn_fdot2_f32_bf16(p, p, a1, false);
+  }
 }
 
 // ---------------------------------------------------------------------------

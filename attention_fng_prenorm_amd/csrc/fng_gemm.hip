@@ -290,9 +290,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    float ss[SS_SLOTS];
+    float ss[SS_SLOTS][2];  // two partial sums per slot: two short dependency chains
 #pragma unroll
-    for (int s = 0; s < SS_SLOTS; ++s) ss[s] = 0.f;
+    for (int s = 0; s < SS_SLOTS; ++s) ss[s][0] = ss[s][1] = 0.f;
 
     // one k16 slice of fragments: X rows of this wave, W columns of this wave
     // (and the matching gamma slice)
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       if constexpr (EPI == EPI_PRENORM) {
         if (ss_owner) {
 #pragma unroll
-          for (int s = 0; s < SS_SLOTS; ++s) ss[s] = sumsq_bf16x8(f.x[s], ss[s]);
+          for (int s = 0; s < SS_SLOTS; ++s) sumsq_bf16x8_2(f.x[s], ss[s][0], ss[s][1]);
         }
       }
       if constexpr (GAMMA) {
@@ -334,6 +334,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(f.w[j], f.x[i], acc[i][j]);
+      if constexpr (EPI == EPI_PRENORM && !GAMMA) {
+        // the sum-of-squares dots go ahead of the slice's MFMAs: placed
+        // between MFMAs they cost more (measured on gfx950, where a dot
+        // issued behind an MFMA stalls the next MFMA of the wave)
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * SS_SLOTS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
+      }
     };
 
     // ---- mainloop: 4-deep ring of K tiles, one barrier per tile ------------
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       FNG_LDS float* red = (FNG_LDS float*)lds;
 #pragma unroll
       for (int s = 0; s < SS_SLOTS; ++s) {
-        const float tot = xor_sum(ss[s], 32);
+        const float tot = xor_sum(ss[s][0] + ss[s][1], 32);
         if (ss_owner && hi == 0) red[lrow(s)] = tot;
       }
       __syncthreads();
