@@ -67,9 +67,14 @@ Workspace layout(void* base, int64_t M, int64_t N) {
   return w;
 }
 
-int resolve_path(int path, int64_t M, int64_t N) {
+// automatic choice, from the measured post-LayerNorm sweep over M = 256k rows
+// and K, N in 64..2048: one workgroup across N wins up to N = 256, and at
+// N = 512 while K <= 512; beyond that the split-N exchange wins
+bool auto_fulln(int64_t N, int64_t K) { return N <= 256 || (N <= fng::fulln_max_n() && K <= 512); }
+
+int resolve_path(int path, int64_t M, int64_t N, int64_t K) {
   if (path == FNG_PATH_AUTO) {
-    if (N <= fng::fulln_max_n()) return FNG_PATH_FULLN;
+    if (auto_fulln(N, K)) return FNG_PATH_FULLN;
     if (fng::splitn_feasible(M, N)) return FNG_PATH_SPLITN;
     return FNG_PATH_TWOPASS;
   }
@@ -84,7 +89,7 @@ int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, fl
   if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
   if (m_or_n_empty(M, N)) return FNG_OK;
   if ((mean_out && !aligned16(mean_out)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
-  path = resolve_path(path, M, N);
+  path = resolve_path(path, M, N, K);
   GemmCall c{X, W, nullptr, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
   if (path == FNG_PATH_FULLN) {
     if (N > fng::fulln_max_n()) return FNG_ERR_UNSUPPORTED;
@@ -143,10 +148,9 @@ FNG_EXPORT const char* fng_status_string(int status) {
 FNG_EXPORT int64_t fng_fulln_max_n(void) { return fng::fulln_max_n(); }
 
 FNG_EXPORT size_t fng_gemm_postnorm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path) {
-  (void)K;
   if (M <= 0 || N <= 0) return 0;
   if (path == FNG_PATH_FULLN) return 0;
-  if (path == FNG_PATH_AUTO && N <= fng::fulln_max_n()) return 0;
+  if (path == FNG_PATH_AUTO && auto_fulln(N, K)) return 0;
   return layout(nullptr, M, N).bytes;
 }
 

@@ -728,11 +728,15 @@ bool small_problem(const GemmCall& c) { return c.M * c.N <= 256LL * 256 * 64; }
 int64_t splitn_tiles_m(int64_t M) { return (M + kBigBM - 1) / kBigBM; }
 int64_t splitn_tiles_n(int64_t N) { return (N + kBigBN - 1) / kBigBN; }
 int64_t splitn_bm() { return kBigBM; }
-int64_t fulln_max_n() { return 256; }
+int64_t fulln_max_n() { return 512; }
 
 int launch_gemm(const GemmCall& c, hipStream_t s) {
   GemmParams p = base_params(c);
   if (small_problem(c)) return launch<64, 64, 64, 2, 2, EPI_PLAIN, false, false>(p, 0, false, s);
+  // narrow outputs with many rows: the same tall tiles as the full-N post-norm,
+  // so the unfused baseline is not handicapped by 256-wide tiles on N <= 128
+  if (c.M >= 256 * 256 && c.N <= 64) return launch<256, 64, 64, 4, 2, EPI_PLAIN, false, false>(p, 0, false, s);
+  if (c.M >= 256 * 256 && c.N <= 128) return launch<256, 128, 32, 2, 4, EPI_PLAIN, false, false>(p, 0, false, s);
   return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PLAIN, false, false>(p, 0, false, s);
 }
 
@@ -749,9 +753,26 @@ int launch_prenorm(const GemmCall& c, hipStream_t s) {
 
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
   GemmParams p = base_params(c);
-  // one workgroup spans all N (<= 256): 32 rows x 256 columns, waves side by side along N
-  return ln ? launch<32, 256, 64, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
-            : launch<32, 256, 64, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
+  // one workgroup spans all N.  With enough rows for >= 256 workgroups of 256
+  // rows, tall tiles (W is re-read from L2 once per row block, so tall tiles
+  // keep that traffic small): N <= 64: 256 x 64, BK 64; N <= 128: 256 x 128;
+  // N <= 256: 256 x 256.  Fewer rows: 32 x 256 tiles, so the grid still fills
+  // the GPU.  N <= 512: 64 x 512 (taller accumulators would not fit).
+  const bool tall = c.M >= 256 * 256;
+  if (tall && c.N <= 64)
+    return ln ? launch<256, 64, 64, 4, 2, EPI_FULLN, true, false>(p, 0, false, s)
+              : launch<256, 64, 64, 4, 2, EPI_FULLN, false, false>(p, 0, false, s);
+  if (tall && c.N <= 128)
+    return ln ? launch<256, 128, 32, 2, 4, EPI_FULLN, true, false>(p, 0, false, s)
+              : launch<256, 128, 32, 2, 4, EPI_FULLN, false, false>(p, 0, false, s);
+  if (tall && c.N <= 256)
+    return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN, true, false>(p, 0, false, s)
+              : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN, false, false>(p, 0, false, s);
+  if (c.N <= 256)
+    return ln ? launch<32, 256, 64, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
+              : launch<32, 256, 64, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
+  return ln ? launch<64, 512, 32, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
+            : launch<64, 512, 32, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
 }
 
 int splitn_feasible(int64_t M, int64_t N) {

@@ -13,12 +13,14 @@ workload shape (post-LayerNorm GEMM with one workgroup across N, the affine
 pre-RMSNorm variant, post-RMSNorm GEMM with the split-N exchange and its
 two-pass fallback, and the norm-sandwiched attention) with the unfused
 baselines they replace, timed interleaved, and the "norm latency hidden"
-figure (T_gemm + T_norm - T_fused) / T_norm of the pages.  The roofline object
+figure (T_gemm + T_norm - T_fused) / T_norm of the pages; and the pages'
+ads-shape sweep of the post-LayerNorm GEMM (M = 256k rows, K and N from 64 to
+2048).  The roofline object
 describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|copy]
+       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|ads|copy]
 """
 
 import argparse
@@ -228,6 +230,58 @@ def main():
             "saving_pct_of_unfused_total": round(100.0 * (base - t["fused"]) / base, 1),
         }
         del qsets, O, Qn, Oa
+
+    # ---------------- ads-shape sweep: post-LayerNorm GEMM, M = 256k rows ---------
+    # K and N from 64 to 2048 (the pages' sweep of the naive full-N regime at small
+    # N and the multi-CTA regime above it); synthetic normal inputs drawn on the
+    # device (timing only; the parity tests cover these shapes at 2048 rows)
+    if args.only in (None, "ads"):
+        Ms = 262144
+        dims = [64, 128, 256, 512, 1024, 2048]
+        gen = torch.Generator(device="cuda").manual_seed(2026)
+        fused_us, unfused_us, hidden, paths = [], [], [], []
+        for Ka in dims:
+            Xa = torch.randn(Ms, Ka, device="cuda", generator=gen).to(torch.bfloat16)
+            rf, ru, rh, rp = [], [], [], []
+            for Na in dims:
+                Wa = (torch.randn(Ka, Na, device="cuda", generator=gen) / math.sqrt(Ka)).to(torch.bfloat16)
+                Ya = torch.empty(Ms, Na, dtype=torch.bfloat16, device="cuda")
+                Za = torch.empty_like(Ya)
+                nb = B.fng_gemm_postnorm_workspace_bytes(Ms, Na, Ka, B.FNG_PATH_AUTO)
+                wsa = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda") if nb else None
+                fns = {
+                    "fused": lambda i: B.fng_gemm_postnorm_ln(Xa, Wa, Ya, 1e-5, wsa),
+                    "gemm": lambda i: B.fng_gemm(Xa, Wa, Za),
+                    "norm": lambda i: B.fng_layernorm(Za, Ya, 1e-5),
+                }
+                if args.only == "ads":  # every path where it applies, to place the automatic choice
+                    nbs = B.fng_gemm_postnorm_workspace_bytes(Ms, Na, Ka, B.FNG_PATH_SPLITN)
+                    wss = torch.zeros(nbs, dtype=torch.uint8, device="cuda")
+                    fns["splitn"] = lambda i: B.fng_gemm_postnorm_ln(Xa, Wa, Ya, 1e-5, wss, B.FNG_PATH_SPLITN)
+                    fns["twopass"] = lambda i: B.fng_gemm_postnorm_ln(Xa, Wa, Ya, 1e-5, wss, B.FNG_PATH_TWOPASS)
+                    if Na <= B.fng_fulln_max_n():
+                        fns["fulln"] = lambda i: B.fng_gemm_postnorm_ln(Xa, Wa, Ya, 1e-5, None, B.FNG_PATH_FULLN)
+                t = time_batches(fns, 3, 5)
+                if args.only == "ads":
+                    log(f"  K={Ka} N={Na}: " + " ".join(f"{k} {v:.1f}" for k, v in t.items()))
+                rf.append(round(t["fused"], 1))
+                ru.append(round(t["gemm"] + t["norm"], 1))
+                rh.append(round(100.0 * (t["gemm"] + t["norm"] - t["fused"]) / t["norm"], 1))
+                rp.append("fulln" if Na <= B.fng_fulln_max_n() else "splitn")
+                del Wa, Ya, Za, wsa
+            fused_us.append(rf)
+            unfused_us.append(ru)
+            hidden.append(rh)
+            paths.append(rp)
+            del Xa
+            torch.cuda.empty_cache()
+        kernels["ads_sweep_postnorm_ln"] = {
+            "M": Ms, "K_rows": dims, "N_cols": dims, "path": paths,
+            "fused_us": fused_us, "unfused_us": unfused_us, "norm_hidden_pct": hidden,
+        }
+        log("ads sweep post-LN (M=262144): rows K, columns N, norm latency hidden %")
+        for Ka, rh in zip(dims, hidden):
+            log(f"  K={Ka:5d}: " + " ".join(f"{h:7.1f}" for h in rh))
 
     out = {
         "metric": "fused norm+GEMM TFLOP/s & % bf16 MFMA peak; % unfused norm latency hidden",

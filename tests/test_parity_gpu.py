@@ -141,6 +141,78 @@ def test_postnorm_paths_ragged(ln, path):
 
 
 @pytest.mark.parametrize("ln", [True, False])
+@pytest.mark.parametrize("N", [264, 392, 512])
+def test_postnorm_fulln_wide(ln, N):
+    """Full-N path with one workgroup across 256 < N <= 512 (64 x 512 tiles)."""
+    M, K = 700, 520
+    assert N <= B.fng_fulln_max_n()
+    spec, d = inputs.make_inputs("postnorm_rms_largen", M=M, K=K, N=N, seed=4242)
+    log(f"postnorm full-N wide ln={ln} M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, 1e-5, M, N, K, ln, B.FNG_PATH_FULLN)
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"]), f64(d["W"]), 1e-5, "ln" if ln else "rms")
+    assert_parity(host(Y), ref, f"post-{'LN' if ln else 'RMS'} full-N N={N}")
+    assert_close_stats(r.cpu().numpy(), rref, "rstd")
+    if ln:
+        assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
+
+
+# the pages' ads-shape sweep (M = 256k rows, K and N from 64 to 2048), here at
+# 2048 rows so the oracle runs in seconds; the path is chosen automatically
+ADS_KN = [(64, 64), (128, 128), (2048, 64), (64, 512), (512, 512), (2048, 512), (256, 1024), (512, 2048),
+          (2048, 2048)]
+
+
+@pytest.mark.parametrize("K,N", ADS_KN, ids=[f"K{k}_N{n}" for k, n in ADS_KN])
+def test_postnorm_ads_shapes(K, N):
+    M = 2048
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=K * 7 + N)
+    log(f"ads shape post-LN M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, 1e-5, M, N, K, True, B.FNG_PATH_AUTO)
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"]), f64(d["W"]), 1e-5, "ln")
+    assert_parity(host(Y), ref, f"ads post-LN K={K} N={N}")
+    assert_close_stats(r.cpu().numpy(), rref, "rstd")
+    assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
+
+
+@pytest.mark.parametrize("ln", [True, False])
+@pytest.mark.parametrize("N", [40, 64, 104, 200])
+def test_postnorm_fulln_tall_tiles(ln, N):
+    """Full-N with 256-row tiles (used from 65536 rows on), ragged M, K and N;
+    sampled rows against the oracle plus the row property on every row."""
+    M, K = 65536 + 72, 136
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=N + 5)
+    log(f"postnorm full-N tall ln={ln} M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, 1e-5, M, N, K, ln, B.FNG_PATH_FULLN)
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 73, M - 1], rng.choice(M, 48, replace=False)]))
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"][rows]), f64(d["W"]), 1e-5, "ln" if ln else "rms")
+    assert_parity(host(Y[torch.as_tensor(rows, device="cuda")]), ref, f"full-N tall N={N}")
+    assert_close_stats(r.cpu().numpy()[rows], rref, "rstd sampled")
+    y = Y.float()
+    if ln:
+        assert np.max(np.abs(mu.cpu().numpy()[rows] - mref)) < 2e-4
+        # zero mean, unit variance per row (up to eps and bf16 rounding)
+        assert torch.max(torch.abs(y.mean(dim=1))).item() < 2e-2
+        assert torch.max(torch.abs(y.var(dim=1, unbiased=False) - 1.0)).item() < 2e-2
+    else:
+        assert torch.max(torch.abs(torch.sqrt((y * y).mean(dim=1)) - 1.0)).item() < 1e-2
+
+
+def test_postnorm_ads_full_rows_sampled():
+    """One ads shape at its full 256k rows, sampled rows against the oracle."""
+    M, K, N = 262144, 512, 512
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=262)
+    log(f"ads shape full rows post-LN M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, 1e-5, M, N, K, True, B.FNG_PATH_AUTO)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, 63, 64, M - 1], rng.choice(M, 64, replace=False)]))
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"][rows]), f64(d["W"]), 1e-5, "ln")
+    assert_parity(host(Y[torch.as_tensor(rows, device="cuda")]), ref, "ads full rows sampled")
+    assert_close_stats(r.cpu().numpy()[rows], rref, "rstd sampled")
+    assert np.max(np.abs(mu.cpu().numpy()[rows] - mref)) < 2e-4
+
+
+@pytest.mark.parametrize("ln", [True, False])
 def test_postnorm_three_paths_agree_at_n256(ln):
     M, K, N = 600, 256, 256
     spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=77)
@@ -311,7 +383,7 @@ def test_row_norm_in_place():
     assert_parity(host(X), ref, "in-place rmsnorm")
 
 
-@pytest.mark.parametrize("shape", [(256, 128, 128), (1100, 520, 4000)])
+@pytest.mark.parametrize("shape", [(256, 128, 128), (1100, 520, 4000), (65600, 136, 40), (65600, 72, 120)])
 def test_gemm_baseline(shape):
     M, K, N = shape
     spec, d = inputs.make_inputs("prenorm_rms_small", M=M, K=K, N=N, seed=3)
