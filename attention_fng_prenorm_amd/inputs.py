@@ -18,9 +18,15 @@ sides).  "N(mu, v)" is mean and *variance*:
                       eps 1e-6
   norm_attention      Q, K, V [32,1024,4,128] (BSHD) ~ N(0,1),
                       eps_ln 1e-5, eps_rms 1e-6, sm_scale 1/sqrt(128)
+  flash_norm_attention  768 batches; per-batch query length uniform on
+                      1..512 (mean 256.5: the pages' average sparsity 0.5 of
+                      the maximum length); Q [sum of lengths, 4, 128] jagged,
+                      K, V [768, 128, 4, 128] dense, all ~ N(0,1); eps_ln 1e-5,
+                      eps_rms 1e-6, sm_scale 1/sqrt(128), GELU activation
 
 Draw order inside one generator: X (row scales first when present), W,
-gamma; for attention Q, K, V.
+gamma; for attention Q, K, V; for the jagged attention the lengths, then Q,
+K, V.
 """
 
 import math
@@ -43,6 +49,8 @@ WORKLOADS = {
                                 x_dist="normal", gamma=False, seed=1004),
     "norm_attention": dict(kind="norm_attention", B=32, Sq=1024, Skv=1024, H=4, D=128,
                            eps_ln=1e-5, eps_rms=1e-6, seed=1005),
+    "flash_norm_attention": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
+                                 D=128, eps_ln=1e-5, eps_rms=1e-6, act="gelu", seed=1006),
 }
 
 
@@ -111,9 +119,31 @@ def make_attention_inputs(spec):
     return {"Q": q, "K": k, "V": v}
 
 
+def make_jagged_attention_inputs(spec):
+    """Jagged queries and dense keys/values: dict Q [T,H,D] bf16 bits, K, V
+    [B,Skv,H,D] bf16 bits, offsets [B+1] int32 (row offsets of each batch).
+    A spec entry "lengths" (a list) fixes the per-batch lengths instead of
+    drawing them."""
+    rng = np.random.Generator(np.random.PCG64(spec["seed"]))
+    B, Skv, H, D = spec["B"], spec["Skv"], spec["H"], spec["D"]
+    if spec.get("lengths") is not None:
+        lengths = np.asarray(spec["lengths"], dtype=np.int64)
+    else:
+        lengths = rng.integers(1, spec["max_len"] + 1, size=B)
+    offsets = np.zeros(B + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(lengths)
+    T = int(offsets[-1])
+    q = f32_to_bf16_bits(_normal(rng, (T, H, D)))
+    k = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
+    v = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
+    return {"Q": q, "K": k, "V": v, "offsets": offsets}
+
+
 def make_inputs(name, **overrides):
     """Spec and inputs for workload `name` (see the recipe in the header)."""
     spec = workload(name, **overrides)
     if spec["kind"] == "norm_attention":
         return spec, make_attention_inputs(spec)
+    if spec["kind"] == "flash_norm_attention":
+        return spec, make_jagged_attention_inputs(spec)
     return spec, make_gemm_inputs(spec)

@@ -8,6 +8,8 @@ from .fng_oracle import (  # noqa: F401
     gemm_postnorm,
     layernorm_rows,
     norm_attention,
+    gelu_tanh,
+    flash_norm_attention,
     prenorm_rms_gemm,
     rms_rstd,
     rmsnorm_rows,

@@ -35,6 +35,15 @@ Readings of points the page leaves open (each also listed in the design notes):
     all keys (non-causal, no mask), product with V, then RMSNorm of each output
     row over head_dim; K and V are not normalised; layout BSHD (section 4's
     pseudocode header gives [batch, seq, H, head_dim]).
+  * full FlashNormAttention (section 4's fused short-KV kernel as written):
+    LayerNorm of each query row across all heads (H*head_dim values), the
+    scores of each head scaled by sm_scale after the product (the pseudocode
+    shows no scale: sm_scale = 1 reproduces it literally), an activation that
+    is either the max-subtracted softmax over the keys or the elementwise GELU
+    in its tanh form (the pseudocode names a generic elementwise activation),
+    the first residual adds the normalised query to the attention output, the
+    RMSNorm runs across all heads, the second residual adds the raw query.
+    Query rows are jagged (per-batch lengths given by offsets), keys dense.
 """
 
 import numpy as np
@@ -185,6 +194,59 @@ def norm_attention(q, k, v, eps_ln, eps_rms, sm_scale):
             ln_mean[b, :, h] = mu
             ln_rstd[b, :, h] = r1
             rms_rstd[b, :, h] = r2
+    return out, ln_mean, ln_rstd, rms_rstd
+
+
+def gelu_tanh(x):
+    """GELU in its tanh form (Hendrycks and Gimpel's approximation):
+    0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
+    """Section 4's FlashNormAttention, fused short-KV form, on jagged queries.
+
+    q: [T, H, D] query rows of all batches back to back, rows offsets[b] ..
+    offsets[b+1]-1 belonging to batch b; k, v: [B, Skv, H, D] dense.
+    For every query row x (H*D values):
+        ln  = layernorm(x) over all H*D                       (norm 1)
+        o_h = act(ln_h k[b,:,h,:]^T * sm_scale) v[b,:,h,:] + ln_h   (residual 1)
+        out = rmsnorm(o) over all H*D + x                      (norm 2, residual 2)
+    act is "softmax" (over the keys) or "gelu" (elementwise, tanh form).
+    Returns (out [T,H,D], ln_mean [T], ln_rstd [T], rms_rstd [T]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    T, H, D = q.shape
+    out = np.empty_like(q)
+    ln_mean = np.empty(T)
+    ln_rstd = np.empty(T)
+    rms_rstd = np.empty(T)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        x = q[r0:r1].reshape(r1 - r0, H * D)
+        ln, mu, rs1 = layernorm_rows(x, eps_ln)
+        ln = ln.reshape(r1 - r0, H, D)
+        o = np.empty_like(ln)
+        for h in range(H):
+            s = (ln[:, h, :] @ k[b, :, h, :].T) * sm_scale
+            if act == "softmax":
+                p = softmax_rows(s)
+            elif act == "gelu":
+                p = gelu_tanh(s)
+            else:
+                raise ValueError(act)
+            o[:, h, :] = p @ v[b, :, h, :] + ln[:, h, :]
+        y, rs2 = rmsnorm_rows(o.reshape(r1 - r0, H * D), eps_rms)
+        out[r0:r1] = (y + x).reshape(r1 - r0, H, D)
+        ln_mean[r0:r1] = mu
+        ln_rstd[r0:r1] = rs1
+        rms_rstd[r0:r1] = rs2
     return out, ln_mean, ln_rstd, rms_rstd
 
 

@@ -118,6 +118,40 @@ def bf_norm_attention(q, k, v, eps_ln, eps_rms, scale):
     return out
 
 
+def bf_gelu_erf(x):
+    """GELU by its definition x * Phi(x), Phi the standard normal CDF."""
+    return 0.5 * x * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+
+def bf_flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, scale, act):
+    """Full FlashNormAttention on nested lists: q[t][h][d] jagged rows,
+    k, v [b][t][h][d]; act 'softmax' or a Python function applied per score."""
+    H, D = len(q[0]), len(q[0][0])
+    out = [None] * len(q)
+    for b in range(len(offsets) - 1):
+        for r in range(offsets[b], offsets[b + 1]):
+            x = [q[r][h][d] for h in range(H) for d in range(D)]
+            ln, _, _ = bf_layernorm([x], eps_ln)
+            ln = ln[0]
+            o = []
+            for h in range(H):
+                sc = []
+                for t in range(len(k[b])):
+                    acc = 0.0
+                    for d in range(D):
+                        acc += ln[h * D + d] * k[b][t][h][d]
+                    sc.append(acc * scale)
+                p = bf_softmax(sc) if act == "softmax" else [act(s) for s in sc]
+                for d in range(D):
+                    acc = 0.0
+                    for t in range(len(k[b])):
+                        acc += p[t] * v[b][t][h][d]
+                    o.append(acc + ln[h * D + d])
+            y, _ = bf_rmsnorm([o], eps_rms)
+            out[r] = [[y[0][h * D + d] + x[h * D + d] for d in range(D)] for h in range(H)]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # bf16 decoding
 # ---------------------------------------------------------------------------
@@ -421,6 +455,79 @@ def check_attention_closed_forms(O):
     _close(np.mean(o1 * o1, axis=-1), np.ones(o1.shape[:-1]), 1e-3, "output row rms")
 
 
+def check_gelu(O):
+    xs = np.linspace(-8.0, 8.0, 401)
+    g = O.gelu_tanh(xs)
+    # the tanh form stays within 5e-4 of the exact x * Phi(x) everywhere
+    _close(g, [bf_gelu_erf(x) for x in xs], 5e-4, "gelu tanh form vs erf definition")
+    # exact identities of the form: odd part x/2, value 0 at 0
+    _close(g - O.gelu_tanh(-xs), xs, 1e-12, "gelu(x) - gelu(-x) = x")
+    _close(O.gelu_tanh(np.array([0.0])), [0.0], 0.0, "gelu(0)")
+
+
+def _fna_case(seed, lengths, Skv, H, D, qscale=1.0):
+    rng = _rng(seed)
+    off = [0]
+    for n in lengths:
+        off.append(off[-1] + n)
+    q = rng.standard_normal((off[-1], H, D)) * qscale + 0.3
+    q[:, 0, :] *= 3.0  # heads on different scales: per-head and cross-head norms differ
+    k = rng.standard_normal((len(lengths), Skv, H, D))
+    v = rng.standard_normal((len(lengths), Skv, H, D))
+    return q, np.array(off), k, v
+
+
+def check_fna_bruteforce(O):
+    q, off, k, v = _fna_case(61, [2, 0, 3], 4, 2, 3)
+    for act, f in (("softmax", "softmax"), ("gelu", bf_gelu_erf)):
+        out, _, _, _ = O.flash_norm_attention(q, off, k, v, 1e-5, 1e-6, 0.6, act)
+        ref = bf_flash_norm_attention(q.tolist(), off.tolist(), k.tolist(), v.tolist(), 1e-5, 1e-6, 0.6, f)
+        # softmax: exact up to rounding; gelu: the reference uses the erf definition
+        _close(out, ref, 1e-12 if act == "softmax" else 2e-3, f"flash norm attention ({act}) vs brute force")
+
+
+def check_fna_torch(O):
+    import torch
+    import torch.nn.functional as F
+    q, off, k, v = _fna_case(62, [5, 7], 6, 3, 8, qscale=2.0)
+    H, D = 3, 8
+    out, mu, r1, r2 = O.flash_norm_attention(q, off, k, v, 1e-5, 1e-6, 0.4, "softmax")
+    for b in range(2):
+        x = torch.from_numpy(q[off[b]:off[b + 1]]).reshape(-1, H * D)
+        ln = F.layer_norm(x, (H * D,), eps=1e-5).reshape(-1, H, D)
+        tq = ln.permute(1, 0, 2).contiguous()
+        tk = torch.from_numpy(k[b]).permute(1, 0, 2).contiguous()
+        tv = torch.from_numpy(v[b]).permute(1, 0, 2).contiguous()
+        o = F.scaled_dot_product_attention(tq, tk, tv, scale=0.4).permute(1, 0, 2) + ln
+        ref = F.rms_norm(o.reshape(-1, H * D), (H * D,), eps=1e-6) + x
+        _close(out[off[b]:off[b + 1]].reshape(-1, H * D), ref.numpy(), 1e-12, "fna vs torch fp64")
+        _close(mu[off[b]:off[b + 1]], x.numpy().mean(axis=1), 1e-13, "fna ln mean")
+
+
+def check_fna_closed_forms(O):
+    q, off, k, v = _fna_case(63, [3, 4], 5, 2, 4)
+    T, H, D = q.shape
+    flat = q.reshape(T, H * D).tolist()
+    ln, _, _ = bf_layernorm(flat, 1e-5)
+    # V = 0: the attention term vanishes, out = rmsnorm(layernorm(x)) + x
+    out, _, _, _ = O.flash_norm_attention(q, off, k, np.zeros_like(v), 1e-5, 1e-6, 0.5, "gelu")
+    y, _ = bf_rmsnorm(ln, 1e-6)
+    _close(out.reshape(T, H * D), np.array(y) + q.reshape(T, H * D), 1e-12, "V = 0")
+    # K = 0 with softmax: uniform weights, o_h = mean_t v + ln_h
+    out, _, _, _ = O.flash_norm_attention(q, off, np.zeros_like(k), v, 1e-5, 1e-6, 0.5, "softmax")
+    o = np.array(ln).reshape(T, H, D).copy()
+    for b in range(2):
+        o[off[b]:off[b + 1]] += np.mean(v[b], axis=0)[None]
+    y, _ = bf_rmsnorm(o.reshape(T, H * D).tolist(), 1e-6)
+    _close(out.reshape(T, H * D), np.array(y) + q.reshape(T, H * D), 1e-12, "K = 0 softmax")
+    # batches are independent: each batch alone gives the same rows
+    full, _, _, _ = O.flash_norm_attention(q, off, k, v, 1e-5, 1e-6, 0.5, "gelu")
+    for b in range(2):
+        one, _, _, _ = O.flash_norm_attention(q[off[b]:off[b + 1]], np.array([0, off[b + 1] - off[b]]),
+                                              k[b:b + 1], v[b:b + 1], 1e-5, 1e-6, 0.5, "gelu")
+        _close(full[off[b]:off[b + 1]], one, 0.0, f"batch {b} independent")
+
+
 def check_compare(O):
     e = O.compare(np.array([1.0, 2.0]), np.array([1.0, 3.0]))
     assert abs(e["normwise_rel"] - 1.0 / 3.0) < 1e-15, e
@@ -447,6 +554,10 @@ ALL_CHECKS = [
     check_attention_bruteforce,
     check_attention_torch,
     check_attention_closed_forms,
+    check_gelu,
+    check_fna_bruteforce,
+    check_fna_torch,
+    check_fna_closed_forms,
     check_compare,
 ]
 

@@ -47,11 +47,56 @@ def _ns(**over):
                 mu_a[b, :, h] = mu; r1_a[b, :, h] = r1; r2_a[b, :, h] = r2
         return out, mu_a, r1_a, r2_a
 
+    def flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
+        return _fna(ns, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act)
+
     for name, fn in (("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
-                     ("norm_attention", norm_attention)):
+                     ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention)):
         if name not in over:
             setattr(ns, name, fn)
     return ns
+
+
+def _fna(ns, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act, ln_per_head=False, res1=True,
+         res2="q", rms_per_head=False):
+    """The full FlashNormAttention from the (possibly mutated) pieces in ns,
+    with switches that plant structural mistakes."""
+    q = np.asarray(q, dtype=np.float64)
+    T, H, D = q.shape
+    out = np.empty_like(q)
+    mu_a, r1_a, r2_a = np.zeros(T), np.zeros(T), np.zeros(T)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        x = q[r0:r1]
+        if ln_per_head:
+            ln = np.stack([ns.layernorm_rows(x[:, h, :], eps_ln)[0] for h in range(H)], axis=1)
+        else:
+            ln, mu_a[r0:r1], r1_a[r0:r1] = ns.layernorm_rows(x.reshape(-1, H * D), eps_ln)
+            ln = ln.reshape(-1, H, D)
+        o = np.empty_like(ln)
+        for h in range(H):
+            s = (ln[:, h, :] @ np.asarray(k)[b, :, h, :].T) * sm_scale
+            p = ns.softmax_rows(s) if act == "softmax" else ns.gelu_tanh(s)
+            o[:, h, :] = p @ np.asarray(v)[b, :, h, :] + (ln[:, h, :] if res1 else 0.0)
+        if rms_per_head:
+            y = np.stack([ns.rmsnorm_rows(o[:, h, :], eps_rms)[0] for h in range(H)], axis=1)
+        else:
+            y = ns.rmsnorm_rows(o.reshape(-1, H * D), eps_rms)[0].reshape(-1, H, D)
+        out[r0:r1] = y + (x if res2 == "q" else ln if res2 == "ln" else 0.0)
+    return out, mu_a, r1_a, r2_a
+
+
+def _fna_mutant(**switches):
+    def f(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
+        return _fna(F, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act, **switches)
+    return f
+
+
+def _gelu_wrong_constant(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.44715 * x ** 3)))
 
 
 def _rms_eps_outside(x, eps, gamma=None):
@@ -178,6 +223,12 @@ MUTANTS = {
     "attn_scale_inverted": dict(norm_attention=_attn_scale_divided(F.norm_attention)),
     "attn_normalises_k": dict(norm_attention=_attn_norm_k),
     "attn_missing_out_rmsnorm": dict(norm_attention=_attn_no_out_norm),
+    "fna_layernorm_per_head": dict(flash_norm_attention=_fna_mutant(ln_per_head=True)),
+    "fna_rmsnorm_per_head": dict(flash_norm_attention=_fna_mutant(rms_per_head=True)),
+    "fna_missing_residual_1": dict(flash_norm_attention=_fna_mutant(res1=False)),
+    "fna_missing_residual_2": dict(flash_norm_attention=_fna_mutant(res2=None)),
+    "fna_residual_2_adds_ln_q": dict(flash_norm_attention=_fna_mutant(res2="ln")),
+    "gelu_cubic_constant_x10": dict(gelu_tanh=_gelu_wrong_constant),
 }
 
 
