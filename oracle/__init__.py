@@ -10,6 +10,7 @@ from .fng_oracle import (  # noqa: F401
     norm_attention,
     gelu_tanh,
     flash_norm_attention,
+    jagged_attention,
     prenorm_rms_gemm,
     rms_rstd,
     rmsnorm_rows,

@@ -204,6 +204,36 @@ def gelu_tanh(x):
     return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
 
 
+def _activation(s, act):
+    if act == "softmax":
+        return softmax_rows(s)
+    if act == "gelu":
+        return gelu_tanh(s)
+    raise ValueError(act)
+
+
+def jagged_attention(q, offsets, k, v, sm_scale, act):
+    """The attention inside FlashNormAttention without its norms and
+    residuals (the unfused baseline's attention step), jagged queries:
+    out[r, h, :] = act(q[r, h, :] k[b, :, h, :]^T * sm_scale) v[b, :, h, :]
+    for every row r of batch b.  Layouts as in flash_norm_attention.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    T, H, D = q.shape
+    out = np.zeros((T, H, v.shape[-1]))
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        for h in range(H):
+            s = (q[r0:r1, h, :] @ k[b, :, h, :].T) * sm_scale
+            out[r0:r1, h, :] = _activation(s, act) @ v[b, :, h, :]
+    return out
+
+
 def flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
     """Section 4's FlashNormAttention, fused short-KV form, on jagged queries.
 

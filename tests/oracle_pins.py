@@ -528,6 +528,28 @@ def check_fna_closed_forms(O):
         _close(full[off[b]:off[b + 1]], one, 0.0, f"batch {b} independent")
 
 
+def check_jagged_attention(O):
+    q, off, k, v = _fna_case(64, [3, 0, 2], 5, 2, 3)
+    T, H, D = q.shape
+    out = O.jagged_attention(q, off, k, v, 0.7, "gelu")
+    ql, kl, vl = q.tolist(), k.tolist(), v.tolist()
+    for b in range(3):
+        for r in range(off[b], off[b + 1]):
+            for h in range(H):
+                sc = [0.7 * sum(ql[r][h][d] * kl[b][t][h][d] for d in range(D)) for t in range(5)]
+                p = [bf_gelu_erf(s) for s in sc]
+                ref = [sum(p[t] * vl[b][t][h][d] for t in range(5)) for d in range(D)]
+                _close(out[r, h], ref, 2e-3, "jagged gelu attention vs brute force")
+    # softmax on equal lengths is the dense attention, batch by batch
+    q, off, k, v = _fna_case(65, [4, 4, 4], 6, 3, 5)
+    dense = O.attention(q.reshape(3, 4, 3, 5), k, v, 0.45)
+    _close(O.jagged_attention(q, off, k, v, 0.45, "softmax"), dense.reshape(12, 3, 5), 1e-13,
+           "jagged softmax attention vs dense")
+    # the attention step inside FlashNormAttention: V = 0 leaves only ln + x
+    # there, and out here is exactly zero
+    assert np.all(O.jagged_attention(q, off, k, np.zeros_like(v), 0.45, "gelu") == 0.0)
+
+
 def check_compare(O):
     e = O.compare(np.array([1.0, 2.0]), np.array([1.0, 3.0]))
     assert abs(e["normwise_rel"] - 1.0 / 3.0) < 1e-15, e
@@ -558,6 +580,7 @@ ALL_CHECKS = [
     check_fna_bruteforce,
     check_fna_torch,
     check_fna_closed_forms,
+    check_jagged_attention,
     check_compare,
 ]
 

@@ -50,11 +50,41 @@ def _ns(**over):
     def flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
         return _fna(ns, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act)
 
+    def jagged_attention(q, offsets, k, v, sm_scale, act):
+        return _jagged(ns, q, offsets, k, v, sm_scale, act)
+
     for name, fn in (("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
-                     ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention)):
+                     ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
+                     ("jagged_attention", jagged_attention)):
         if name not in over:
             setattr(ns, name, fn)
     return ns
+
+
+def _jagged(ns, q, offsets, k, v, sm_scale, act, kv_batch_shift=0, scale_after=False):
+    """The jagged attention from the pieces in ns, with switches that plant
+    mistakes: keys/values of another batch, the scale applied after the
+    activation."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, H, D = q.shape
+    nb = len(offsets) - 1
+    out = np.zeros((T, H, v.shape[-1]))
+    for b in range(nb):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        bk = (b + kv_batch_shift) % nb
+        for h in range(H):
+            s = q[r0:r1, h, :] @ k[bk, :, h, :].T
+            if not scale_after:
+                s = s * sm_scale
+            p = ns.softmax_rows(s) if act == "softmax" else ns.gelu_tanh(s)
+            if scale_after:
+                p = p * sm_scale
+            out[r0:r1, h, :] = p @ v[bk, :, h, :]
+    return out
 
 
 def _fna(ns, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act, ln_per_head=False, res1=True,
@@ -229,6 +259,10 @@ MUTANTS = {
     "fna_missing_residual_2": dict(flash_norm_attention=_fna_mutant(res2=None)),
     "fna_residual_2_adds_ln_q": dict(flash_norm_attention=_fna_mutant(res2="ln")),
     "gelu_cubic_constant_x10": dict(gelu_tanh=_gelu_wrong_constant),
+    "jagged_kv_of_next_batch": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
+        oracle, q, o, k, v, s, a, kv_batch_shift=1)),
+    "jagged_scale_after_activation": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
+        oracle, q, o, k, v, s, a, scale_after=True)),
 }
 
 
