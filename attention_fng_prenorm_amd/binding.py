@@ -28,6 +28,9 @@ FNG_PATH_FULLN = 1
 FNG_PATH_SPLITN = 2
 FNG_PATH_TWOPASS = 3
 
+FNG_ACT_SOFTMAX = 0
+FNG_ACT_GELU = 1
+
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 _vp = ctypes.c_void_p
@@ -48,6 +51,10 @@ SIGNATURES = {
     "fng_layernorm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]),
     "fng_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fng_attention": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _vp]),
+    "fng_flash_norm_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                        _i64, _i64, _i64, _f32, _f32, _f32, _int, _vp]),
+    "fng_jagged_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                    _f32, _int, _vp]),
     "fng_status_string": (ctypes.c_char_p, [_int]),
     "fng_version": (_int, []),
 }
@@ -213,6 +220,40 @@ def fng_attention(Q, K, V, out, sm_scale=0.0, stream=None):
     _check("fng_attention", lib().fng_attention(
         _bf(Q, "Q"), _bf(K, "K"), _bf(V, "V"), _bf(out, "out"), B, Sq, Skv, H, D, sm_scale,
         _stream(stream)))
+
+
+def _act(act):
+    codes = {"softmax": FNG_ACT_SOFTMAX, "gelu": FNG_ACT_GELU}
+    return codes[act] if isinstance(act, str) else int(act)
+
+
+def _jagged_shapes(Q, q_offsets, K, V, out):
+    T, H, D = Q.shape
+    B, Skv = K.shape[0], K.shape[1]
+    if tuple(K.shape) != (B, Skv, H, D) or tuple(V.shape) != (B, Skv, H, D) or out.shape != Q.shape:
+        raise ValueError("shapes: Q/out [T,H,D], K/V [B,Skv,H,D]")
+    if tuple(q_offsets.shape) != (B + 1,):
+        raise ValueError("q_offsets must be [B+1]")
+    return T, H, D, B, Skv
+
+
+def fng_flash_norm_attention(Q, q_offsets, K, V, out, max_len_q, eps_ln, eps_rms, sm_scale=0.0,
+                             act="softmax", ln_mean_out=None, ln_rstd_out=None, rms_rstd_out=None,
+                             stream=None):
+    T, H, D, B, Skv = _jagged_shapes(Q, q_offsets, K, V, out)
+    _check("fng_flash_norm_attention", lib().fng_flash_norm_attention(
+        _bf(Q, "Q"), _ptr(q_offsets, torch.int32, "q_offsets"), _bf(K, "K"), _bf(V, "V"),
+        _bf(out, "out"), _f(ln_mean_out, "ln_mean_out"), _f(ln_rstd_out, "ln_rstd_out"),
+        _f(rms_rstd_out, "rms_rstd_out"), B, T, max_len_q, Skv, H, D, sm_scale, eps_ln, eps_rms,
+        _act(act), _stream(stream)))
+
+
+def fng_jagged_attention(Q, q_offsets, K, V, out, max_len_q, sm_scale=0.0, act="softmax",
+                         stream=None):
+    T, H, D, B, Skv = _jagged_shapes(Q, q_offsets, K, V, out)
+    _check("fng_jagged_attention", lib().fng_jagged_attention(
+        _bf(Q, "Q"), _ptr(q_offsets, torch.int32, "q_offsets"), _bf(K, "K"), _bf(V, "V"),
+        _bf(out, "out"), B, T, max_len_q, Skv, H, D, sm_scale, _act(act), _stream(stream)))
 
 
 def fng_status_string(status):

@@ -128,6 +128,25 @@ int check_attn(const void* Q, const void* K, const void* V, const void* O, int64
   return FNG_OK;
 }
 
+int check_fna(const void* Q, const int32_t* off, const void* K, const void* V, const void* O,
+              int64_t B, int64_t T, int64_t max_len, int64_t Skv, int64_t H, int64_t D, int act) {
+  if (B < 0 || T < 0 || max_len < 0 || H < 0 || Skv < 1 || D < 1) return FNG_ERR_INVALID_ARG;
+  if (act != FNG_ACT_SOFTMAX && act != FNG_ACT_GELU) return FNG_ERR_INVALID_ARG;
+  if (D != 128) return FNG_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0 || max_len == 0 || H == 0) return FNG_OK;
+  if (H != 1 && H != 2 && H != 4) return FNG_ERR_UNSUPPORTED;
+  if (!Q || !off || !K || !V || !O) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (uintptr_t)off % 4 != 0)
+    return FNG_ERR_MISALIGNED;
+  // 32-bit row indices and per-batch buffer ranges (one block of query rows
+  // and one 32-key tile of overrun), and the grid size
+  if (T >= (int64_t)INT32_MAX || B >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if ((max_len + 256) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if ((Skv + 32) * H * D * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if (B * ((max_len + 255) / 32) >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  return FNG_OK;
+}
+
 }  // namespace
 
 FNG_EXPORT int fng_version(void) { return kVersion; }
@@ -199,6 +218,19 @@ FNG_EXPORT int fng_norm_attention(const void* Q, const void* K, const void* V, v
   return fng::launch_attention(c, true, as_stream(stream));
 }
 
+FNG_EXPORT int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void* K, const void* V,
+                                        void* out, float* ln_mean_out, float* ln_rstd_out, float* rms_rstd_out,
+                                        int64_t B, int64_t T, int64_t max_len_q, int64_t Skv, int64_t H, int64_t D,
+                                        float sm_scale, float eps_ln, float eps_rms, int act, void* stream) {
+  if (!(eps_ln > 0.f && isfinite(eps_ln)) || !(eps_rms > 0.f && isfinite(eps_rms))) return FNG_ERR_INVALID_ARG;
+  if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
+  const int st = check_fna(Q, q_offsets, K, V, out, B, T, max_len_q, Skv, H, D, act);
+  if (st != FNG_OK || B == 0 || T == 0 || max_len_q == 0 || H == 0) return st;
+  fng::FnaCall c{Q, q_offsets, K, V, out, ln_mean_out, ln_rstd_out, rms_rstd_out, B, T, max_len_q, Skv, H,
+                 sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), eps_ln, eps_rms, act};
+  return fng::launch_fna(c, true, as_stream(stream));
+}
+
 FNG_EXPORT int fng_rmsnorm(const void* X, const void* gamma, void* Y, float* rstd_out, int64_t M, int64_t N,
                            float eps, void* stream) {
   if (M < 0 || N < 1 || !(eps > 0.f && isfinite(eps))) return FNG_ERR_INVALID_ARG;
@@ -234,4 +266,15 @@ FNG_EXPORT int fng_attention(const void* Q, const void* K, const void* V, void* 
   fng::AttnCall c{Q, K, V, out, nullptr, nullptr, nullptr, B, Sq, Skv, H, D,
                   sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), 1e-5f, 1e-6f};
   return fng::launch_attention(c, false, as_stream(stream));
+}
+
+FNG_EXPORT int fng_jagged_attention(const void* Q, const int32_t* q_offsets, const void* K, const void* V,
+                                    void* out, int64_t B, int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
+                                    int64_t D, float sm_scale, int act, void* stream) {
+  if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
+  const int st = check_fna(Q, q_offsets, K, V, out, B, T, max_len_q, Skv, H, D, act);
+  if (st != FNG_OK || B == 0 || T == 0 || max_len_q == 0 || H == 0) return st;
+  fng::FnaCall c{Q, q_offsets, K, V, out, nullptr, nullptr, nullptr, B, T, max_len_q, Skv, H,
+                 sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), 1e-5f, 1e-6f, act};
+  return fng::launch_fna(c, false, as_stream(stream));
 }

@@ -58,4 +58,20 @@ struct AttnCall {
 };
 int launch_attention(const AttnCall& c, bool norm, hipStream_t s);
 
+// fng_fna.hip
+struct FnaCall {
+  const void* Q;
+  const int32_t* offsets;
+  const void* K;
+  const void* V;
+  void* O;
+  float* ln_mean_out;
+  float* ln_rstd_out;
+  float* rms_rstd_out;
+  int64_t B, T, max_len, Skv, H;
+  float sm_scale, eps_ln, eps_rms;
+  int act;
+};
+int launch_fna(const FnaCall& c, bool norm, hipStream_t s);
+
 }  // namespace fng

@@ -11,7 +11,8 @@ step warmed.
 Beside it, the same JSON line carries every fused kernel of the hot path at its
 workload shape (post-LayerNorm GEMM with one workgroup across N, the affine
 pre-RMSNorm variant, post-RMSNorm GEMM with the split-N exchange and its
-two-pass fallback, and the norm-sandwiched attention) with the unfused
+two-pass fallback, the norm-sandwiched attention, and the full
+FlashNormAttention on jagged queries with short keys) with the unfused
 baselines they replace, timed interleaved, and the "norm latency hidden"
 figure (T_gemm + T_norm - T_fused) / T_norm of the pages; and the pages'
 ads-shape sweep of the post-LayerNorm GEMM (M = 256k rows, K and N from 64 to
@@ -20,7 +21,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|ads|copy]
+       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|ads|copy]
 """
 
 import argparse
@@ -230,6 +231,45 @@ def main():
             "saving_pct_of_unfused_total": round(100.0 * (base - t["fused"]) / base, 1),
         }
         del qsets, O, Qn, Oa
+
+    # ---------------- full FlashNormAttention, jagged queries, short KV ------------
+    if args.only in (None, "fna"):
+        s6, d6 = inputs.make_inputs("flash_norm_attention")
+        Q6, K6, V6 = dev(d6["Q"]), dev(d6["K"]), dev(d6["V"])
+        off6 = torch.from_numpy(d6["offsets"]).to("cuda")
+        T6, H6, D6 = Q6.shape
+        sets6 = [(Q6, K6, V6), (Q6.flip(0).contiguous(), K6.flip(0).contiguous(), V6.flip(0).contiguous())]
+        O6 = torch.empty_like(Q6)
+        st6 = [torch.empty(T6, dtype=torch.float32, device="cuda") for _ in range(3)]
+        ln6, at6, y6 = torch.empty_like(Q6), torch.empty_like(Q6), torch.empty_like(Q6)
+        R6 = T6 * H6 * D6 // 512
+        ml, act = s6["max_len"], s6["act"]
+
+        def unfused_tail(i):
+            o = at6 + ln6  # first residual (torch elementwise)
+            B.fng_rmsnorm(o.view(T6, H6 * D6), y6.view(T6, H6 * D6), s6["eps_rms"])
+            torch.add(y6, sets6[i % 2][0], out=O6)  # second residual
+        t = time_batches({
+            "fused": lambda i: B.fng_flash_norm_attention(sets6[i % 2][0], off6, sets6[i % 2][1], sets6[i % 2][2],
+                                                          O6, ml, s6["eps_ln"], s6["eps_rms"], 0.0, act, *st6),
+            "ln": lambda i: B.fng_layernorm(sets6[i % 2][0].view(T6, H6 * D6), ln6.view(T6, H6 * D6),
+                                            s6["eps_ln"]),
+            "attn": lambda i: B.fng_jagged_attention(ln6, off6, sets6[i % 2][1], sets6[i % 2][2], at6, ml, 0.0, act),
+            "tail": unfused_tail,
+        }, args.reps, args.batch)
+        f6 = 4.0 * T6 * H6 * s6["Skv"] * D6
+        b6 = 2.0 * (2 * T6 * H6 * D6 + 2 * s6["B"] * s6["Skv"] * H6 * D6) + 12.0 * T6
+        base = t["ln"] + t["attn"] + t["tail"]
+        kernels["flash_norm_attention"] = {
+            "T": T6, "B": s6["B"], "Skv": s6["Skv"], "H": H6, "act": act,
+            "fused_us": round(t["fused"], 2), "ln_us": round(t["ln"], 2), "attn_us": round(t["attn"], 2),
+            "adds_rms_us": round(t["tail"], 2), "unfused_us": round(base, 2),
+            "fused_tflops": round(f6 / t["fused"] / 1e6, 1),
+            "fused_gbs": round(b6 / t["fused"] / 1e3, 1),
+            "fused_frac_hbm": round(b6 / t["fused"] / 1e3 / PEAK_HBM_GBS, 4),
+            "speedup_vs_unfused": round(base / t["fused"], 2),
+        }
+        del sets6, O6, st6, ln6, at6, y6
 
     # ---------------- ads-shape sweep: post-LayerNorm GEMM, M = 256k rows ---------
     # K and N from 64 to 2048 (the pages' sweep of the naive full-N regime at small

@@ -133,6 +133,35 @@ int fng_norm_attention(const void* Q, const void* K, const void* V, void* out,
                        float sm_scale, float eps_ln, float eps_rms, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Full FlashNormAttention (section 4, the fused short-KV kernel), on jagged
+ * queries.  Q and out are [T, H, D] (rows of all batches back to back; batch
+ * b owns rows q_offsets[b] .. q_offsets[b+1]-1); K and V are [B, Skv, H, D]
+ * dense.  For every query row x (all H*D values of one row):
+ *     ln  = layernorm(x) over all H*D values           (eps_ln, no affine)
+ *     o_h = act(ln_h K[b,:,h,:]^T * sm_scale) V[b,:,h,:] + ln_h
+ *     out = rmsnorm(o) over all H*D values + x         (eps_rms, no affine)
+ * act: FNG_ACT_SOFTMAX (over the keys, non-causal) or FNG_ACT_GELU
+ * (elementwise, tanh form).  sm_scale <= 0 selects 1/sqrt(D).
+ * q_offsets: int32 DEVICE memory, [B + 1], non-decreasing, q_offsets[0] >= 0,
+ *   q_offsets[B] <= T, every batch length <= max_len_q.  The contents are not
+ *   checked on the host; the kernel never reads or writes outside Q, out and
+ *   the statistics buffers whatever they hold, but rows a batch owns beyond
+ *   max_len_q, and rows no batch owns, are left unwritten.
+ * H must be 1, 2 or 4 and D 128; Skv >= 1.  Optional fp32 [T] statistics:
+ * ln mean and rstd, rms rstd.  K and V below 65504 in magnitude (fp16 MFMA
+ * operands; the normalized queries are pre-multiplied by sm_scale (times
+ * log2(e) for softmax) before their fp16 rounding).
+ * ------------------------------------------------------------------------- */
+typedef enum { FNG_ACT_SOFTMAX = 0, FNG_ACT_GELU = 1 } fng_act_t;
+
+int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void* K,
+                             const void* V, void* out, float* ln_mean_out,
+                             float* ln_rstd_out, float* rms_rstd_out, int64_t B,
+                             int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
+                             int64_t D, float sm_scale, float eps_ln, float eps_rms,
+                             int act, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Unfused baselines (the separate kernels the fusions replace; section 1
  * describes the standalone row norm that loads whole rows).
  * ------------------------------------------------------------------------- */
@@ -151,6 +180,14 @@ int fng_gemm(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_
 int fng_attention(const void* Q, const void* K, const void* V, void* out, int64_t B,
                   int64_t Sq, int64_t Skv, int64_t H, int64_t D, float sm_scale,
                   void* stream);
+
+/* out = act(Q K^T * sm_scale) V per head on jagged queries: the attention of
+ * fng_flash_norm_attention without its norms and residuals (same layouts,
+ * offsets contract, limits and kernel). */
+int fng_jagged_attention(const void* Q, const int32_t* q_offsets, const void* K,
+                         const void* V, void* out, int64_t B, int64_t T, int64_t max_len_q,
+                         int64_t Skv, int64_t H, int64_t D, float sm_scale, int act,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------
  * Misc.

@@ -22,7 +22,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for must in ("fng_prenorm_rms_gemm", "fng_gemm_postnorm_ln", "fng_gemm_postnorm_rms",
-                 "fng_norm_attention", "fng_rmsnorm", "fng_layernorm", "fng_gemm", "fng_attention"):
+                 "fng_norm_attention", "fng_rmsnorm", "fng_layernorm", "fng_gemm", "fng_attention",
+                 "fng_flash_norm_attention", "fng_jagged_attention"):
         assert must in names
 
 
@@ -125,6 +126,39 @@ def test_attention_validation(lib):
     assert a(*args, 1, 8, 8, 2, 96, 0.0, None) == B.FNG_ERR_UNSUPPORTED
     assert a(*args, 1, 1 << 22, 8, 64, 128, 0.0, None) == B.FNG_ERR_UNSUPPORTED
     assert a(None, None, None, None, 2, 0, 8, 2, 128, 0.0, None) == B.FNG_OK
+
+
+def test_flash_norm_attention_validation(lib):
+    f = lib.fng_flash_norm_attention
+    j = lib.fng_jagged_attention
+    S = B.FNG_ACT_SOFTMAX
+
+    def call(Q=FAKE, off=FAKE, K=FAKE, V=FAKE, O=FAKE, b=2, T=16, L=8, skv=8, H=2, D=128,
+             scale=0.0, e1=1e-5, e2=1e-6, act=S):
+        return f(Q, off, K, V, O, None, None, None, b, T, L, skv, H, D, scale, e1, e2, act, None)
+
+    assert call(D=64) == B.FNG_ERR_UNSUPPORTED
+    assert call(H=3) == B.FNG_ERR_UNSUPPORTED            # heads must be 1, 2 or 4
+    assert call(H=8) == B.FNG_ERR_UNSUPPORTED
+    assert call(skv=0) == B.FNG_ERR_INVALID_ARG
+    assert call(T=-1) == B.FNG_ERR_INVALID_ARG
+    assert call(act=2) == B.FNG_ERR_INVALID_ARG
+    assert call(e1=0.0) == B.FNG_ERR_INVALID_ARG
+    assert call(e2=float("nan")) == B.FNG_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == B.FNG_ERR_INVALID_ARG
+    assert call(off=None) == B.FNG_ERR_INVALID_ARG
+    assert call(Q=None) == B.FNG_ERR_INVALID_ARG
+    assert call(Q=MIS) == B.FNG_ERR_MISALIGNED
+    assert call(off=FAKE + 2) == B.FNG_ERR_MISALIGNED     # int32 offsets need 4-byte alignment
+    assert call(L=1 << 22, H=4) == B.FNG_ERR_UNSUPPORTED  # per-batch query range beyond 32 bits
+    assert call(skv=1 << 22, H=4) == B.FNG_ERR_UNSUPPORTED
+    # empty problems: nothing enqueued
+    assert call(Q=None, off=None, K=None, V=None, O=None, b=0) == B.FNG_OK
+    assert call(Q=None, off=None, K=None, V=None, O=None, T=0) == B.FNG_OK
+    assert call(Q=None, off=None, K=None, V=None, O=None, L=0) == B.FNG_OK
+    assert j(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 8, 2, 128, 0.0, 5, None) == B.FNG_ERR_INVALID_ARG
+    assert j(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 8, 2, 96, 0.0, S, None) == B.FNG_ERR_UNSUPPORTED
+    assert j(None, None, None, None, None, 2, 0, 8, 8, 2, 128, 0.0, S, None) == B.FNG_OK
 
 
 def test_norm_and_gemm_validation(lib):

@@ -1,0 +1,196 @@
+"""GPU parity of the full FlashNormAttention and its unfused attention step
+(fng_flash_norm_attention, fng_jagged_attention, called through the C ABI)
+against the fp64 oracle on seeded bf16 inputs: jagged query batches with
+empty, single-row, tile-straddling and maximum lengths, key counts that leave
+a ragged last key tile, one, two and four heads, softmax and GELU.
+
+Tolerance: normwise max relative error <= 1e-2 and mean absolute error <=
+2e-3 against the oracle, the MAE bound scaled by the output's mean magnitude
+over 0.8 (the mean magnitude of a unit-normal output) where that is larger.
+The second residual adds the raw query, so the output's mean magnitude is
+about 1.6 and the exact result rounded to bf16 alone already has an MAE of
+about 2.2e-3; the plain attention output is not normalised at all.  The fused
+kernel must also stay within 1e-3 of that rounding floor."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_fng_prenorm_amd import binding as B
+from attention_fng_prenorm_amd import inputs
+from gpu_util import assert_close_stats, assert_parity, dev, empty_bf16, host, log
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [0, 1, 300, 37, 256, 65, 0, 129, 64, 128]   # straddle 64/128/256-row blocks
+SCALE = 1.0 / math.sqrt(128)
+
+
+def f64(bits):
+    return oracle.bf16_to_f64(bits)
+
+
+def fna_parity(y, ref, what):
+    scale = max(1.0, float(np.mean(np.abs(ref))) / 0.8)
+    e = assert_parity(y, ref, what, mae=2e-3 * scale)
+    floor = oracle.compare(torch.from_numpy(ref).to(torch.bfloat16).double().numpy(), ref)["mae"]
+    log(f"{what}: bf16 rounding floor mae={floor:.3e}")
+    assert e["mae"] <= floor + 1e-3, (what, e, floor)
+
+
+def jagged(H, Skv, lengths=LENGTHS, seed=7, **kw):
+    spec, d = inputs.make_inputs("flash_norm_attention", B=len(lengths), H=H, Skv=Skv,
+                                 lengths=list(lengths), max_len=max(max(lengths), 1), seed=seed, **kw)
+    return spec, d
+
+
+def run_fna(d, max_len, act, eps_ln=1e-5, eps_rms=1e-6, scale=SCALE, T_extra=0, norm=True):
+    Q = dev(d["Q"])
+    T, H, D = Q.shape
+    if T_extra:
+        Q = torch.cat([Q, torch.zeros(T_extra, H, D, dtype=torch.bfloat16, device="cuda")])
+    K, V = dev(d["K"]), dev(d["V"])
+    off = torch.from_numpy(np.ascontiguousarray(d["offsets"])).to("cuda")
+    O = empty_bf16(*Q.shape)
+    st = [torch.full((Q.shape[0],), float("nan"), dtype=torch.float32, device="cuda") for _ in range(3)]
+    if norm:
+        B.fng_flash_norm_attention(Q, off, K, V, O, max_len, eps_ln, eps_rms, scale, act, *st)
+    else:
+        B.fng_jagged_attention(Q, off, K, V, O, max_len, scale, act)
+    torch.cuda.synchronize()
+    return O, st
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu"])
+@pytest.mark.parametrize("H", [1, 2, 4])
+def test_fna_reduced(H, act):
+    spec, d = jagged(H, 72)
+    log(f"fna H={H} act={act} lengths={LENGTHS} Skv=72")
+    O, st = run_fna(d, spec["max_len"], act, spec["eps_ln"], spec["eps_rms"])
+    ref, mu, r1, r2 = oracle.flash_norm_attention(f64(d["Q"]), d["offsets"], f64(d["K"]), f64(d["V"]),
+                                                  spec["eps_ln"], spec["eps_rms"], SCALE, act)
+    fna_parity(host(O), ref, f"fna H={H} {act}")
+    assert np.max(np.abs(st[0].cpu().numpy() - mu)) < 1e-4
+    assert_close_stats(st[1].cpu().numpy(), r1, "fna ln rstd")
+    assert_close_stats(st[2].cpu().numpy(), r2, "fna rms rstd", rtol=3e-3)
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu"])
+@pytest.mark.parametrize("H", [1, 4])
+def test_jagged_attention_reduced(H, act):
+    spec, d = jagged(H, 72, seed=8)
+    log(f"jagged attention H={H} act={act}")
+    O, _ = run_fna(d, spec["max_len"], act, scale=0.1, norm=False)
+    ref = oracle.jagged_attention(f64(d["Q"]), d["offsets"], f64(d["K"]), f64(d["V"]), 0.1, act)
+    assert_parity(host(O), ref, f"jagged attention H={H} {act}",
+                  mae=2e-3 * max(np.mean(np.abs(ref)), 0.8) / 0.8)
+
+
+@pytest.mark.parametrize("Skv", [1, 32, 33, 200])
+def test_fna_key_counts(Skv):
+    lengths = [5, 70, 0, 3]
+    for act in ("softmax", "gelu"):
+        spec, d = jagged(2, Skv, lengths=lengths, seed=9)
+        log(f"fna Skv={Skv} act={act}")
+        O, _ = run_fna(d, spec["max_len"], act)
+        ref, _, _, _ = oracle.flash_norm_attention(f64(d["Q"]), d["offsets"], f64(d["K"]), f64(d["V"]),
+                                                   spec["eps_ln"], spec["eps_rms"], SCALE, act)
+        fna_parity(host(O), ref, f"fna Skv={Skv} {act}")
+
+
+def test_fna_rows_outside_batches_untouched():
+    # rows past offsets[B] and rows a batch owns beyond max_len_q are not written
+    lengths = [40, 90, 7]
+    spec, d = jagged(4, 48, lengths=lengths, seed=10)
+    log("fna unowned rows")
+    O, st = run_fna(d, 64, "gelu", T_extra=5)
+    y = host(O)
+    off = d["offsets"]
+    owned = np.zeros(y.shape[0], dtype=bool)
+    for b in range(len(lengths)):
+        owned[off[b]:off[b] + min(lengths[b], 64)] = True
+    assert np.all(np.isnan(y[~owned])), "a row outside the batches was written"
+    assert np.all(np.isnan(st[0].cpu().numpy()[~owned]))
+    # the owned rows: batch 1 truncated to its first 64 rows
+    cut = [min(n, 64) for n in lengths]
+    rows = np.concatenate([np.arange(off[b], off[b] + cut[b]) for b in range(len(lengths))])
+    q2 = d["Q"][rows]
+    off2 = np.concatenate([[0], np.cumsum(cut)])
+    ref, _, _, _ = oracle.flash_norm_attention(f64(q2), off2, f64(d["K"]), f64(d["V"]), spec["eps_ln"],
+                                               spec["eps_rms"], SCALE, "gelu")
+    fna_parity(y[rows], ref, "fna owned rows")
+
+
+def test_fna_deterministic_and_scale_default():
+    spec, d = jagged(4, 72, seed=11)
+    log("fna determinism")
+    O1, _ = run_fna(d, spec["max_len"], "softmax")
+    O2, _ = run_fna(d, spec["max_len"], "softmax", scale=0.0)   # 0 selects 1/sqrt(D)
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+
+
+def test_fused_matches_unfused_composition():
+    # layernorm over all heads -> jagged attention -> + ln -> rmsnorm -> + x,
+    # each step its own kernel (the unfused baseline) against the fused kernel
+    spec, d = jagged(4, 72, seed=12)
+    log("fna fused vs unfused")
+    Q, K, V = dev(d["Q"]), dev(d["K"]), dev(d["V"])
+    T, H, D = Q.shape
+    off = torch.from_numpy(np.ascontiguousarray(d["offsets"])).to("cuda")
+    ln = empty_bf16(T, H, D)
+    B.fng_layernorm(Q.view(T, H * D), ln.view(T, H * D), spec["eps_ln"])
+    att = empty_bf16(T, H, D)
+    B.fng_jagged_attention(ln, off, K, V, att, spec["max_len"], SCALE, "gelu")
+    o = (att.float() + ln.float()).to(torch.bfloat16).contiguous()
+    y = empty_bf16(T, H * D)
+    B.fng_rmsnorm(o.view(T, H * D), y, spec["eps_rms"])
+    unfused = (y.float().view(T, H, D) + Q.float()).to(torch.bfloat16)
+    fused, _ = run_fna(d, spec["max_len"], "gelu", spec["eps_ln"], spec["eps_rms"])
+    ref, _, _, _ = oracle.flash_norm_attention(f64(d["Q"]), d["offsets"], f64(d["K"]), f64(d["V"]),
+                                               spec["eps_ln"], spec["eps_rms"], SCALE, "gelu")
+    fna_parity(host(fused), ref, "fused fna")
+    # the unfused chain rounds four intermediates (ln, attention, o, rmsnorm)
+    # to bf16 between its kernels, each about one more output-rounding floor:
+    # it gets twice the scaled MAE bound, and the fused kernel must beat it
+    eu = assert_parity(host(unfused), ref, "unfused ln + attention + rmsnorm",
+                       mae=4e-3 * max(1.0, float(np.mean(np.abs(ref))) / 0.8))
+    assert oracle.compare(host(fused), ref)["mae"] < eu["mae"]
+
+
+@pytest.fixture(scope="module")
+def full_inputs():
+    return inputs.make_inputs("flash_norm_attention")
+
+
+@pytest.mark.parametrize("act", ["gelu", "softmax"])
+def test_fna_full_size_sampled(full_inputs, act):
+    spec, d = full_inputs
+    off = d["offsets"]
+    log(f"fna full size B={spec['B']} T={off[-1]} Skv={spec['Skv']} H={spec['H']} act={act}")
+    O, st = run_fna(d, spec["max_len"], act, spec["eps_ln"], spec["eps_rms"])
+    y = host(O)
+    lengths = np.diff(off)
+    picks = [0, int(np.argmax(lengths)), int(np.argmin(lengths)), 383, spec["B"] - 1]
+    for b in picks:
+        r0, r1 = int(off[b]), int(off[b + 1])
+        ref, mu, r1s, r2s = oracle.flash_norm_attention(
+            f64(d["Q"][r0:r1]), np.array([0, r1 - r0]), f64(d["K"][b:b + 1]), f64(d["V"][b:b + 1]),
+            spec["eps_ln"], spec["eps_rms"], SCALE, act)
+        fna_parity(y[r0:r1], ref, f"fna full size batch {b} (len {r1 - r0})")
+        assert_close_stats(st[2].cpu().numpy()[r0:r1], r2s, "fna rms rstd", rtol=3e-3)
+    # every row: out - x has unit RMS over all heads (up to eps and bf16 rounding)
+    r = (O.float() - dev(d["Q"]).float()).reshape(O.shape[0], -1)
+    rms = torch.sqrt(torch.mean(r * r, dim=1)).cpu().numpy()
+    assert np.max(np.abs(rms - 1.0)) < 1e-2, np.max(np.abs(rms - 1.0))
+
+
+def test_fna_empty_calls():
+    Q = empty_bf16(0, 4, 128)
+    K = empty_bf16(2, 8, 4, 128)
+    off = torch.zeros(3, dtype=torch.int32, device="cuda")
+    B.fng_flash_norm_attention(Q, off, K, K, Q, 16, 1e-5, 1e-6)
+    B.fng_jagged_attention(Q, off, K, K, Q, 16)
+    torch.cuda.synchronize()
