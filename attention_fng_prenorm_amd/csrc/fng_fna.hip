@@ -57,12 +57,14 @@ struct FnaParams {
 
 __device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// GELU, tanh form: 0.5 s (1 + tanh(u)), u = sqrt(2/pi) (s + 0.044715 s^3),
-// tanh(u) = 1 - 2 / (1 + e^(2u)) (saturates correctly for large |u|)
+// GELU, tanh form: 0.5 s (1 + tanh(u)) with u = sqrt(2/pi) (s + 0.044715 s^3),
+// evaluated as s * sigmoid(2u) = s / (1 + 2^w), w = -2 u log2(e): one exp2 and
+// one reciprocal; saturates to s (w -> -inf) and to -0 (w -> +inf, 2^w = inf)
+constexpr float kGeluC0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+constexpr float kGeluC1 = kGeluC0 * 0.044715f;
 __device__ __forceinline__ float gelu_tanh(float s) {
-  const float u = 0.7978845608028654f * fmaf(0.044715f * s, s * s, s);
-  const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // e^(2u)
-  return 0.5f * s * (2.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e));
+  const float w = s * fmaf(kGeluC1, s * s, kGeluC0);
+  return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
 }
 
 template <int H, bool NORM, int ACT>
@@ -101,59 +103,6 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.K + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * H * kD * 2));
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.V + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * H * kD * 2));
   const uint32_t qrow_off = (uint32_t)(((size_t)qi * H + h) * kD * 2);
-
-  // ---- prologue: query fragments (lane holds d = 16kk + 8hi + 0..7) -------
-  u32x4_t qf[8];
-  float mu = 0.f, rstd = 1.f;
-  {
-    u32x4_t raw[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) raw[kk] = buffer_load16(qr, qrow_off + (uint32_t)(16 * kk + 8 * hi) * 2u);
-    if constexpr (NORM) {
-      // this head's (mean, M2) over its 128 values, then merged across heads
-      float s = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s += bf16lo(raw[kk][e]) + bf16hi(raw[kk][e]);
-      const float mh = half_swap_sum(s) * (1.0f / kD);
-      float s2 = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a0 = bf16lo(raw[kk][e]) - mh, a1 = bf16hi(raw[kk][e]) - mh;
-          s2 += a0 * a0 + a1 * a1;
-        }
-      const float m2h = half_swap_sum(s2);
-      if (hi == 0) {
-        xch[(lrow * H + h) * 2 + 0] = mh;
-        xch[(lrow * H + h) * 2 + 1] = m2h;
-      }
-      __syncthreads();
-      float msum = 0.f;
-#pragma unroll
-      for (int j = 0; j < H; ++j) msum += xch[(lrow * H + j) * 2 + 0];
-      mu = msum * (1.0f / H);
-      float m2 = 0.f;
-#pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const float dm = xch[(lrow * H + j) * 2 + 0] - mu;
-        m2 += xch[(lrow * H + j) * 2 + 1] + (float)kD * dm * dm;
-      }
-      rstd = __builtin_amdgcn_rsqf(m2 * (1.0f / (H * kD)) + p.eps_ln);
-      if (h == 0 && hi == 0 && valid) {
-        if (p.ln_mean_out) p.ln_mean_out[row] = mu;
-        if (p.ln_rstd_out) p.ln_rstd_out[row] = rstd;
-      }
-    }
-    const float mul = rstd * p.scale;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qf[kk][e] = pack_f16((bf16lo(raw[kk][e]) - mu) * mul, (bf16hi(raw[kk][e]) - mu) * mul);
-  }
 
   // ---- K/V staging, all heads of one 32-key tile ---------------------------
   // K: chunk c = tid + 512 i (i < H) is head i, key (tid / 16), d 8 (tid % 16)..
@@ -203,9 +152,76 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
     }
   };
 
+  gload(0);  // the first key tile's loads overlap the query prologue
+
+  // ---- prologue: query fragments (lane holds d = 16kk + 8hi + 0..7) -------
+  u32x4_t qf[8];
+  float mu = 0.f, rstd = 1.f;
+  {
+    u32x4_t raw[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) raw[kk] = buffer_load16(qr, qrow_off + (uint32_t)(16 * kk + 8 * hi) * 2u);
+    if constexpr (NORM) {
+      // this head's sum and sum of squares over its 128 values (exact bf16
+      // products, fp32 accumulation), then (mean, M2) merged across heads
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+      float s[2] = {0.f, 0.f}, s2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = raw[kk][e];
+          const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w);
+          s[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(v, ones, s[e & 1], false);
+          s2[e & 1] = __builtin_amdgcn_fdot2_f32_bf16(v, v, s2[e & 1], false);
+        }
+      const float sh = half_swap_sum(s[0] + s[1]);
+      const float mh = sh * (1.0f / kD);
+      const float m2h = fmaxf(half_swap_sum(s2[0] + s2[1]) - sh * mh, 0.f);
+      if (hi == 0) {
+        xch[(lrow * H + h) * 2 + 0] = mh;
+        xch[(lrow * H + h) * 2 + 1] = m2h;
+      }
+      __syncthreads();
+      float msum = 0.f;
+#pragma unroll
+      for (int j = 0; j < H; ++j) msum += xch[(lrow * H + j) * 2 + 0];
+      mu = msum * (1.0f / H);
+      float m2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const float dm = xch[(lrow * H + j) * 2 + 0] - mu;
+        m2 += xch[(lrow * H + j) * 2 + 1] + (float)kD * dm * dm;
+      }
+      rstd = __builtin_amdgcn_rsqf(m2 * (1.0f / (H * kD)) + p.eps_ln);
+      if (h == 0 && hi == 0 && valid) {
+        if (p.ln_mean_out) p.ln_mean_out[row] = mu;
+        if (p.ln_rstd_out) p.ln_rstd_out[row] = rstd;
+      }
+    }
+    const float mul = rstd * p.scale, add = -mu * mul;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = raw[kk][e];
+        qf[kk][e] = pack_f16(fmaf(bf16lo(w), mul, add), fmaf(bf16hi(w), mul, add));
+      }
+  }
+
   // fragment offsets: K row kappa(l32), chunk hi; V^T row l32, keys 8hi..
   const int koff = h * kTileK + kappa(l32) * kRowK + hi * 16;
   const int voff = H * kTileK + h * kTileV + l32 * kRowV + hi * 16;
+
+  // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e
+  u32x2_t xq[4][4];
+  auto xload = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        xq[dt][r4] = buffer_load8(qr, qrow_off + (uint32_t)(32 * dt + 8 * r4 + 4 * hi) * 2u);
+  };
 
   f32x16_t o[4];
 #pragma unroll
@@ -215,30 +231,28 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   float mrun = -INFINITY, lrun = 0.f;
 
   const int ntiles = (p.Skv + kKT - 1) / kKT;
-  gload(0);
   sstore(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     const bool more = kt + 1 < ntiles;
     if (more) gload(kt + 1);
+    else if constexpr (NORM) xload();  // raw query rows for the residuals
     const FNG_LDS char* st = lds + (kt & 1) * STAGE;
 
-    // S^T (32 keys x 32 queries): register r <-> key 16(r/8) + 8hi + r%8;
-    // two accumulators break the dependency chain over the 8 k16 steps
-    f32x16_t sa, sb;
+    // S^T (32 keys x 32 queries): register r <-> key 16(r/8) + 8hi + r%8
+    f32x16_t sa;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = sb[r] = 0.f;
+    for (int r = 0; r < 16; ++r) sa[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; kk += 2) {
-      sa = mfma_f16(lds_read16(st + koff + kk * 32), qf[kk], sa);
-      sb = mfma_f16(lds_read16(st + koff + (kk + 1) * 32), qf[kk + 1], sb);
-    }
+    for (int kk = 0; kk < 8; ++kk) sa = mfma_f16(lds_read16(st + koff + kk * 32), qf[kk], sa);
     float sc[16];
-    const int kvalid = p.Skv - kt * kKT;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = sa[r] + sb[r];
-      if (16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) sc[r] = (ACT == ACT_SOFTMAX) ? -INFINITY : 0.f;
+    for (int r = 0; r < 16; ++r) sc[r] = sa[r];
+    const int kvalid = p.Skv - kt * kKT;
+    if (kvalid < kKT) {  // ragged last tile only
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) sc[r] = (ACT == ACT_SOFTMAX) ? -INFINITY : 0.f;
     }
     float pr[16];
     if constexpr (ACT == ACT_SOFTMAX) {
@@ -287,14 +301,7 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   }
 
   // ---- epilogue ------------------------------------------------------------
-  // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e
   const float inv = (ACT == ACT_SOFTMAX) ? 1.0f / half_swap_sum(lrun) : 1.0f;
-  u32x2_t xq[4][4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      xq[dt][r4] = buffer_load8(qr, qrow_off + (uint32_t)(32 * dt + 8 * r4 + 4 * hi) * 2u);
   float rstd2 = 1.f;
   if constexpr (NORM) {
     float ss = 0.f;
