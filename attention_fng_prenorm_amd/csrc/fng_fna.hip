@@ -18,11 +18,21 @@
 // each head merged with the pairwise formula for the LayerNorm, sums of
 // squares for the RMSNorm.
 //
-// Per key tile every wave computes S^T = K_h Q^T (its A rows loaded in the
-// key order that hands P to the next MFMA without a shuffle, as in the
-// norm-sandwiched attention kernel), the activation, and O^T += V_h^T P^T;
-// fp16 MFMA operands, fp32 accumulation.  The raw query rows are read again
-// in the epilogue for the two residuals rather than held in registers.
+// Data movement: every global read is an HBM -> LDS copy of whole rows
+// (buffer_load ... lds, 16 B per lane, 16-B chunks XOR-swizzled per row so
+// the fragment reads below are bank-conflict free): the block's query rows
+// (all heads, contiguous in memory), key/value tiles of 32 keys for all heads
+// (double-buffered: tile t+1 is in flight while tile t is computed), and the
+// raw query rows again for the residuals while the last tile is computed.
+// The output goes back through LDS so that it is stored as whole rows.
+//
+// Arithmetic: K and V stay bf16 as stored.  The normalized queries and the
+// activations P are split into bf16 high and low parts (x = hi + lo to about
+// 16 significant bits), so every product is a bf16 MFMA with fp32
+// accumulation: S^T = K_h (q_hi + q_lo)^T, O^T += V_h^T (P_hi + P_lo)^T.  K
+// fragments are read with ds_read_b128 in the key order that hands P to the
+// next MFMA without a shuffle; V^T fragments come from V [key][d] through the
+// transposing read ds_read_b64_tr_b16.
 #include "fng_device.h"
 #include "fng_internal.h"
 
@@ -32,10 +42,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kKT = 32;                 // keys per tile
-constexpr int kRowK = kD * 2 + 16;      // bytes per K row ([key][d]), padded
-constexpr int kRowV = kKT * 2 + 16;     // bytes per V^T row ([d][key]), padded
-constexpr int kTileK = kKT * kRowK;     // per head
-constexpr int kTileV = kD * kRowV;      // per head
+constexpr int kRowB = kD * 2;           // bytes of one head's row
+constexpr int kTileB = kKT * kRowB;     // one head's K (or V) tile, [key][d]
+constexpr int kQSB = 64 * 1024;         // a block's query rows: 32 * (8/H) rows x H * 256 B
 constexpr float kLazy = 8.0f;           // running-max hysteresis (log2 units)
 
 enum : int { ACT_SOFTMAX = 0, ACT_GELU = 1 };
@@ -69,18 +78,23 @@ __device__ __forceinline__ float gelu_tanh(float s) {
 
 template <int H, bool NORM, int ACT>
 __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
-  constexpr int G = 8 / H;            // row groups
-  constexpr int BM = 32 * G;          // query rows per workgroup
-  constexpr int STAGE = H * (kTileK + kTileV);
-  constexpr int NST = 2;
-  static_assert(NST * STAGE + BM * H * 2 * 4 <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE + BM * H * 2 * 4];
+  constexpr int G = 8 / H;                 // row groups
+  constexpr int BM = 32 * G;               // query rows per workgroup
+  constexpr int RB = H * kRowB;            // bytes per query row (all heads)
+  constexpr int STG = 2 * H * kTileB;      // one K/V stage: K of every head, then V
+  // query staging: one whole stage when it fits (H = 4), else its own region
+  constexpr int QSEP = 2 * STG;
+  constexpr int MAIN = (H == 4) ? 2 * STG : 2 * STG + kQSB;
+  static_assert(BM * RB == kQSB, "query block size");
+  static_assert(H != 4 || STG == kQSB, "query block fills one stage");
+  static_assert(MAIN + BM * H * 8 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[MAIN + BM * H * 8];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
-  FNG_LDS float* xch = (FNG_LDS float*)(lds + NST * STAGE);  // [BM][H][2] statistics exchange
+  FNG_LDS float* xch = (FNG_LDS float*)(lds + MAIN);  // [BM][H][2] statistics exchange
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = wave % H;
   const int g = wave / H;
   const int l32 = lane & 31;
@@ -97,70 +111,53 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   const int qi = qb * BM + lrow;           // row within the batch
   const int row = r0 + qi;                 // global query row
   const bool valid = qi < len && row < p.T;
-  // query rows of this batch, beyond its length read as zero
-  const uint32_t qbytes = (uint32_t)(max(0, min(len, p.T - r0)) * H * kD * 2);
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(p.Q + (size_t)r0 * H * kD, qbytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(p.K + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * H * kD * 2));
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(p.V + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * H * kD * 2));
-  const uint32_t qrow_off = (uint32_t)(((size_t)qi * H + h) * kD * 2);
+  // the batch's query rows that exist; rows past them copy as zeros
+  const int brows = max(0, min(len, p.T - r0));
+  const i32x4_t qr = dma_rsrc(p.Q + (size_t)r0 * H * kD, (uint32_t)(brows * RB));
+  const i32x4_t kr = dma_rsrc(p.K + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
+  const i32x4_t vr = dma_rsrc(p.V + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
+  const uint32_t qblk = (uint32_t)(qb * BM) * (uint32_t)RB;
 
-  // ---- K/V staging, all heads of one 32-key tile ---------------------------
-  // K: chunk c = tid + 512 i (i < H) is head i, key (tid / 16), d 8 (tid % 16)..
-  // V: item j = tid + 512 i (i < H / 2, or tid < 256 for one head) is head
-  //    j / 256, keys 2p, 2p+1 (p = j % 16), d 8 ((j / 16) % 16).., written
-  //    transposed as one 4-byte word per d row.
-  constexpr int VIT = H >= 2 ? H / 2 : 1;
-  u32x4_t rk[H], rv[VIT][2];
-  auto gload = [&](int kt) __attribute__((always_inline)) {
+  // ---- HBM -> LDS copies ---------------------------------------------------
+  // Rows keep their global layout; the 16-B chunk c of row r sits at chunk
+  // c ^ (r % 16) (query rows, K) or c ^ 4 (r % 4) (V).  Wave w copies 1 KB
+  // blocks; lane l's 16 B are block byte 16 l.
+  auto copy_q = [&](FNG_LDS char* qs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < H; ++i) {
-      const int key = kt * kKT + (tid >> 4), dc = tid & 15;
-      rk[i] = buffer_load16(kr, (uint32_t)((((size_t)key * H + i) * kD + dc * 8) * 2));
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int j = tid + 512 * i;
-      if (H == 1 && j >= 256) continue;
-      const int hv = j >> 8, pp = j & 15, dc = (j >> 4) & 15;
-      const int key = kt * kKT + 2 * pp;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        rv[i][u] = buffer_load16(vr, (uint32_t)((((size_t)(key + u) * H + hv) * kD + dc * 8) * 2));
+    for (int i = 0; i < 8; ++i) {
+      const int blk = wave * 8 + i;
+      const int idx = blk * 1024 + lane * 16;
+      const int r = idx / RB, pc = (idx % RB) / 16;
+      dma16(qr, qs + blk * 1024, qblk + (uint32_t)(r * RB + (pc ^ (r & 15)) * 16));
     }
   };
-  auto sstore = [&](int buf) __attribute__((always_inline)) {
-    FNG_LDS char* st = lds + buf * STAGE;
+  auto copy_kv = [&](int kt, int s) __attribute__((always_inline)) {
+    FNG_LDS char* st = lds + s * STG;
 #pragma unroll
     for (int i = 0; i < H; ++i) {
-      u32x4_t v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = bf16x2_to_f16x2(rk[i][e]);
-      lds_write16(st + i * kTileK + (tid >> 4) * kRowK + (tid & 15) * 16, v);
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int j = tid + 512 * i;
-      if (H == 1 && j >= 256) continue;
-      const int hv = j >> 8, pp = j & 15, dc = (j >> 4) & 15;
-      FNG_LDS char* dst = st + H * kTileK + hv * kTileV + (dc * 8) * kRowV + pp * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<FNG_LDS uint32_t*>(dst + (2 * e) * kRowV) = pack_f16(bf16lo(rv[i][0][e]), bf16lo(rv[i][1][e]));
-        *reinterpret_cast<FNG_LDS uint32_t*>(dst + (2 * e + 1) * kRowV) =
-            pack_f16(bf16hi(rv[i][0][e]), bf16hi(rv[i][1][e]));
-      }
+      const int blk = wave * H + i;                 // head blk / 8, keys 4 (blk % 8) ..
+      const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
+      const uint32_t base = (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2);
+      dma16(kr, st + blk * 1024, base + (uint32_t)((pc ^ (r & 15)) * 16));
+      dma16(vr, st + H * kTileB + blk * 1024, base + (uint32_t)((pc ^ (4 * (r & 3))) * 16));
     }
   };
 
-  gload(0);  // the first key tile's loads overlap the query prologue
+  // ---- prologue: the block's query rows and the first key tile -------------
+  FNG_LDS char* qs_pro = lds + (H == 4 ? STG : QSEP);
+  copy_q(qs_pro);
+  copy_kv(0, 0);
+  wait_vmcnt<2 * H>();  // this wave's query copies have landed
+  lds_barrier();
 
-  // ---- prologue: query fragments (lane holds d = 16kk + 8hi + 0..7) -------
-  u32x4_t qf[8];
+  // lane holds d = 16kk + 8hi + 0..7 of its row and head: the MFMA B operand
+  u32x4_t qh[8], ql[8];
   float mu = 0.f, rstd = 1.f;
   {
     u32x4_t raw[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) raw[kk] = buffer_load16(qr, qrow_off + (uint32_t)(16 * kk + 8 * hi) * 2u);
+    for (int kk = 0; kk < 8; ++kk)
+      raw[kk] = lds_read16(qs_pro + lrow * RB + (((16 * h + 2 * kk + hi) ^ (lrow & 15)) * 16));
     if constexpr (NORM) {
       // this head's sum and sum of squares over its 128 values (exact bf16
       // products, fp32 accumulation), then (mean, M2) merged across heads
@@ -199,29 +196,37 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
         if (p.ln_rstd_out) p.ln_rstd_out[row] = rstd;
       }
     }
+    // normalized (and pre-scaled) query, split into bf16 high and low parts
     const float mul = rstd * p.scale, add = -mu * mul;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t w = raw[kk][e];
-        qf[kk][e] = pack_f16(fmaf(bf16lo(w), mul, add), fmaf(bf16hi(w), mul, add));
+        const float x0 = fmaf(bf16lo(w), mul, add), x1 = fmaf(bf16hi(w), mul, add);
+        const uint32_t hw = pack_bf16(x0, x1);
+        qh[kk][e] = hw;
+        ql[kk][e] = pack_bf16(x0 - bf16lo(hw), x1 - bf16hi(hw));
       }
   }
 
-  // fragment offsets: K row kappa(l32), chunk hi; V^T row l32, keys 8hi..
-  const int koff = h * kTileK + kappa(l32) * kRowK + hi * 16;
-  const int voff = H * kTileK + h * kTileV + l32 * kRowV + hi * 16;
-
-  // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e
-  u32x2_t xq[4][4];
-  auto xload = [&]() __attribute__((always_inline)) {
+  // ---- main loop over key tiles ----------------------------------------------
+  // K fragment (A operand of S^T): row kappa(l32), 16 B at d = 16kk + 8hi.
+  const int krow = kappa(l32);
+  int koff[8];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = h * kTileB + krow * kRowB + (((2 * kk + hi) ^ (krow & 15)) * 16);
+  // V^T fragment (A operand of O^T) through two transposing reads: lane
+  // (group g4 = lane / 16, li = lane % 16) addresses key 8 (g4 / 2) + li / 4
+  // (+4 for the second read) and d = 32 dt + 16 (g4 % 2) + 4 (li % 4)
+  const int g4 = lane >> 4, li = lane & 15;
+  const int vkey = 8 * (g4 >> 1) + (li >> 2);
+  int voff[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        xq[dt][r4] = buffer_load8(qr, qrow_off + (uint32_t)(32 * dt + 8 * r4 + 4 * hi) * 2u);
-  };
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
+    voff[dt] = H * kTileB + h * kTileB + vkey * kRowB + ((((d >> 3) ^ (4 * (vkey & 3)))) * 16) + (d & 7) * 2;
+  }
 
   f32x16_t o[4];
 #pragma unroll
@@ -231,20 +236,25 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   float mrun = -INFINITY, lrun = 0.f;
 
   const int ntiles = (p.Skv + kKT - 1) / kKT;
-  sstore(0);
-  __syncthreads();
+  // residual / output staging: the stage the last tile does not use (H = 4)
+  FNG_LDS char* qs_epi = lds + (H == 4 ? (ntiles & 1) * STG : QSEP);
   for (int kt = 0; kt < ntiles; ++kt) {
-    const bool more = kt + 1 < ntiles;
-    if (more) gload(kt + 1);
-    else if constexpr (NORM) xload();  // raw query rows for the residuals
-    const FNG_LDS char* st = lds + (kt & 1) * STAGE;
+    wait_vmcnt<0>();
+    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt - 1
+    if (kt + 1 < ntiles) copy_kv(kt + 1, (kt + 1) & 1);
+    else if constexpr (NORM) copy_q(qs_epi);  // raw query rows for the residuals
+    const FNG_LDS char* st = lds + (kt & 1) * STG;
 
     // S^T (32 keys x 32 queries): register r <-> key 16(r/8) + 8hi + r%8
     f32x16_t sa;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) sa = mfma_f16(lds_read16(st + koff + kk * 32), qf[kk], sa);
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4_t kf = lds_read16(st + koff[kk]);
+      sa = mfma_bf16(kf, qh[kk], sa);
+      sa = mfma_bf16(kf, ql[kk], sa);
+    }
     float sc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = sa[r];
@@ -270,40 +280,59 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
       }
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[r] - mrun);
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(sc[r] - mrun);
+        ls[r & 1] += pr[r];
+      }
+      lrun += ls[0] + ls[1];
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) pr[r] = gelu_tanh(sc[r]);
     }
-    // P^T operand, k16 step c: keys 16c + 8hi + (0..7); row sum over the
-    // same fp16 values (softmax)
-    u32x4_t pf[2];
-    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float ls[2] = {0.f, 0.f};
+    // P^T operand, k16 step c: keys 16c + 8hi + (0..7), as bf16 hi + lo
+    u32x4_t ph[2], pl[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const f16x2_t h2 = {(_Float16)pr[8 * c + 2 * e], (_Float16)pr[8 * c + 2 * e + 1]};
-        pf[c][e] = __builtin_bit_cast(uint32_t, h2);
-        if constexpr (ACT == ACT_SOFTMAX) ls[e & 1] = __builtin_amdgcn_fdot2(h2, ones, ls[e & 1], false);
+        const float a0 = pr[8 * c + 2 * e], a1 = pr[8 * c + 2 * e + 1];
+        const uint32_t hw = pack_bf16(a0, a1);
+        ph[c][e] = hw;
+        pl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
       }
-    if constexpr (ACT == ACT_SOFTMAX) lrun += ls[0] + ls[1];
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        o[dt] = mfma_f16(lds_read16(st + voff + c * 32 + dt * 32 * kRowV), pf[c], o[dt]);
-    if (more) sstore((kt + 1) & 1);
-    __syncthreads();
+      for (int dt = 0; dt < 4; ++dt) {
+        const FNG_LDS char* va = st + voff[dt] + c * 16 * kRowB;
+        const u32x2_t lo = lds_read_tr16(va);
+        const u32x2_t hi2 = lds_read_tr16(va + 4 * kRowB);
+        const u32x4_t vf = {lo[0], lo[1], hi2[0], hi2[1]};
+        o[dt] = mfma_bf16(vf, ph[c], o[dt]);
+        o[dt] = mfma_bf16(vf, pl[c], o[dt]);
+      }
   }
 
   // ---- epilogue ------------------------------------------------------------
+  wait_vmcnt<0>();
+  lds_barrier();  // residual rows are in LDS; every wave is done with the last tile
+  // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e:
+  // 8 B at chunk 16h + 4dt + r4 (swizzled), byte 8hi of the chunk
+  auto epi_addr = [&](int dt, int r4) __attribute__((always_inline)) {
+    return qs_epi + lrow * RB + (((16 * h + 4 * dt + r4) ^ (lrow & 15)) * 16) + hi * 8;
+  };
   const float inv = (ACT == ACT_SOFTMAX) ? 1.0f / half_swap_sum(lrun) : 1.0f;
   float rstd2 = 1.f;
+  u32x2_t xq[4][4];
   if constexpr (NORM) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) xq[dt][r4] = *reinterpret_cast<const FNG_LDS u32x2_t*>(epi_addr(dt, r4));
+    const float add1 = -mu * rstd;
     float ss = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -312,13 +341,12 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
         const float x[4] = {bf16lo(xq[dt][r4][0]), bf16hi(xq[dt][r4][0]), bf16lo(xq[dt][r4][1]), bf16hi(xq[dt][r4][1])};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = fmaf(o[dt][4 * r4 + e], inv, (x[e] - mu) * rstd);  // + ln (residual 1)
+          const float v = fmaf(o[dt][4 * r4 + e], inv, fmaf(x[e], rstd, add1));  // + ln (residual 1)
           o[dt][4 * r4 + e] = v;
           ss = fmaf(v, v, ss);
         }
       }
     ss = half_swap_sum(ss);
-    __syncthreads();  // the prologue's statistics have been read
     if (hi == 0) xch[(lrow * H + h) * 2] = ss;
     __syncthreads();
     float tot = 0.f;
@@ -327,8 +355,7 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
     rstd2 = __builtin_amdgcn_rsqf(tot * (1.0f / (H * kD)) + p.eps_rms);
     if (h == 0 && hi == 0 && valid && p.rms_rstd_out) p.rms_rstd_out[row] = rstd2;
   }
-  if (!valid) return;
-  uint16_t* orow = p.O + ((size_t)row * H + h) * kD;
+  // the output replaces the residual rows in LDS (each lane rewrites what it read)
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -342,9 +369,20 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * r4 + e] * inv;
       }
-      *reinterpret_cast<u32x2_t*>(orow + 32 * dt + 8 * r4 + 4 * hi) =
-          u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      *reinterpret_cast<FNG_LDS u32x2_t*>(epi_addr(dt, r4)) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
+  lds_barrier();
+  // whole rows back to HBM: 16 B per lane, rows of the batch only
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 512 * i;
+    const int r = c / (RB / 16), lc = c % (RB / 16);
+    const int q = qb * BM + r;
+    if (q < len && r0 + q < p.T) {
+      const u32x4_t v = lds_read16(qs_epi + r * RB + ((lc ^ (r & 15)) * 16));
+      *reinterpret_cast<u32x4_t*>(p.O + (size_t)(r0 + q) * H * kD + lc * 8) = v;
+    }
+  }
 }
 
 template <int H>

@@ -90,44 +90,6 @@ __device__ __forceinline__ int swz_a(int row) {
 template <int NC>
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) << 2) & (NC - 1); }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
-// only (global copies are waited for explicitly with wait_vmcnt), and is a
-// compiler memory barrier
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// HBM -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l
-// writes LDS bytes [base + 16 l, +16).  Written as inline asm so that the
-// compiler does not model the LDS write: it would otherwise wait for every
-// copy in flight before each LDS read.  The ring's explicit vmcnt waits and
-// barriers are the synchronization.  The descriptor words and the LDS base
-// are wave-uniform scalars.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
-                 (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffff),
-                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(i32x4_t rsrc, const FNG_LDS char* lds_wave_base, uint32_t off) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer range: DMA writes zeros
-
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams p) {
   constexpr int NWAVES = WAVES_M * WAVES_N;
