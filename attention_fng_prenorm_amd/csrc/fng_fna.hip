@@ -11,7 +11,7 @@
 // the plain activation attention (no norms, no residuals): the unfused
 // baseline's attention.
 //
-// Work split: one workgroup = 8 waves = (8/H row groups) x H heads; wave
+// Work split: one workgroup = 4 waves = (4/H row groups) x H heads; wave
 // (g, h) owns 32 query rows of head h.  The page's norms run across heads, so
 // where it exchanges statistics between the CTAs of a cluster, the waves of
 // one workgroup exchange per-(row, head) partials through LDS: (mean, M2) of
@@ -21,9 +21,12 @@
 // Data movement: every global read is an HBM -> LDS copy of whole rows
 // (buffer_load ... lds, 16 B per lane, 16-B chunks XOR-swizzled per row so
 // the fragment reads below are bank-conflict free): the block's query rows
-// (all heads, contiguous in memory), key/value tiles of 32 keys for all heads
-// (double-buffered: tile t+1 is in flight while tile t is computed), and the
-// raw query rows again for the residuals while the last tile is computed.
+// (all heads, contiguous in memory), key and value tiles of 32 keys for all
+// heads, and the raw query rows again for the residuals while the last tile
+// is computed.  One K region and one V region are recycled separately: the
+// next K tile is copied while this tile's activation and P V run, the next V
+// tile while the next scores are computed.  At 65 KB of LDS two workgroups
+// share a CU, so one's MFMAs overlap the other's vector work and copies.
 // The output goes back through LDS so that it is stored as whole rows.
 //
 // Arithmetic: K and V stay bf16 as stored.  The normalized queries and the
@@ -44,7 +47,7 @@ constexpr int kD = 128;
 constexpr int kKT = 32;                 // keys per tile
 constexpr int kRowB = kD * 2;           // bytes of one head's row
 constexpr int kTileB = kKT * kRowB;     // one head's K (or V) tile, [key][d]
-constexpr int kQSB = 64 * 1024;         // a block's query rows: 32 * (8/H) rows x H * 256 B
+constexpr int kQSB = 32 * 1024;         // a block's query rows: 32 * (4/H) rows x H * 256 B
 constexpr float kLazy = 8.0f;           // running-max hysteresis (log2 units)
 
 enum : int { ACT_SOFTMAX = 0, ACT_GELU = 1 };
@@ -77,17 +80,22 @@ __device__ __forceinline__ float gelu_tanh(float s) {
 }
 
 template <int H, bool NORM, int ACT>
-__global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
-  constexpr int G = 8 / H;                 // row groups
+__global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
+  constexpr int G = 4 / H;                 // row groups
   constexpr int BM = 32 * G;               // query rows per workgroup
   constexpr int RB = H * kRowB;            // bytes per query row (all heads)
-  constexpr int STG = 2 * H * kTileB;      // one K/V stage: K of every head, then V
-  // query staging: one whole stage when it fits (H = 4), else its own region
-  constexpr int QSEP = 2 * STG;
-  constexpr int MAIN = (H == 4) ? 2 * STG : 2 * STG + kQSB;
+  constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
+  constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one K or V tile
+  constexpr int NQ = kQSB / 4096;          // ... for the block's query rows
+  // LDS: K tile | V tile | query rows (their own region unless they fit the V
+  // region, H = 4) | statistics exchange
+  constexpr int KREG = 0, VREG = KVB;
+  constexpr int QPRO = (H == 4) ? VREG : 2 * KVB;      // query rows in the prologue
+  constexpr int QEPI = (H == 4) ? KREG : 2 * KVB;      // residual rows / output
+  constexpr int MAIN = (H == 4) ? 2 * KVB : 2 * KVB + kQSB;
   static_assert(BM * RB == kQSB, "query block size");
-  static_assert(H != 4 || STG == kQSB, "query block fills one stage");
-  static_assert(MAIN + BM * H * 8 <= 160 * 1024, "LDS budget");
+  static_assert(H != 4 || KVB == kQSB, "query block fills the K or V region");
+  static_assert(MAIN + BM * H * 8 <= 80 * 1024, "two workgroups per CU");
   __shared__ __attribute__((aligned(1024))) char smem[MAIN + BM * H * 8];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
   FNG_LDS float* xch = (FNG_LDS float*)(lds + MAIN);  // [BM][H][2] statistics exchange
@@ -124,30 +132,30 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   // blocks; lane l's 16 B are block byte 16 l.
   auto copy_q = [&](FNG_LDS char* qs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int blk = wave * 8 + i;
+    for (int i = 0; i < NQ; ++i) {
+      const int blk = wave * NQ + i;
       const int idx = blk * 1024 + lane * 16;
       const int r = idx / RB, pc = (idx % RB) / 16;
       dma16(qr, qs + blk * 1024, qblk + (uint32_t)(r * RB + (pc ^ (r & 15)) * 16));
     }
   };
-  auto copy_kv = [&](int kt, int s) __attribute__((always_inline)) {
-    FNG_LDS char* st = lds + s * STG;
+  // K or V tile kt of every head: block j is head j / 8, keys 4 (j % 8) ..
+  auto copy_kv = [&](bool isv, int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < H; ++i) {
-      const int blk = wave * H + i;                 // head blk / 8, keys 4 (blk % 8) ..
+    for (int i = 0; i < NK; ++i) {
+      const int blk = wave * NK + i;
       const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
       const uint32_t base = (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2);
-      dma16(kr, st + blk * 1024, base + (uint32_t)((pc ^ (r & 15)) * 16));
-      dma16(vr, st + H * kTileB + blk * 1024, base + (uint32_t)((pc ^ (4 * (r & 3))) * 16));
+      if (isv) dma16(vr, lds + VREG + blk * 1024, base + (uint32_t)((pc ^ (4 * (r & 3))) * 16));
+      else dma16(kr, lds + KREG + blk * 1024, base + (uint32_t)((pc ^ (r & 15)) * 16));
     }
   };
 
   // ---- prologue: the block's query rows and the first key tile -------------
-  FNG_LDS char* qs_pro = lds + (H == 4 ? STG : QSEP);
-  copy_q(qs_pro);
-  copy_kv(0, 0);
-  wait_vmcnt<2 * H>();  // this wave's query copies have landed
+  copy_q(lds + QPRO);
+  copy_kv(false, 0);
+  if constexpr (H != 4) copy_kv(true, 0);
+  wait_vmcnt<(H == 4 ? NK : 2 * NK)>();  // this wave's query copies have landed
   lds_barrier();
 
   // lane holds d = 16kk + 8hi + 0..7 of its row and head: the MFMA B operand
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
     u32x4_t raw[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      raw[kk] = lds_read16(qs_pro + lrow * RB + (((16 * h + 2 * kk + hi) ^ (lrow & 15)) * 16));
+      raw[kk] = lds_read16(lds + QPRO + lrow * RB + (((16 * h + 2 * kk + hi) ^ (lrow & 15)) * 16));
     if constexpr (NORM) {
       // this head's sum and sum of squares over its 128 values (exact bf16
       // products, fp32 accumulation), then (mean, M2) merged across heads
@@ -191,10 +199,6 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
         m2 += xch[(lrow * H + j) * 2 + 1] + (float)kD * dm * dm;
       }
       rstd = __builtin_amdgcn_rsqf(m2 * (1.0f / (H * kD)) + p.eps_ln);
-      if (h == 0 && hi == 0 && valid) {
-        if (p.ln_mean_out) p.ln_mean_out[row] = mu;
-        if (p.ln_rstd_out) p.ln_rstd_out[row] = rstd;
-      }
     }
     // normalized (and pre-scaled) query, split into bf16 high and low parts
     const float mul = rstd * p.scale, add = -mu * mul;
@@ -209,13 +213,17 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
         ql[kk][e] = pack_bf16(x0 - bf16lo(hw), x1 - bf16hi(hw));
       }
   }
+  if constexpr (H == 4) {
+    lds_barrier();  // every wave has read its query rows: the V region is free
+    copy_kv(true, 0);
+  }
 
   // ---- main loop over key tiles ----------------------------------------------
   // K fragment (A operand of S^T): row kappa(l32), 16 B at d = 16kk + 8hi.
   const int krow = kappa(l32);
   int koff[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = h * kTileB + krow * kRowB + (((2 * kk + hi) ^ (krow & 15)) * 16);
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = KREG + h * kTileB + krow * kRowB + (((2 * kk + hi) ^ (krow & 15)) * 16);
   // V^T fragment (A operand of O^T) through two transposing reads: lane
   // (group g4 = lane / 16, li = lane % 16) addresses key 8 (g4 / 2) + li / 4
   // (+4 for the second read) and d = 32 dt + 16 (g4 % 2) + 4 (li % 4)
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
-    voff[dt] = H * kTileB + h * kTileB + vkey * kRowB + ((((d >> 3) ^ (4 * (vkey & 3)))) * 16) + (d & 7) * 2;
+    voff[dt] = VREG + h * kTileB + vkey * kRowB + ((((d >> 3) ^ (4 * (vkey & 3)))) * 16) + (d & 7) * 2;
   }
 
   f32x16_t o[4];
@@ -235,15 +243,13 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
+  // Copies in flight, oldest first: K(t), V(t) when tile t's scores start;
+  // V(t), then K(t+1) (or the residual rows) when its P V product starts.
   const int ntiles = (p.Skv + kKT - 1) / kKT;
-  // residual / output staging: the stage the last tile does not use (H = 4)
-  FNG_LDS char* qs_epi = lds + (H == 4 ? (ntiles & 1) * STG : QSEP);
   for (int kt = 0; kt < ntiles; ++kt) {
-    wait_vmcnt<0>();
-    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt - 1
-    if (kt + 1 < ntiles) copy_kv(kt + 1, (kt + 1) & 1);
-    else if constexpr (NORM) copy_q(qs_epi);  // raw query rows for the residuals
-    const FNG_LDS char* st = lds + (kt & 1) * STG;
+    const bool more = kt + 1 < ntiles;
+    wait_vmcnt<NK>();
+    lds_barrier();  // K tile kt is in LDS
 
     // S^T (32 keys x 32 queries): register r <-> key 16(r/8) + 8hi + r%8
     f32x16_t sa;
@@ -251,10 +257,14 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
     for (int r = 0; r < 16; ++r) sa[r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const u32x4_t kf = lds_read16(st + koff[kk]);
+      const u32x4_t kf = lds_read16(lds + koff[kk]);
       sa = mfma_bf16(kf, qh[kk], sa);
       sa = mfma_bf16(kf, ql[kk], sa);
     }
+    lds_barrier();  // every wave has read K tile kt
+    if (more) copy_kv(false, kt + 1);
+    else if constexpr (NORM) copy_q(lds + QEPI);  // raw query rows for the residuals
+
     float sc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = sa[r];
@@ -302,27 +312,37 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
         ph[c][e] = hw;
         pl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
       }
+
+    if (more) wait_vmcnt<NK>();
+    else if constexpr (NORM) wait_vmcnt<NQ>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // V tile kt is in LDS
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const FNG_LDS char* va = st + voff[dt] + c * 16 * kRowB;
+        const FNG_LDS char* va = lds + voff[dt] + c * 16 * kRowB;
         const u32x2_t lo = lds_read_tr16(va);
         const u32x2_t hi2 = lds_read_tr16(va + 4 * kRowB);
         const u32x4_t vf = {lo[0], lo[1], hi2[0], hi2[1]};
         o[dt] = mfma_bf16(vf, ph[c], o[dt]);
         o[dt] = mfma_bf16(vf, pl[c], o[dt]);
       }
+    if (more) {
+      lds_barrier();  // every wave has read V tile kt
+      copy_kv(true, kt + 1);
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------
   wait_vmcnt<0>();
   lds_barrier();  // residual rows are in LDS; every wave is done with the last tile
+  FNG_LDS char* qs = lds + QEPI;
   // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e:
   // 8 B at chunk 16h + 4dt + r4 (swizzled), byte 8hi of the chunk
   auto epi_addr = [&](int dt, int r4) __attribute__((always_inline)) {
-    return qs_epi + lrow * RB + (((16 * h + 4 * dt + r4) ^ (lrow & 15)) * 16) + hi * 8;
+    return qs + lrow * RB + (((16 * h + 4 * dt + r4) ^ (lrow & 15)) * 16) + hi * 8;
   };
   const float inv = (ACT == ACT_SOFTMAX) ? 1.0f / half_swap_sum(lrun) : 1.0f;
   float rstd2 = 1.f;
@@ -353,7 +373,11 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
 #pragma unroll
     for (int j = 0; j < H; ++j) tot += xch[(lrow * H + j) * 2];
     rstd2 = __builtin_amdgcn_rsqf(tot * (1.0f / (H * kD)) + p.eps_rms);
-    if (h == 0 && hi == 0 && valid && p.rms_rstd_out) p.rms_rstd_out[row] = rstd2;
+    if (h == 0 && hi == 0 && valid) {
+      if (p.ln_mean_out) p.ln_mean_out[row] = mu;
+      if (p.ln_rstd_out) p.ln_rstd_out[row] = rstd;
+      if (p.rms_rstd_out) p.rms_rstd_out[row] = rstd2;
+    }
   }
   // the output replaces the residual rows in LDS (each lane rewrites what it read)
 #pragma unroll
@@ -374,12 +398,12 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
   lds_barrier();
   // whole rows back to HBM: 16 B per lane, rows of the batch only
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 512 * i;
+  for (int i = 0; i < kQSB / (16 * 256); ++i) {
+    const int c = tid + 256 * i;
     const int r = c / (RB / 16), lc = c % (RB / 16);
     const int q = qb * BM + r;
     if (q < len && r0 + q < p.T) {
-      const u32x4_t v = lds_read16(qs_epi + r * RB + ((lc ^ (r & 15)) * 16));
+      const u32x4_t v = lds_read16(qs + r * RB + ((lc ^ (r & 15)) * 16));
       *reinterpret_cast<u32x4_t*>(p.O + (size_t)(r0 + q) * H * kD + lc * 8) = v;
     }
   }
@@ -387,7 +411,7 @@ __global__ __launch_bounds__(512, 1) void fna_kernel(FnaParams p) {
 
 template <int H>
 int launch_h(const FnaParams& p, bool norm, int act, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.qblocks)), block(512);
+  const dim3 grid((unsigned)(p.B * p.qblocks)), block(256);
   if (norm) {
     if (act == ACT_GELU) hipLaunchKernelGGL((fna_kernel<H, true, ACT_GELU>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((fna_kernel<H, true, ACT_SOFTMAX>), grid, block, 0, s, p);
@@ -417,7 +441,7 @@ int launch_fna(const FnaCall& c, bool norm, hipStream_t s) {
   p.scale = c.act == FNG_ACT_SOFTMAX ? c.sm_scale * 1.4426950408889634f : c.sm_scale;
   p.eps_ln = c.eps_ln;
   p.eps_rms = c.eps_rms;
-  const int bm = 32 * (8 / (int)c.H);
+  const int bm = 32 * (4 / (int)c.H);
   p.qblocks = (int)((c.max_len + bm - 1) / bm);
   const int act = c.act == FNG_ACT_GELU ? ACT_GELU : ACT_SOFTMAX;
   switch (c.H) {
