@@ -36,6 +36,8 @@
 // fragments are read with ds_read_b128 in the key order that hands P to the
 // next MFMA without a shuffle; V^T fragments come from V [key][d] through the
 // transposing read ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "fng_device.h"
 #include "fng_internal.h"
 
@@ -51,6 +53,9 @@ constexpr int kQSB = 32 * 1024;         // a block's query rows: 32 * (4/H) rows
 constexpr float kLazy = 8.0f;           // running-max hysteresis (log2 units)
 
 enum : int { ACT_SOFTMAX = 0, ACT_GELU = 1 };
+
+template <bool B>
+using flag = std::integral_constant<bool, B>;
 
 struct FnaParams {
   const uint16_t* Q;
@@ -242,17 +247,10 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
-
-  // Copies in flight, oldest first: K(t), V(t) when tile t's scores start;
-  // V(t), then K(t+1) (or the residual rows) when its P V product starts.
   const int ntiles = (p.Skv + kKT - 1) / kKT;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const bool more = kt + 1 < ntiles;
-    wait_vmcnt<NK>();
-    lds_barrier();  // K tile kt is in LDS
 
-    // S^T (32 keys x 32 queries): register r <-> key 16(r/8) + 8hi + r%8
-    f32x16_t sa;
+  // S^T (32 keys x 32 queries) of tile kt: register r <-> key 16(r/8) + 8hi + r%8
+  auto scores = [&](f32x16_t& sa) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = 0.f;
 #pragma unroll
@@ -261,48 +259,46 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
       sa = mfma_bf16(kf, qh[kk], sa);
       sa = mfma_bf16(kf, ql[kk], sa);
     }
-    lds_barrier();  // every wave has read K tile kt
-    if (more) copy_kv(false, kt + 1);
-    else if constexpr (NORM) copy_q(lds + QEPI);  // raw query rows for the residuals
-
-    float sc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = sa[r];
-    const int kvalid = p.Skv - kt * kKT;
-    if (kvalid < kKT) {  // ragged last tile only
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) sc[r] = (ACT == ACT_SOFTMAX) ? -INFINITY : 0.f;
-    }
+  };
+  // activation of tile kt's scores -> the P^T operand (k16 step c: keys
+  // 16c + 8hi + 0..7) as bf16 high and low parts.  Branch-free, so that it
+  // interleaves with the next tile's score MFMAs.  Keys past Skv have zero K
+  // rows (the copies zero-fill), hence score 0: GELU(0) = 0 needs no mask;
+  // softmax masks them (only the last tile, RAGGED).  Softmax keeps a running
+  // max and sum and returns the factor O must be rescaled by (rescale()).
+  auto activate = [&](auto ragged, const f32x16_t& sa, int kt, u32x4_t (&ph)[2], u32x4_t (&pl)[2])
+      __attribute__((always_inline)) {
+    constexpr bool RAGGED = decltype(ragged)::value;
     float pr[16];
+    float alpha = 1.f;
     if constexpr (ACT == ACT_SOFTMAX) {
+      float sc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[r] = sa[r];
+      if constexpr (RAGGED) {
+        const int kvalid = p.Skv - kt * kKT;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) sc[r] = -INFINITY;
+      }
       float mx = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
       mx = half_swap_max(mx);
       const float mnew = mx > mrun + kLazy ? mx : mrun;
-      const float alpha = (mnew == mrun || mrun == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+      alpha = (mnew == mrun || mrun == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
       mrun = mnew;
-      lrun *= alpha;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      }
       float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         pr[r] = __builtin_amdgcn_exp2f(sc[r] - mrun);
         ls[r & 1] += pr[r];
       }
-      lrun += ls[0] + ls[1];
+      lrun = fmaf(lrun, alpha, ls[0] + ls[1]);
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pr[r] = gelu_tanh(sc[r]);
+      for (int r = 0; r < 16; ++r) pr[r] = gelu_tanh(sa[r]);
     }
-    // P^T operand, k16 step c: keys 16c + 8hi + (0..7), as bf16 hi + lo
-    u32x4_t ph[2], pl[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -312,12 +308,20 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
         ph[c][e] = hw;
         pl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
       }
-
-    if (more) wait_vmcnt<NK>();
-    else if constexpr (NORM) wait_vmcnt<NQ>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // V tile kt is in LDS
-    // O^T += V^T P^T
+    return alpha;
+  };
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+    if constexpr (ACT == ACT_SOFTMAX) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      }
+    }
+  };
+  // O^T += V^T P^T with the V tile in the V region
+  auto pv = [&](const u32x4_t (&ph)[2], const u32x4_t (&pl)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -329,15 +333,65 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
         o[dt] = mfma_bf16(vf, ph[c], o[dt]);
         o[dt] = mfma_bf16(vf, pl[c], o[dt]);
       }
-    if (more) {
-      lds_barrier();  // every wave has read V tile kt
-      copy_kv(true, kt + 1);
+  };
+  // after the K region is read: the next K tile, or the residual rows
+  auto next_k = [&](int kt) __attribute__((always_inline)) {
+    if (kt + 1 < ntiles) copy_kv(false, kt + 1);
+    else if constexpr (NORM) copy_q(lds + QEPI);
+  };
+  // wait for the V tile, which is older than the copy next_k(kt) issued
+  auto wait_v = [&](int kt) __attribute__((always_inline)) {
+    if (kt + 1 < ntiles) wait_vmcnt<NK>();
+    else if constexpr (NORM) wait_vmcnt<NQ>();
+    else wait_vmcnt<0>();
+  };
+
+  // Software pipeline: the scores of tile kt are computed while the
+  // activation of tile kt - 1 runs (MFMA and vector work of one wave
+  // overlap), then tile kt - 1's P V product.  K is one tile ahead of V:
+  // the K region holds tile kt while the V region still holds tile kt - 1.
+  // Copies in flight, oldest first: K(kt), V(kt - 1) before tile kt's scores
+  // (V(0), K(1) at kt = 1); V(kt - 1), then K(kt + 1) or the residual rows
+  // before tile kt - 1's P V product.
+  f32x16_t scur, sprev;
+  u32x4_t ph[2], pl[2];
+  wait_vmcnt<NK>();
+  lds_barrier();  // K tile 0 is in LDS
+  scores(scur);
+  lds_barrier();  // every wave has read K tile 0
+  next_k(0);
+  for (int kt = 1; kt < ntiles; ++kt) {
+    sprev = scur;
+    if (kt == 1) wait_vmcnt<0>();
+    else wait_vmcnt<NK>();
+    lds_barrier();  // K tile kt is in LDS
+    scores(scur);
+    float alpha = activate(flag<false>{}, sprev, kt - 1, ph, pl);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // ten vector ops
     }
+    // the operands are produced here, beside the MFMAs, not sunk past the
+    // barrier to their use
+    asm volatile("" : "+v"(ph[0]), "+v"(ph[1]), "+v"(pl[0]), "+v"(pl[1]), "+v"(alpha));
+    lds_barrier();  // every wave has read K tile kt
+    next_k(kt);
+    wait_v(kt);
+    rescale(alpha);
+    lds_barrier();  // V tile kt - 1 is in LDS
+    pv(ph, pl);
+    lds_barrier();  // every wave has read V tile kt - 1
+    copy_kv(true, kt);
   }
+  const float alpha = activate(flag<true>{}, scur, ntiles - 1, ph, pl);
+  rescale(alpha);
+  wait_vmcnt<0>();
+  lds_barrier();  // the last V tile (and the residual rows) are in LDS
+  pv(ph, pl);
 
   // ---- epilogue ------------------------------------------------------------
-  wait_vmcnt<0>();
-  lds_barrier();  // residual rows are in LDS; every wave is done with the last tile
+  lds_barrier();  // every wave is done with the last tile
   FNG_LDS char* qs = lds + QEPI;
   // lane (l32, hi) holds, in register 4 r4 + e of o[dt], d = 32 dt + 8 r4 + 4 hi + e:
   // 8 B at chunk 16h + 4dt + r4 (swizzled), byte 8hi of the chunk
