@@ -334,15 +334,13 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
         o[dt] = mfma_bf16(vf, pl[c], o[dt]);
       }
   };
-  // after the K region is read: the next K tile, or the residual rows
+  // after the K region is read: the next K tile
   auto next_k = [&](int kt) __attribute__((always_inline)) {
     if (kt + 1 < ntiles) copy_kv(false, kt + 1);
-    else if constexpr (NORM) copy_q(lds + QEPI);
   };
   // wait for the V tile, which is older than the copy next_k(kt) issued
   auto wait_v = [&](int kt) __attribute__((always_inline)) {
     if (kt + 1 < ntiles) wait_vmcnt<NK>();
-    else if constexpr (NORM) wait_vmcnt<NQ>();
     else wait_vmcnt<0>();
   };
 
@@ -351,8 +349,8 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
   // overlap), then tile kt - 1's P V product.  K is one tile ahead of V:
   // the K region holds tile kt while the V region still holds tile kt - 1.
   // Copies in flight, oldest first: K(kt), V(kt - 1) before tile kt's scores
-  // (V(0), K(1) at kt = 1); V(kt - 1), then K(kt + 1) or the residual rows
-  // before tile kt - 1's P V product.
+  // (V(0), K(1) at kt = 1); V(kt - 1), then K(kt + 1) before tile kt - 1's
+  // P V product.
   f32x16_t scur, sprev;
   u32x4_t ph[2], pl[2];
   wait_vmcnt<NK>();
@@ -400,26 +398,41 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
   };
   const float inv = (ACT == ACT_SOFTMAX) ? 1.0f / half_swap_sum(lrun) : 1.0f;
   float rstd2 = 1.f;
-  u32x2_t xq[4][4];
+  // the residuals come from the split query still in registers: qh + ql is
+  // (x - mu) rstd scale to about 2^-17 relative, so ln = (qh + ql) / scale and
+  // x = (qh + ql) / (scale rstd) + mu.  Its lane layout (d = 16kk + 8hi + ..)
+  // is moved to O's (d = 32dt + 8r4 + 4hi + ..) by swapping the words the
+  // lane halves exchange (v_permlane32_swap): word pair e, e + 2 of kk gives
+  // d = 8(2kk) + 4hi + 2e .. in the first result and d = 8(2kk + 1) + 4hi + 2e
+  // .. in the second.
+  float xres[4][4][4];  // [dt][r4][e] residual-1 term ln and x, see below
   if constexpr (NORM) {
+    const float to_ln = 1.0f / p.scale;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) xq[dt][r4] = *reinterpret_cast<const FNG_LDS u32x2_t*>(epi_addr(dt, r4));
-    const float add1 = -mu * rstd;
+      for (int e = 0; e < 2; ++e) {
+        const auto sh = __builtin_amdgcn_permlane32_swap(qh[kk][e], qh[kk][e + 2], false, false);
+        const auto sl = __builtin_amdgcn_permlane32_swap(ql[kk][e], ql[kk][e + 2], false, false);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int m = 2 * kk + half;  // 8-block of d: dt = m / 4, r4 = m % 4
+          const uint32_t wh = half ? sh[1] : sh[0], wl = half ? sl[1] : sl[0];
+          xres[m >> 2][m & 3][2 * e] = (bf16lo(wh) + bf16lo(wl)) * to_ln;
+          xres[m >> 2][m & 3][2 * e + 1] = (bf16hi(wh) + bf16hi(wl)) * to_ln;
+        }
+      }
     float ss = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float x[4] = {bf16lo(xq[dt][r4][0]), bf16hi(xq[dt][r4][0]), bf16lo(xq[dt][r4][1]), bf16hi(xq[dt][r4][1])};
+      for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = fmaf(o[dt][4 * r4 + e], inv, fmaf(x[e], rstd, add1));  // + ln (residual 1)
+          const float v = fmaf(o[dt][4 * r4 + e], inv, xres[dt][r4][e]);  // + ln (residual 1)
           o[dt][4 * r4 + e] = v;
           ss = fmaf(v, v, ss);
         }
-      }
     ss = half_swap_sum(ss);
     if (hi == 0) xch[(lrow * H + h) * 2] = ss;
     __syncthreads();
@@ -433,16 +446,17 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
       if (p.rms_rstd_out) p.rms_rstd_out[row] = rstd2;
     }
   }
-  // the output replaces the residual rows in LDS (each lane rewrites what it read)
+  // the output goes to LDS, then back to HBM as whole rows
+  const float inv_rstd = 1.0f / rstd;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float v[4];
       if constexpr (NORM) {
-        const float x[4] = {bf16lo(xq[dt][r4][0]), bf16hi(xq[dt][r4][0]), bf16lo(xq[dt][r4][1]), bf16hi(xq[dt][r4][1])};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(o[dt][4 * r4 + e], rstd2, x[e]);  // + x (residual 2)
+        for (int e = 0; e < 4; ++e)  // + x (residual 2), x = ln / rstd + mu
+          v[e] = fmaf(o[dt][4 * r4 + e], rstd2, fmaf(xres[dt][r4][e], inv_rstd, mu));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * r4 + e] * inv;
