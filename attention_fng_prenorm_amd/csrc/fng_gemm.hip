@@ -51,6 +51,7 @@ struct GemmParams {
   int M, N, K;
   float eps;
   int tiles_m, tiles_n, total_tiles;
+  int n_off, n_end;  // this launch's output columns [n_off, n_end) (plain and lazy GEMM)
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
   uint32_t spin_limit;
 };
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       tn = r / gsize;
     }
     const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    const int n0 = p.n_off + tn * BN;
 
     // rows of X past M and K/N tails of W read as zero; X's range is capped
     // below kOOB so that kOOB offsets are always out of range
@@ -565,7 +566,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 
     // statistics outputs (one writer per row)
     if constexpr (EPI == EPI_PRENORM || EPI == EPI_FULLN || EPI == EPI_SPLITN) {
-      if (tn == 0 && wn == 0 && hi == 0) {
+      if (n0 == 0 && wn == 0 && hi == 0) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int m = row_of(i);
@@ -633,7 +634,7 @@ template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bo
 int launch(const GemmParams& p0, int grid, bool cooperative, hipStream_t stream) {
   GemmParams p = p0;
   p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;
+  p.tiles_n = (p.n_end - p.n_off + BN - 1) / BN;
   p.total_tiles = p.tiles_m * p.tiles_n;
   auto kern = gemm_kernel<BM, BN, BK, WAVES_M, WAVES_N, EPI, LN, GAMMA>;
   constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -674,6 +675,8 @@ GemmParams base_params(const GemmCall& c) {
   p.N = (int)c.N;
   p.K = (int)c.K;
   p.eps = c.eps;
+  p.n_off = 0;
+  p.n_end = p.N;
   p.group_m = 4;
   p.spin_limit = 1u << 22;
   return p;
@@ -683,6 +686,50 @@ GemmParams base_params(const GemmCall& c) {
 constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigWM = 2, kBigWN = 4;
 
 bool small_problem(const GemmCall& c) { return c.M * c.N <= 256LL * 256 * 64; }
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
+
+// The big tiles' last round often fills only part of the GPU (4096 x 14336 is
+// 896 tiles of 256 x 256 on 256 CUs: 3.5 rounds, the last one half empty).
+// Then the trailing column blocks run as a second launch of 256 x 128 tiles,
+// chosen so that the first launch is a whole number of rounds and the tail
+// has twice as many half-size tiles: 3 rounds + 1 round at half cost.
+// Returns the first tail column (N when no split pays off).
+int64_t tail_split_column(int64_t M, int64_t N) {
+  const int cus = device_cus();
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+  if (cus <= 0 || tn < 2 || (tm * tn) % cus == 0) return N;
+  // main column blocks: a multiple of the blocks per whole round of CUs
+  int64_t g = tm, c = cus;
+  while (c) { const int64_t t = g % c; g = c; c = t; }
+  const int64_t per_round = cus / g;  // column blocks whose tiles fill whole rounds
+  const int64_t nb_main = (tn / per_round) * per_round;
+  if (nb_main == 0 || nb_main == tn) return N;
+  // estimated time in units of one 256 x 256 tile per CU
+  const double single = (double)((tm * tn + cus - 1) / cus);
+  const double split = (double)(tm * nb_main / cus) + 0.5 * (double)((2 * tm * (tn - nb_main) + cus - 1) / cus);
+  return split + 0.25 < single ? nb_main * 256 : N;
+}
+
+template <int EPI, bool GAMMA>
+int launch_big(const GemmParams& p0, hipStream_t s) {
+  const int64_t ns = tail_split_column(p0.M, p0.N);
+  GemmParams p = p0;
+  p.n_end = (int)ns;
+  int st = launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI, false, GAMMA>(p, 0, false, s);
+  if (st != FNG_OK || ns >= p0.N) return st;
+  p.n_off = (int)ns;
+  p.n_end = p0.N;
+  return launch<kBigBM, 128, kBigBK, kBigWM, kBigWN, EPI, false, GAMMA>(p, 0, false, s);
+}
 
 }  // namespace
 
@@ -699,7 +746,7 @@ int launch_gemm(const GemmCall& c, hipStream_t s) {
   // so the unfused baseline is not handicapped by 256-wide tiles on N <= 128
   if (c.M >= 256 * 256 && c.N <= 64) return launch<256, 64, 64, 4, 2, EPI_PLAIN, false, false>(p, 0, false, s);
   if (c.M >= 256 * 256 && c.N <= 128) return launch<256, 128, 32, 2, 4, EPI_PLAIN, false, false>(p, 0, false, s);
-  return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PLAIN, false, false>(p, 0, false, s);
+  return launch_big<EPI_PLAIN, false>(p, s);
 }
 
 int launch_prenorm(const GemmCall& c, hipStream_t s) {
@@ -709,8 +756,7 @@ int launch_prenorm(const GemmCall& c, hipStream_t s) {
     return g ? launch<64, 64, 64, 2, 2, EPI_PRENORM, false, true>(p, 0, false, s)
              : launch<64, 64, 64, 2, 2, EPI_PRENORM, false, false>(p, 0, false, s);
   }
-  return g ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, true>(p, 0, false, s)
-           : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, false>(p, 0, false, s);
+  return g ? launch_big<EPI_PRENORM, true>(p, s) : launch_big<EPI_PRENORM, false>(p, s);
 }
 
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {

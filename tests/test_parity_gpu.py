@@ -77,6 +77,40 @@ def test_prenorm_full_size_sampled(gamma):
     assert_close_stats(r.cpu().numpy(), rall, "prenorm rstd (all rows)")
 
 
+@pytest.mark.parametrize("kind", ["gemm", "prenorm", "prenorm_gamma"])
+def test_big_tiles_with_tail_launch(kind):
+    # 16 x 56 tiles of 256 x 256 are 3.5 rounds of 256 CUs: the trailing 8 column
+    # blocks run as a second launch of 256 x 128 tiles (ragged here: N = 14200)
+    M, K, N = 4000, 264, 14200
+    spec, d = inputs.make_inputs("prenorm_rms_mlp_gamma" if kind == "prenorm_gamma" else "prenorm_rms_mlp",
+                                 M=M, K=K, N=N, seed=17)
+    X, W = dev(d["X"]), dev(d["W"])
+    g = dev(d["gamma"]) if kind == "prenorm_gamma" else None
+    guard = 2 * N
+    buf = empty_bf16(M * N + guard)
+    buf.view(torch.int16).fill_(0x1234)
+    Y = buf[: M * N].view(M, N)
+    r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"big tiles + tail {kind} {M}x{K}x{N}")
+    if kind == "gemm":
+        B.fng_gemm(X, W, Y)
+    else:
+        B.fng_prenorm_rms_gemm(X, W, Y, spec["eps"], gamma=g, rstd_out=r)
+    torch.cuda.synchronize()
+    assert bool((buf[M * N:].view(torch.int16) == 0x1234).all()), "write past the end of Y"
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, M - 1], np.random.default_rng(5).choice(M, 40, replace=False)]))
+    x = f64(d["X"][rows])
+    if kind == "gemm":
+        ref = oracle.gemm(x, f64(d["W"]))
+    else:
+        ref, _ = oracle.prenorm_rms_gemm(x, f64(d["W"]), spec["eps"], f64(d["gamma"]) if g is not None else None)
+        assert_close_stats(r.cpu().numpy(), oracle.rms_rstd(f64(d["X"]), spec["eps"]), "rstd (all rows)")
+    y = host(Y[torch.as_tensor(rows, device="cuda")])
+    assert_parity(y, ref, f"{kind} sampled rows")
+    # the tail columns on their own (the second launch)
+    assert_parity(y[:, 12288:], ref[:, 12288:], f"{kind} tail columns")
+
+
 def test_prenorm_deterministic_and_guarded():
     spec, d = inputs.make_inputs("prenorm_rms_mlp", M=520, K=256, N=2048)
     M, N, K = 520, 2048, 256
