@@ -11,6 +11,10 @@ from .fng_oracle import (  # noqa: F401
     gelu_tanh,
     flash_norm_attention,
     jagged_attention,
+    layernorm_backward_rows,
+    rmsnorm_backward_rows,
+    gemm_postnorm_backward,
+    prenorm_rms_backward_dx,
     prenorm_rms_gemm,
     rms_rstd,
     rmsnorm_rows,

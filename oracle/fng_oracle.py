@@ -44,6 +44,12 @@ Readings of points the page leaves open (each also listed in the design notes):
     the first residual adds the normalised query to the attention output, the
     RMSNorm runs across all heads, the second residual adds the raw query.
     Query rows are jagged (per-batch lengths given by offsets), keys dense.
+  * backward (section 3's fusion regrouping): the norm's input gradient is
+    the textbook closed form of the derivative of LayerNorm / RMSNorm (no
+    affine), applied row-wise to the upstream gradient, which is the product
+    of the next layer's output gradient with that layer's weight; the
+    normalized values come from the forward (the norm's output, or for the
+    lazy pre-norm rebuilt as x * rstd from its input and statistic).
 """
 
 import numpy as np
@@ -137,6 +143,60 @@ def gemm_postnorm(x, w, eps, kind):
         y, r = rmsnorm_rows(z, eps)
         return y, None, r
     raise ValueError(f"unknown norm kind {kind!r}")
+
+
+# ---------------------------------------------------------------------------
+# backward by fusion regrouping (section 3, "What about backward?")
+# ---------------------------------------------------------------------------
+
+def layernorm_backward_rows(g, xhat, rstd):
+    """Gradient of LayerNorm (no affine, biased variance) with respect to its
+    input, per row of the last axis, from the upstream gradient g, the
+    normalized values xhat = (z - mean) * rstd and rstd:
+        dz = rstd * (g - mean(g) - xhat * mean(g * xhat)).
+    (Differentiate y = (z - mu) * rstd with mu and rstd functions of z.)
+    """
+    g = np.asarray(g, dtype=np.float64)
+    xhat = np.asarray(xhat, dtype=np.float64)
+    r = np.asarray(rstd, dtype=np.float64)[..., None]
+    return r * (g - np.mean(g, axis=-1, keepdims=True) - xhat * np.mean(g * xhat, axis=-1, keepdims=True))
+
+
+def rmsnorm_backward_rows(g, xhat, rstd):
+    """Gradient of RMSNorm (no gain) with respect to its input, per row:
+        dz = rstd * (g - xhat * mean(g * xhat)),  xhat = z * rstd.
+    """
+    g = np.asarray(g, dtype=np.float64)
+    xhat = np.asarray(xhat, dtype=np.float64)
+    r = np.asarray(rstd, dtype=np.float64)[..., None]
+    return r * (g - xhat * np.mean(g * xhat, axis=-1, keepdims=True))
+
+
+def gemm_postnorm_backward(dy2, w, y, rstd, kind):
+    """The post-norm backward as the page regroups it: the norm's upstream
+    gradient is the product of the next layer's output gradient dy2 [M, K]
+    with that layer's weight read as w [K, N], and the norm backward (over the
+    N axis) is that product's epilogue.  y [M, N] is the forward output of the
+    norm (the normalized values), rstd [M] its forward statistic.
+    Returns dz [M, N], the gradient at the norm's input.
+    """
+    g = gemm(dy2, w)
+    if kind == "ln":
+        return layernorm_backward_rows(g, y, rstd)
+    if kind == "rms":
+        return rmsnorm_backward_rows(g, y, rstd)
+    raise ValueError(kind)
+
+
+def prenorm_rms_backward_dx(dy, w, x, rstd):
+    """Input gradient of the lazy pre-RMSNorm GEMM y = rmsnorm(x) @ W: the
+    gradient at rmsnorm's output is dy @ W^T (w [N, K] is W^T read row-major:
+    w = W.T), then the RMSNorm backward with xhat rebuilt from x and the
+    forward rstd.  Returns dx [M, K].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(rstd, dtype=np.float64)
+    return rmsnorm_backward_rows(gemm(dy, w), x * r[..., None], r)
 
 
 # ---------------------------------------------------------------------------

@@ -550,6 +550,113 @@ def check_jagged_attention(O):
     assert np.all(O.jagged_attention(q, off, k, np.zeros_like(v), 0.45, "gelu") == 0.0)
 
 
+# ---------------------------------------------------------------------------
+# backward (fusion regrouping)
+# ---------------------------------------------------------------------------
+
+def _bwd_case(seed, M=5, N=7, shift=0.4):
+    rng = _rng(seed)
+    z = rng.standard_normal((M, N)) * (1.0 + np.arange(M)[:, None]) + shift
+    g = rng.standard_normal((M, N))
+    return z, g
+
+
+def check_norm_backward_torch(O):
+    import torch
+    import torch.nn.functional as F
+    z, g = _bwd_case(71, 6, 40)
+    for kind in ("ln", "rms"):
+        zt = torch.from_numpy(z.copy()).requires_grad_(True)
+        if kind == "ln":
+            F.layer_norm(zt, (40,), eps=1e-5).backward(torch.from_numpy(g))
+            y, _, r = O.layernorm_rows(z, 1e-5)
+            dz = O.layernorm_backward_rows(g, y, r)
+        else:
+            F.rms_norm(zt, (40,), eps=1e-6).backward(torch.from_numpy(g))
+            y, r = O.rmsnorm_rows(z, 1e-6)
+            dz = O.rmsnorm_backward_rows(g, y, r)
+        _close(dz, zt.grad.numpy(), 1e-12, f"{kind} backward vs torch autograd fp64")
+
+
+def check_norm_backward_finite_differences(O):
+    # central differences of L(z) = sum(g * norm(z)) with the brute-force forward
+    z, g = _bwd_case(72, 2, 5)
+    h = 1e-6
+    for kind in ("ln", "rms"):
+        fwd = (lambda rows: bf_layernorm(rows, 1e-5)[0]) if kind == "ln" else (lambda rows: bf_rmsnorm(rows, 1e-6)[0])
+        if kind == "ln":
+            y, _, r = O.layernorm_rows(z, 1e-5)
+            dz = O.layernorm_backward_rows(g, y, r)
+        else:
+            y, r = O.rmsnorm_rows(z, 1e-6)
+            dz = O.rmsnorm_backward_rows(g, y, r)
+        for m in range(2):
+            for k in range(5):
+                zp = z[m].tolist(); zm = z[m].tolist()
+                zp[k] += h; zm[k] -= h
+                lp = sum(a * b for a, b in zip(g[m], fwd([zp])[0]))
+                lm = sum(a * b for a, b in zip(g[m], fwd([zm])[0]))
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - dz[m, k]) <= 1e-7 * (1 + abs(fd)), (kind, m, k, fd, dz[m, k])
+
+
+def check_norm_backward_invariants(O):
+    z, g = _bwd_case(73, 4, 9)
+    # eps = 0: the gradient is orthogonal to xhat (norm(a z) = norm(z)); LN's
+    # also sums to zero (norm(z + c) = norm(z))
+    y, _, r = O.layernorm_rows(z, 0.0)
+    dz = O.layernorm_backward_rows(g, y, r)
+    _close(np.sum(dz, axis=1), np.zeros(4), 1e-12, "LN backward sums to zero")
+    _close(np.sum(dz * y, axis=1), np.zeros(4), 1e-12, "LN backward orthogonal to xhat")
+    # a constant upstream gradient has no effect through LN; through RMS it does
+    _close(O.layernorm_backward_rows(np.ones_like(z), y, r), np.zeros_like(z), 1e-12, "LN: constant g")
+    yr, rr = O.rmsnorm_rows(z, 0.0)
+    dr = O.rmsnorm_backward_rows(g, yr, rr)
+    _close(np.sum(dr * yr, axis=1), np.zeros(4), 1e-12, "RMS backward orthogonal to xhat")
+    assert np.max(np.abs(O.rmsnorm_backward_rows(np.ones_like(z), yr, rr))) > 1e-3
+    # g along xhat: no gradient (eps = 0)
+    _close(O.layernorm_backward_rows(3.0 * y, y, r), np.zeros_like(z), 1e-12, "LN: g = 3 xhat")
+    _close(O.rmsnorm_backward_rows(-2.0 * yr, yr, rr), np.zeros_like(z), 1e-12, "RMS: g = -2 xhat")
+    # scaling z by a scales dz by 1/a
+    y2, _, r2 = O.layernorm_rows(2.5 * z, 0.0)
+    _close(O.layernorm_backward_rows(g, y2, r2), dz / 2.5, 1e-12, "LN backward scaling")
+
+
+def check_gemm_postnorm_backward_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(74)
+    M, N, K2 = 9, 24, 11
+    z = rng.standard_normal((M, N)) * 2.0 + 0.5
+    W2 = rng.standard_normal((N, K2)) / 4.0      # next layer: out = y @ W2
+    dy2 = rng.standard_normal((M, K2))
+    for kind in ("ln", "rms"):
+        zt = torch.from_numpy(z.copy()).requires_grad_(True)
+        yt = F.layer_norm(zt, (N,), eps=1e-5) if kind == "ln" else F.rms_norm(zt, (N,), eps=1e-6)
+        (yt @ torch.from_numpy(W2)).backward(torch.from_numpy(dy2))
+        if kind == "ln":
+            y, _, r = O.layernorm_rows(z, 1e-5)
+        else:
+            y, r = O.rmsnorm_rows(z, 1e-6)
+        dz = O.gemm_postnorm_backward(dy2, W2.T.copy(), y, r, kind)
+        _close(dz, zt.grad.numpy(), 1e-12, f"post-{kind} backward (regrouped) vs autograd")
+
+
+def check_prenorm_backward_torch(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(75)
+    M, K, N = 7, 20, 13
+    x = rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))
+    W = rng.standard_normal((K, N)) / 4.0
+    dy = rng.standard_normal((M, N))
+    xt = torch.from_numpy(x.copy()).requires_grad_(True)
+    (F.rms_norm(xt, (K,), eps=1e-6) @ torch.from_numpy(W)).backward(torch.from_numpy(dy))
+    r = O.rms_rstd(x, 1e-6)
+    _close(O.prenorm_rms_backward_dx(dy, W.T.copy(), x, r), xt.grad.numpy(), 1e-12,
+           "lazy pre-RMS dx vs autograd")
+
+
 def check_compare(O):
     e = O.compare(np.array([1.0, 2.0]), np.array([1.0, 3.0]))
     assert abs(e["normwise_rel"] - 1.0 / 3.0) < 1e-15, e
@@ -581,6 +688,11 @@ ALL_CHECKS = [
     check_fna_torch,
     check_fna_closed_forms,
     check_jagged_attention,
+    check_norm_backward_torch,
+    check_norm_backward_finite_differences,
+    check_norm_backward_invariants,
+    check_gemm_postnorm_backward_torch,
+    check_prenorm_backward_torch,
     check_compare,
 ]
 

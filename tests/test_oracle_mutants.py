@@ -53,9 +53,19 @@ def _ns(**over):
     def jagged_attention(q, offsets, k, v, sm_scale, act):
         return _jagged(ns, q, offsets, k, v, sm_scale, act)
 
+    def gemm_postnorm_backward(dy2, w, y, rstd, kind):
+        g = ns.gemm(dy2, w)
+        return (ns.layernorm_backward_rows if kind == "ln" else ns.rmsnorm_backward_rows)(g, y, rstd)
+
+    def prenorm_rms_backward_dx(dy, w, x, rstd):
+        r = np.asarray(rstd, dtype=np.float64)
+        return ns.rmsnorm_backward_rows(ns.gemm(dy, w), np.asarray(x, dtype=np.float64) * r[..., None], r)
+
     for name, fn in (("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
                      ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
-                     ("jagged_attention", jagged_attention)):
+                     ("jagged_attention", jagged_attention),
+                     ("gemm_postnorm_backward", gemm_postnorm_backward),
+                     ("prenorm_rms_backward_dx", prenorm_rms_backward_dx)):
         if name not in over:
             setattr(ns, name, fn)
     return ns
@@ -235,6 +245,29 @@ def _attn_no_out_norm(q, k, v, eps_ln, eps_rms, sm_scale):
     return out, z, z, z
 
 
+def _ln_bwd_no_mean(g, xhat, rstd):
+    g = np.asarray(g, dtype=np.float64); xhat = np.asarray(xhat, dtype=np.float64)
+    return np.asarray(rstd)[..., None] * (g - xhat * np.mean(g * xhat, axis=-1, keepdims=True))
+
+
+def _ln_bwd_sign(g, xhat, rstd):
+    g = np.asarray(g, dtype=np.float64); xhat = np.asarray(xhat, dtype=np.float64)
+    return np.asarray(rstd)[..., None] * (g - np.mean(g, axis=-1, keepdims=True) + xhat * np.mean(g * xhat, axis=-1, keepdims=True))
+
+
+def _rms_bwd_with_mean(g, xhat, rstd):
+    return F.layernorm_backward_rows(g, xhat, rstd)
+
+
+def _rms_bwd_no_rstd(g, xhat, rstd):
+    g = np.asarray(g, dtype=np.float64); xhat = np.asarray(xhat, dtype=np.float64)
+    return g - xhat * np.mean(g * xhat, axis=-1, keepdims=True)
+
+
+def _prenorm_dx_raw_xhat(dy, w, x, rstd):
+    return F.rmsnorm_backward_rows(F.gemm(dy, w), x, rstd)
+
+
 MUTANTS = {
     "rms_eps_outside_sqrt": dict(rmsnorm_rows=_rms_eps_outside),
     "rms_divides_by_n_minus_1": dict(rmsnorm_rows=_rms_sum_not_mean),
@@ -259,6 +292,11 @@ MUTANTS = {
     "fna_missing_residual_2": dict(flash_norm_attention=_fna_mutant(res2=None)),
     "fna_residual_2_adds_ln_q": dict(flash_norm_attention=_fna_mutant(res2="ln")),
     "gelu_cubic_constant_x10": dict(gelu_tanh=_gelu_wrong_constant),
+    "ln_backward_drops_mean_term": dict(layernorm_backward_rows=_ln_bwd_no_mean),
+    "ln_backward_wrong_sign": dict(layernorm_backward_rows=_ln_bwd_sign),
+    "rms_backward_subtracts_mean": dict(rmsnorm_backward_rows=_rms_bwd_with_mean),
+    "rms_backward_missing_rstd": dict(rmsnorm_backward_rows=_rms_bwd_no_rstd),
+    "prenorm_dx_xhat_not_rebuilt": dict(prenorm_rms_backward_dx=_prenorm_dx_raw_xhat),
     "jagged_kv_of_next_batch": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
         oracle, q, o, k, v, s, a, kv_batch_shift=1)),
     "jagged_scale_after_activation": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
