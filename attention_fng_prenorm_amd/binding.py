@@ -51,6 +51,11 @@ SIGNATURES = {
     "fng_layernorm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp]),
     "fng_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fng_attention": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _vp]),
+    "fng_gemm_postnorm_ln_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
+    "fng_gemm_postnorm_rms_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
+    "fng_prenorm_rms_bwd_dx": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
+    "fng_layernorm_bwd": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
+    "fng_rmsnorm_bwd": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp]),
     "fng_flash_norm_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                         _i64, _i64, _i64, _f32, _f32, _f32, _int, _vp]),
     "fng_jagged_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -220,6 +225,53 @@ def fng_attention(Q, K, V, out, sm_scale=0.0, stream=None):
     _check("fng_attention", lib().fng_attention(
         _bf(Q, "Q"), _bf(K, "K"), _bf(V, "V"), _bf(out, "out"), B, Sq, Skv, H, D, sm_scale,
         _stream(stream)))
+
+
+def _bwd(fn, G, Wt, H, rstd, dZ, workspace, path, stream, sizes):
+    wp, wb = _ws(workspace)
+    _check(fn, getattr(lib(), fn)(_bf(G, "G"), _bf(Wt, "Wt"), _bf(H, "saved tensor"), _f(rstd, "rstd"),
+                                  _bf(dZ, "output"), *sizes, wp, wb, path, _stream(stream)))
+
+
+def fng_gemm_postnorm_ln_bwd(G, Wt, Y, rstd, dZ, workspace=None, path=FNG_PATH_AUTO, stream=None):
+    M, K = G.shape
+    N = Wt.shape[1]
+    if Wt.shape[0] != K or tuple(Y.shape) != (M, N) or tuple(dZ.shape) != (M, N) or tuple(rstd.shape) != (M,):
+        raise ValueError("shapes: G [M,K], Wt [K,N], Y/dZ [M,N], rstd [M]")
+    _bwd("fng_gemm_postnorm_ln_bwd", G, Wt, Y, rstd, dZ, workspace, path, stream, (M, N, K))
+
+
+def fng_gemm_postnorm_rms_bwd(G, Wt, Y, rstd, dZ, workspace=None, path=FNG_PATH_AUTO, stream=None):
+    M, K = G.shape
+    N = Wt.shape[1]
+    if Wt.shape[0] != K or tuple(Y.shape) != (M, N) or tuple(dZ.shape) != (M, N) or tuple(rstd.shape) != (M,):
+        raise ValueError("shapes: G [M,K], Wt [K,N], Y/dZ [M,N], rstd [M]")
+    _bwd("fng_gemm_postnorm_rms_bwd", G, Wt, Y, rstd, dZ, workspace, path, stream, (M, N, K))
+
+
+def fng_prenorm_rms_bwd_dx(dY, Wt, X, rstd, dX, workspace=None, path=FNG_PATH_AUTO, stream=None):
+    M, N = dY.shape
+    K = Wt.shape[1]
+    if Wt.shape[0] != N or tuple(X.shape) != (M, K) or tuple(dX.shape) != (M, K) or tuple(rstd.shape) != (M,):
+        raise ValueError("shapes: dY [M,N], Wt [N,K], X/dX [M,K], rstd [M]")
+    _bwd("fng_prenorm_rms_bwd_dx", dY, Wt, X, rstd, dX, workspace, path, stream, (M, N, K))
+
+
+def fng_layernorm_bwd(G, Y, rstd, dZ, stream=None):
+    M, N = G.shape
+    if tuple(Y.shape) != (M, N) or tuple(dZ.shape) != (M, N):
+        raise ValueError("G, Y, dZ must share one shape")
+    _check("fng_layernorm_bwd", lib().fng_layernorm_bwd(_bf(G, "G"), _bf(Y, "Y"), _f(rstd, "rstd"),
+                                                        _bf(dZ, "dZ"), M, N, _stream(stream)))
+
+
+def fng_rmsnorm_bwd(G, H, rstd, dZ, h_is_input=False, stream=None):
+    M, N = G.shape
+    if tuple(H.shape) != (M, N) or tuple(dZ.shape) != (M, N):
+        raise ValueError("G, H, dZ must share one shape")
+    _check("fng_rmsnorm_bwd", lib().fng_rmsnorm_bwd(_bf(G, "G"), _bf(H, "H"), _f(rstd, "rstd"),
+                                                    _bf(dZ, "dZ"), M, N, int(bool(h_is_input)),
+                                                    _stream(stream)))
 
 
 def _act(act):

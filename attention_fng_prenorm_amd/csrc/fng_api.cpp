@@ -195,6 +195,81 @@ FNG_EXPORT int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, floa
   return postnorm(false, X, W, Y, nullptr, rstd_out, M, N, K, eps, workspace, workspace_bytes, path, stream);
 }
 
+namespace {
+
+// dZ = norm_backward(G @ Wt) over rows of length N; xhat = H (h_raw: H * rstd)
+int norm_bwd(bool ln, const void* G, const void* Wt, const void* H, const float* rstd, bool h_raw, void* dZ,
+             int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, int path, void* stream) {
+  int st = check_gemm(G, Wt, dZ, M, N, K, 1.f, false);
+  if (st != FNG_OK) return st;
+  if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
+  if (m_or_n_empty(M, N)) return FNG_OK;
+  if (!H || !rstd) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(H) || reinterpret_cast<uintptr_t>(rstd) % 4 != 0) return FNG_ERR_MISALIGNED;
+  if (M * N * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;  // the saved tensor's 32-bit copy offsets
+  if (path == FNG_PATH_TWOPASS) return FNG_ERR_UNSUPPORTED;        // the backward has no two-pass path
+  path = resolve_path(path, M, N, K);
+  if (path == FNG_PATH_TWOPASS) return FNG_ERR_UNSUPPORTED;
+  GemmCall c{G, Wt, nullptr, dZ, nullptr, nullptr, M, N, K, 1.f, nullptr, nullptr, nullptr, nullptr};
+  const fng::NormBwdArgs b{H, rstd, h_raw};
+  if (path == FNG_PATH_FULLN) {
+    if (N > fng::fulln_max_n()) return FNG_ERR_UNSUPPORTED;
+    return fng::launch_norm_bwd_fulln(c, b, ln, as_stream(stream));
+  }
+  const size_t need = fng_gemm_postnorm_workspace_bytes(M, N, K, FNG_PATH_SPLITN);
+  if (!workspace || workspace_bytes < need) return FNG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
+  Workspace w = layout(workspace, M, N);
+  c.part = w.part;
+  c.cnt = w.cnt;
+  c.done = w.done;
+  c.status = w.status;
+  if (!fng::splitn_feasible(M, N)) return FNG_ERR_UNSUPPORTED;
+  return fng::launch_norm_bwd_splitn(c, b, ln, as_stream(stream));
+}
+
+int row_bwd(bool ln, const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N, bool h_raw,
+            void* stream) {
+  if (M < 0 || N < 1) return FNG_ERR_INVALID_ARG;
+  if (M == 0) return FNG_OK;
+  if (!G || !H || !rstd || !dZ) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(G) || !aligned16(H) || !aligned16(dZ) || reinterpret_cast<uintptr_t>(rstd) % 4 != 0 || N % 8 != 0)
+    return FNG_ERR_MISALIGNED;
+  if (N > INT32_MAX / 4 || M > INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  return fng::launch_rownorm_bwd(G, H, rstd, dZ, M, N, h_raw, ln, as_stream(stream));
+}
+
+}  // namespace
+
+FNG_EXPORT int fng_gemm_postnorm_ln_bwd(const void* G, const void* Wt, const void* Y, const float* rstd, void* dZ,
+                                        int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                        int path, void* stream) {
+  return norm_bwd(true, G, Wt, Y, rstd, false, dZ, M, N, K, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_gemm_postnorm_rms_bwd(const void* G, const void* Wt, const void* Y, const float* rstd, void* dZ,
+                                         int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                         int path, void* stream) {
+  return norm_bwd(false, G, Wt, Y, rstd, false, dZ, M, N, K, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_prenorm_rms_bwd_dx(const void* dY, const void* Wt, const void* X, const float* rstd, void* dX,
+                                      int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                      int path, void* stream) {
+  // the product dY [M, N] @ Wt [N, K] has K columns: the norm axis
+  return norm_bwd(false, dY, Wt, X, rstd, true, dX, M, K, N, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_layernorm_bwd(const void* G, const void* Y, const float* rstd, void* dZ, int64_t M, int64_t N,
+                                 void* stream) {
+  return row_bwd(true, G, Y, rstd, dZ, M, N, false, stream);
+}
+
+FNG_EXPORT int fng_rmsnorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N,
+                               int h_is_input, void* stream) {
+  return row_bwd(false, G, H, rstd, dZ, M, N, h_is_input != 0, stream);
+}
+
 FNG_EXPORT int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || workspace_bytes < 256) return FNG_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;

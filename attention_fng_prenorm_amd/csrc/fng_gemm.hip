@@ -35,7 +35,11 @@
 
 namespace fng {
 
-enum : int { EPI_PLAIN = 0, EPI_PRENORM = 1, EPI_FULLN = 2, EPI_SPLITN = 3, EPI_PARTIAL = 4 };
+enum : int {
+  EPI_PLAIN = 0, EPI_PRENORM = 1, EPI_FULLN = 2, EPI_SPLITN = 3, EPI_PARTIAL = 4,
+  EPI_BWD_FULLN = 5,   // norm backward over whole rows held by one workgroup
+  EPI_BWD_SPLITN = 6   // norm backward, row sums exchanged like EPI_SPLITN
+};
 
 struct GemmParams {
   const uint16_t* X;
@@ -52,6 +56,9 @@ struct GemmParams {
   float eps;
   int tiles_m, tiles_n, total_tiles;
   int n_off, n_end;  // this launch's output columns [n_off, n_end) (plain and lazy GEMM)
+  const uint16_t* H;     // norm backward: xhat [M, N], or the norm's input when h_raw
+  const float* rstd_in;  // norm backward: the forward rstd [M]
+  int h_raw;
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
   uint32_t spin_limit;
 };
@@ -121,7 +128,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   static_assert(S::BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES == 4, "the ring below is written out for 4 stages");
 
-  __shared__ __attribute__((aligned(1024))) char smem[S::BYTES];
+  // the norm backward stages the saved [BM, BN] tile over the whole ring and
+  // keeps its row reductions in an extra region after it
+  constexpr bool IS_BWD = EPI == EPI_BWD_FULLN || EPI == EPI_BWD_SPLITN;
+  constexpr bool IS_SPLIT = EPI == EPI_SPLITN || EPI == EPI_BWD_SPLITN;
+  constexpr int RED = IS_BWD ? S::BYTES : 0;
+  constexpr int EXTRA = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
+  static_assert(S::BYTES + EXTRA <= 160 * 1024, "LDS budget with the backward's reductions");
+  __shared__ __attribute__((aligned(1024))) char smem[S::BYTES + EXTRA];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   const uint32_t slot = xcd_remap(blockIdx.x, G);
   for (int t = (int)slot; t < p.total_tiles; t += (int)G) {
     int tm, tn;
-    if constexpr (EPI == EPI_SPLITN) {
+    if constexpr (IS_SPLIT) {
       tm = t / p.tiles_n;
       tn = t % p.tiles_n;
     } else {
@@ -375,10 +389,44 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       }
     }
 
-    if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN || EPI == EPI_PARTIAL) {
+    // norm backward: the saved tile (xhat or the norm's input) goes to LDS in
+    // the output staging layout below, the forward rstd to registers
+    float bw_r[FM], bw_hs[FM];
+    if constexpr (IS_BWD) {
+      constexpr int HB = BM * BN * 2 / 1024 / NWAVES;  // 1 KB copies per wave
+      static_assert(HB * NWAVES * 1024 == BM * BN * 2, "saved tile split evenly over the waves");
+      constexpr int NCH = BN / 8;
+      const i32x4_t hr = dma_rsrc(p.H, (uint32_t)((int64_t)M * N * 2));
+#pragma unroll
+      for (int i = 0; i < HB; ++i) {
+        const int blk = wave * HB + i;
+        const int idx = blk * 1024 + lane * 16;
+        const int row = idx / (BN * 2), pc = (idx % (BN * 2)) / 16;
+        const int ch = (pc ^ row) & (NCH - 1);
+        dma16(hr, lds + blk * 1024, (uint32_t)(((int64_t)(m0 + row) * N + n0 + ch * 8) * 2));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = row_of(i);
+        bw_r[i] = m < M ? p.rstd_in[m] : 1.f;
+        bw_hs[i] = p.h_raw ? bw_r[i] : 1.f;
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    // 8 B of the staged tile at this lane's (row slot i, columns col_of(j, r4) ..)
+    auto stage_addr = [&](int i, int j, int r4) __attribute__((always_inline)) {
+      constexpr int NCH = BN / 8;
+      const int row = lrow(i);
+      const int ch = (wn * WN + 32 * j + 8 * r4) / 8;
+      return lds + row * (BN * 2) + ((ch ^ row) & (NCH - 1)) * 16 + hi * 8;
+    };
+
+    if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN || EPI == EPI_PARTIAL || IS_BWD) {
       // per-row statistics of this tile's valid columns, fp32 accumulators
-      // red: [WAVES_N][BM] floats in LDS (the stage buffers are free now)
-      FNG_LDS float* red = (FNG_LDS float*)lds;
+      // red: [WAVES_N][BM] floats in LDS (the stage buffers are free now, or
+      // hold the backward's saved tile: then the extra region)
+      FNG_LDS float* red = (FNG_LDS float*)(lds + RED);
       const int nvalid = min(BN, N - n0);
       auto row_reduce = [&](float (&v)[FM], float (&out)[FM]) {
 #pragma unroll
@@ -397,7 +445,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         __syncthreads();
       };
       float part[FM], s1[FM], s2[FM];
-      if constexpr (LN) {
+      if constexpr (IS_BWD) {
+        // s1 = sum of g (LayerNorm), s2 = sum of g * xhat over the tile's columns
+        float p1[FM], p2[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              if (col_of(j, r4) < N) {
+                const u32x2_t hv = *reinterpret_cast<const FNG_LDS u32x2_t*>(stage_addr(i, j, r4));
+                const float x[4] = {bf16lo(hv[0]), bf16hi(hv[0]), bf16lo(hv[1]), bf16hi(hv[1])};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float gv = acc[i][j][4 * r4 + e];
+                  if constexpr (LN) a1 += gv;
+                  a2 = fmaf(gv, x[e] * bw_hs[i], a2);
+                }
+              }
+          p1[i] = a1;
+          p2[i] = a2;
+        }
+        if constexpr (LN) row_reduce(p1, s1);
+        else {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) s1[i] = 0.f;
+        }
+        row_reduce(p2, s2);
+      } else if constexpr (LN) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           float s = 0.f;
@@ -457,6 +534,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           rs_mean[i] = s1[i];
           rs_rstd[i] = __builtin_amdgcn_rsqf(s2[i] / (float)N + p.eps);
         }
+      } else if constexpr (EPI == EPI_BWD_FULLN) {
+        // backward: rs_mean = mean(g), rs_rstd = mean(g * xhat)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          rs_mean[i] = s1[i] / (float)N;
+          rs_rstd[i] = s2[i] / (float)N;
+        }
       } else {
         // publish partials: part[tm][tn][row][2]
         if constexpr (EPI == EPI_PARTIAL) {
@@ -468,7 +552,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const int row = lrow(i);
-            if constexpr (EPI == EPI_SPLITN) {
+            if constexpr (IS_SPLIT) {
               // device-scope stores: written through to the device-coherent
               // level, visible to every XCD without a cache-wide write-back
               __hip_atomic_store(pp + row * 2 + 0, s1[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -479,7 +563,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
             }
           }
         }
-        if constexpr (EPI == EPI_SPLITN) {
+        if constexpr (IS_SPLIT) {
           // Exchange (section 3's multi-CTA reduction, without clusters).
           // Every access to the exchanged data is a device-scope atomic, which
           // the hardware performs at the device-coherent level (past the
@@ -491,7 +575,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           //    device-scope loads, issued only once the poll has returned.
           wait_vmcnt<0>();
           __syncthreads();
-          FNG_LDS float* stats = (FNG_LDS float*)lds;  // [BM][2]: mean, rstd
+          FNG_LDS float* stats = (FNG_LDS float*)(lds + RED);  // [BM][2]: mean, rstd
           if (tid == 0) {
             __hip_atomic_fetch_add(p.cnt + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t target = (uint32_t)p.tiles_n;
@@ -520,7 +604,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
             float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
             const int nt = p.tiles_n;
             constexpr int BATCH = 16;
-            float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f;
+            float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f, gsum = 0.f;
             for (int q0 = 0; q0 < nt; q0 += BATCH) {
               float mb[BATCH], vb[BATCH];
 #pragma unroll
@@ -533,7 +617,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
               for (int u = 0; u < BATCH; ++u) {
                 if (q0 + u >= nt) break;
-                if constexpr (LN) {
+                if constexpr (IS_BWD) {
+                  // backward: plain sums of g and g * xhat, fixed order
+                  if constexpr (LN) gsum += mb[u];
+                  ssum += vb[u];
+                } else if constexpr (LN) {
                   // Chan et al. pairwise merge of (count, mean, M2)
                   const float nb = (float)min(BN, N - (q0 + u) * BN);
                   const float tot = cn + nb;
@@ -546,7 +634,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
                 }
               }
             }
-            if constexpr (LN) {
+            if constexpr (IS_BWD) {
+              stats[tid * 2 + 0] = gsum / (float)N;
+              stats[tid * 2 + 1] = ssum / (float)N;
+            } else if constexpr (LN) {
               stats[tid * 2 + 0] = mean;
               stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
             } else {
@@ -596,9 +687,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             float v[4];
+            float xh[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (IS_BWD) {  // this lane's staged xhat, about to be overwritten
+              const u32x2_t hv = *reinterpret_cast<const FNG_LDS u32x2_t*>(stage_addr(i, j, r4));
+              xh[0] = bf16lo(hv[0]) * bw_hs[i];
+              xh[1] = bf16hi(hv[0]) * bw_hs[i];
+              xh[2] = bf16lo(hv[1]) * bw_hs[i];
+              xh[3] = bf16hi(hv[1]) * bw_hs[i];
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float a = acc[i][j][4 * r4 + e];
+              // dz = rstd (g - mean(g) - xhat mean(g xhat))
+              if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
               if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
               if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
               // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
@@ -805,6 +906,52 @@ int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
   if (grid > total) grid = total;
   return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>(p, grid, true, s)
             : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>(p, grid, true, s);
+}
+
+// norm backward by regrouping: dZ = norm_bwd(G @ Wt), whole rows per
+// workgroup (the forward full-N tiles) or split-N with the exchange
+int launch_norm_bwd_fulln(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s) {
+  GemmParams p = base_params(c);
+  p.H = static_cast<const uint16_t*>(b.H);
+  p.rstd_in = b.rstd;
+  p.h_raw = b.h_raw ? 1 : 0;
+  const bool tall = c.M >= 256 * 256;
+  // (the forward's 256 x 64 tile with BK 64 fills all 160 KB of LDS; the
+  // backward needs room for its row reductions)
+  if (tall && c.N <= 64)
+    return ln ? launch<256, 64, 32, 2, 2, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+              : launch<256, 64, 32, 2, 2, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+  if (tall && c.N <= 128)
+    return ln ? launch<256, 128, 32, 2, 4, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+              : launch<256, 128, 32, 2, 4, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+  if (tall && c.N <= 256)
+    return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+              : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+  if (c.N <= 256)
+    return ln ? launch<32, 256, 64, 1, 4, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+              : launch<32, 256, 64, 1, 4, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+  return ln ? launch<64, 512, 32, 1, 4, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+            : launch<64, 512, 32, 1, 4, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+}
+
+int launch_norm_bwd_splitn(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s) {
+  GemmParams p = base_params(c);
+  p.H = static_cast<const uint16_t*>(b.H);
+  p.rstd_in = b.rstd;
+  p.h_raw = b.h_raw ? 1 : 0;
+  p.part = static_cast<float*>(c.part);
+  p.cnt = c.cnt;
+  p.done = c.done;
+  p.status = c.status;
+  const int cap = ln ? max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, true, false>()
+                     : max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, false, false>();
+  const int tn = (int)splitn_tiles_n(c.N);
+  const int total = (int)(splitn_tiles_m(c.M) * tn);
+  if (cap <= 0 || tn > cap) return FNG_ERR_UNSUPPORTED;
+  int grid = (cap / tn) * tn;
+  if (grid > total) grid = total;
+  return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, true, false>(p, grid, true, s)
+            : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, false, false>(p, grid, true, s);
 }
 
 int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s) {

@@ -30,6 +30,15 @@ int launch_prenorm(const GemmCall& c, hipStream_t s);
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s);
+// norm backward epilogue inputs: H = xhat [M, N] (or the norm's input when
+// h_raw, xhat = H * rstd), rstd [M] from the forward
+struct NormBwdArgs {
+  const void* H;
+  const float* rstd;
+  bool h_raw;
+};
+int launch_norm_bwd_fulln(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s);
+int launch_norm_bwd_splitn(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s);
 int splitn_feasible(int64_t M, int64_t N);
 int64_t splitn_tiles_m(int64_t M);
 int64_t splitn_tiles_n(int64_t N);
@@ -37,6 +46,8 @@ int64_t splitn_bm();
 int64_t fulln_max_n();
 
 // fng_norm.hip
+int launch_rownorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N,
+                       bool h_raw, bool ln, hipStream_t s);
 int launch_rownorm(const void* X, const void* gamma, void* Y, float* mean_out, float* rstd_out,
                    int64_t M, int64_t N, float eps, bool ln, hipStream_t s);
 // second pass of the two-pass post-norm: merge per-tile partials, normalize Y in place

@@ -197,6 +197,152 @@ int launch_rownorm(const void* X, const void* gamma, void* Y, float* mean_out, f
 }
 
 // ---------------------------------------------------------------------------
+// Standalone norm backward (the unfused baseline of the regrouped backward):
+// per row, from the upstream gradient g, the normalized values xhat (the
+// forward output, or x * rstd from the norm's input) and the forward rstd,
+//   LayerNorm: dz = rstd (g - mean(g) - xhat mean(g xhat))
+//   RMSNorm:   dz = rstd (g - xhat mean(g xhat)).
+// Same row ownership as the forward kernel; both rows are held in registers.
+// ---------------------------------------------------------------------------
+struct RowBwdParams {
+  const uint16_t* G;
+  const uint16_t* H;   // xhat, or the norm's input when h_raw
+  const float* rstd;
+  uint16_t* dZ;
+  int64_t M;
+  int N;
+  int h_raw;
+};
+
+template <int LPR, int CPL, bool LN>
+__global__ __launch_bounds__(256) void rownorm_bwd_kernel(RowBwdParams p) {
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const bool valid = row < p.M;
+  const int N = p.N;
+  const uint32_t bytes = valid ? (uint32_t)N * 2u : 0u;
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(p.G + (valid ? row : 0) * (int64_t)N, bytes);
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(p.H + (valid ? row : 0) * (int64_t)N, bytes);
+  u32x4_t gv[CPL], hv[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    gv[c] = buffer_load16(gr, (uint32_t)((c * LPR + sub) * 16));
+    hv[c] = buffer_load16(hr, (uint32_t)((c * LPR + sub) * 16));
+  }
+  const float r = valid ? p.rstd[row] : 1.f;
+  const float hs = p.h_raw ? r : 1.f;
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g0 = bf16lo(gv[c][e]), g1 = bf16hi(gv[c][e]);
+      if constexpr (LN) s1 += g0 + g1;
+      s2 = fmaf(g0, bf16lo(hv[c][e]) * hs, s2);
+      s2 = fmaf(g1, bf16hi(hv[c][e]) * hs, s2);
+    }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) {
+    if constexpr (LN) s1 = xor_sum(s1, m);
+    s2 = xor_sum(s2, m);
+  }
+  if (!valid) return;
+  const float c1 = s1 / (float)N, c2 = s2 / (float)N;
+  uint16_t* dz = p.dZ + row * (int64_t)N;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int col = (c * LPR + sub) * 8;
+    if (col >= N) continue;
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = r * (bf16lo(gv[c][e]) - c1 - bf16lo(hv[c][e]) * hs * c2);
+      const float b = r * (bf16hi(gv[c][e]) - c1 - bf16hi(hv[c][e]) * hs * c2);
+      o[e] = pack_bf16(a, b);
+    }
+    *reinterpret_cast<u32x4_t*>(dz + col) = o;
+  }
+}
+
+// rows longer than 8192: one block per row, both rows read twice
+template <bool LN>
+__global__ __launch_bounds__(256) void rownorm_bwd_long_kernel(RowBwdParams p) {
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int N = p.N;
+  const uint16_t* g = p.G + row * (int64_t)N;
+  const uint16_t* h = p.H + row * (int64_t)N;
+  uint16_t* dz = p.dZ + row * (int64_t)N;
+  __shared__ float red[2][4];
+  const float r = p.rstd[row];
+  const float hs = p.h_raw ? r : 1.f;
+  float s1 = 0.f, s2 = 0.f;
+  for (int col = tid * 8; col < N; col += 256 * 8) {
+    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(g + col);
+    const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(h + col);
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (LN) s1 += bf16lo(gv[e]) + bf16hi(gv[e]);
+      s2 = fmaf(bf16lo(gv[e]), bf16lo(hv[e]) * hs, s2);
+      s2 = fmaf(bf16hi(gv[e]), bf16hi(hv[e]) * hs, s2);
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    s1 = xor_sum(s1, m);
+    s2 = xor_sum(s2, m);
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = s1;
+    red[1][tid >> 6] = s2;
+  }
+  __syncthreads();
+  const float c1 = (red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)N;
+  const float c2 = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)N;
+  for (int col = tid * 8; col < N; col += 256 * 8) {
+    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(g + col);
+    const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(h + col);
+    u32x4_t o;
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_bf16(r * (bf16lo(gv[e]) - (LN ? c1 : 0.f) - bf16lo(hv[e]) * hs * c2),
+                       r * (bf16hi(gv[e]) - (LN ? c1 : 0.f) - bf16hi(hv[e]) * hs * c2));
+    *reinterpret_cast<u32x4_t*>(dz + col) = o;
+  }
+}
+
+namespace {
+
+template <int LPR, int CPL, bool LN>
+int go_bwd(const RowBwdParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / LPR;
+  const int64_t grid = (p.M + RPB - 1) / RPB;
+  hipLaunchKernelGGL((rownorm_bwd_kernel<LPR, CPL, LN>), dim3((unsigned)grid), dim3(256), 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+template <bool LN>
+int dispatch_bwd(const RowBwdParams& p, hipStream_t s) {
+  const int N = p.N;
+  if (N <= 128) return go_bwd<16, 1, LN>(p, s);
+  if (N <= 256) return go_bwd<32, 1, LN>(p, s);
+  if (N <= 512) return go_bwd<64, 1, LN>(p, s);
+  if (N <= 1024) return go_bwd<64, 2, LN>(p, s);
+  if (N <= 2048) return go_bwd<64, 4, LN>(p, s);
+  if (N <= 4096) return go_bwd<64, 8, LN>(p, s);
+  hipLaunchKernelGGL((rownorm_bwd_long_kernel<LN>), dim3((unsigned)p.M), dim3(256), 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_rownorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N,
+                       bool h_raw, bool ln, hipStream_t s) {
+  RowBwdParams p{static_cast<const uint16_t*>(G), static_cast<const uint16_t*>(H), rstd,
+                 static_cast<uint16_t*>(dZ), M, (int)N, h_raw ? 1 : 0};
+  return ln ? dispatch_bwd<true>(p, s) : dispatch_bwd<false>(p, s);
+}
+
+// ---------------------------------------------------------------------------
 // two-pass post-norm, second kernel: one wave per row merges the per-tile
 // partials (fixed order; Chan et al. pairwise (count, mean, M2) merge for
 // LayerNorm, plain sum of squares for RMSNorm) and normalizes the row of Y

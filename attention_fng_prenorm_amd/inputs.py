@@ -24,6 +24,18 @@ sides).  "N(mu, v)" is mean and *variance*:
                       K, V [768, 128, 4, 128] dense, all ~ N(0,1); eps_ln 1e-5,
                       eps_rms 1e-6, sm_scale 1/sqrt(128), GELU activation
 
+Backward (section 3's fusion regrouping; shapes of the forward workloads):
+  postnorm_ln_smalln_bwd   G[8192,256] ~ N(0,1), Wt[256,256] ~ N(0,1/256),
+                           Y[8192,256] ~ N(0,1) (the forward output),
+                           rstd[8192] = exp(N(0, 0.25)) (fp32)
+  postnorm_rms_largen_bwd  G[16384,1024], Wt[1024,4096] ~ N(0,1/1024),
+                           Y[16384,4096], rstd[16384], as above
+  prenorm_rms_mlp_bwd_dx   dY[4096,14336] ~ N(0,1), Wt[14336,4096] ~
+                           N(0,1/14336), X[4096,4096] with log-normal row
+                           scales (as the forward), rstd[4096] as above
+  The saved tensors and statistics are drawn independently of each other:
+  the backward is a function of them, whatever produced them.
+
 Draw order inside one generator: X (row scales first when present), W,
 gamma; for attention Q, K, V; for the jagged attention the lengths, then Q,
 K, V.
@@ -49,6 +61,12 @@ WORKLOADS = {
                                 x_dist="normal", gamma=False, seed=1004),
     "norm_attention": dict(kind="norm_attention", B=32, Sq=1024, Skv=1024, H=4, D=128,
                            eps_ln=1e-5, eps_rms=1e-6, seed=1005),
+    "postnorm_ln_smalln_bwd": dict(kind="norm_bwd", M=8192, K=256, N=256, norm="ln", h_dist="normal",
+                                   seed=1012),
+    "postnorm_rms_largen_bwd": dict(kind="norm_bwd", M=16384, K=1024, N=4096, norm="rms", h_dist="normal",
+                                    seed=1014),
+    "prenorm_rms_mlp_bwd_dx": dict(kind="norm_bwd", M=4096, K=14336, N=4096, norm="rms",
+                                   h_dist="lognormal_rows", seed=1023),
     "flash_norm_attention": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
                                  D=128, eps_ln=1e-5, eps_rms=1e-6, act="gelu", seed=1006),
 }
@@ -139,6 +157,25 @@ def make_jagged_attention_inputs(spec):
     return {"Q": q, "K": k, "V": v, "offsets": offsets}
 
 
+def make_norm_bwd_inputs(spec):
+    """Inputs of a regrouped norm backward dZ = norm_bwd(G @ Wt) over N:
+    dict G [M,K], Wt [K,N], H [M,N] bf16 bits (the saved forward output, or
+    the norm's input for the lazy pre-norm), rstd [M] float32.  Sizes are
+    those of the product (for the pre-norm input gradient, K is the forward's
+    N and N the forward's K)."""
+    rng = np.random.Generator(np.random.PCG64(spec["seed"]))
+    M, K, N = spec["M"], spec["K"], spec["N"]
+    g = _normal(rng, (M, K))
+    w = _normal(rng, (K, N), var=1.0 / K)
+    if spec["h_dist"] == "lognormal_rows":
+        s = np.exp(_normal(rng, (M, 1)))
+        h = s * _normal(rng, (M, N))
+    else:
+        h = _normal(rng, (M, N))
+    rstd = np.exp(_normal(rng, (M,), var=0.25)).astype(np.float32)
+    return {"G": f32_to_bf16_bits(g), "Wt": f32_to_bf16_bits(w), "H": f32_to_bf16_bits(h), "rstd": rstd}
+
+
 def make_inputs(name, **overrides):
     """Spec and inputs for workload `name` (see the recipe in the header)."""
     spec = workload(name, **overrides)
@@ -146,4 +183,6 @@ def make_inputs(name, **overrides):
         return spec, make_attention_inputs(spec)
     if spec["kind"] == "flash_norm_attention":
         return spec, make_jagged_attention_inputs(spec)
+    if spec["kind"] == "norm_bwd":
+        return spec, make_norm_bwd_inputs(spec)
     return spec, make_gemm_inputs(spec)

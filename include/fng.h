@@ -114,6 +114,39 @@ int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, float* rstd_out
 int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Backward by fusion regrouping (section 3, "What about backward?"): the norm
+ * backward is the epilogue of the GEMM that produces its upstream gradient,
+ * so it stays an epilogue fusion (the forward's full-N and split-N paths).
+ *   dZ = norm_backward(G @ Wt), rows of length N, with the forward's outputs:
+ *     LayerNorm:  dZ = rstd * (g - mean(g) - Y * mean(g * Y))
+ *     RMSNorm:    dZ = rstd * (g - Y * mean(g * Y))
+ * G [M, K]: the gradient at the output of the layer after the norm; Wt [K, N]:
+ * that layer's weight read as [K, N] (a torch Linear's weight [out, in] as
+ * stored); Y [M, N]: the norm's forward output (bf16); rstd [M]: its forward
+ * statistic (fp32).  dZ [M, N] is the gradient at the norm's input.  `path`:
+ * FNG_PATH_AUTO, FULLN (N <= fng_fulln_max_n()) or SPLITN (workspace of
+ * fng_gemm_postnorm_workspace_bytes(M, N, K, FNG_PATH_SPLITN) bytes, zeroed
+ * once, as the forward's); TWOPASS returns FNG_ERR_UNSUPPORTED.  M*N*2 must be
+ * below 2^31.  G, Wt, Y, dZ 16-byte aligned; rstd 4-byte aligned.
+ * ------------------------------------------------------------------------- */
+int fng_gemm_postnorm_ln_bwd(const void* G, const void* Wt, const void* Y, const float* rstd, void* dZ,
+                             int64_t M, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, int path, void* stream);
+int fng_gemm_postnorm_rms_bwd(const void* G, const void* Wt, const void* Y, const float* rstd, void* dZ,
+                              int64_t M, int64_t N, int64_t K, void* workspace,
+                              size_t workspace_bytes, int path, void* stream);
+/* Input gradient of the lazy pre-RMSNorm GEMM Y = rmsnorm(X) @ W (section 2;
+ * the normalized X is rebuilt from X and the forward rstd, never stored):
+ *   dX = rstd * (g - xhat * mean(g * xhat)),  g = dY @ Wt,  xhat = X * rstd
+ * with the forward's sizes: dY [M, N], Wt [N, K] (W transposed, a torch
+ * Linear's weight as stored), X and dX [M, K], rstd [M].  The norm runs over
+ * K: paths and workspace as above with (M, K, N) in place of (M, N, K).  The
+ * weight gradient X^T diag(rstd) dY is a plain GEMM and not part of this call. */
+int fng_prenorm_rms_bwd_dx(const void* dY, const void* Wt, const void* X, const float* rstd, void* dX,
+                           int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, int path, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Norm-sandwiched attention (section 4, FlashNormAttention, in its per-head,
  * softmax, no-residual form):
  *   for each (b, h):  q^ = layernorm(Q[b,:,h,:]) over D   (eps_ln, no affine)
@@ -171,6 +204,14 @@ int fng_rmsnorm(const void* X, const void* gamma, void* Y, float* rstd_out, int6
 /* Y = layernorm(X) over rows of length N (biased variance, no affine). */
 int fng_layernorm(const void* X, void* Y, float* mean_out, float* rstd_out, int64_t M,
                   int64_t N, float eps, void* stream);
+/* Unfused norm backward over rows of length N (the regrouped GEMM's baseline):
+ * dZ = rstd * (G - mean(G) - Y * mean(G * Y)) (LayerNorm), Y the forward output;
+ * dZ = rstd * (G - xhat * mean(G * xhat)) (RMSNorm), xhat = H, or H * rstd when
+ * h_is_input (H is then the norm's input).  G, H/Y, dZ [M, N] bf16, rstd [M]. */
+int fng_layernorm_bwd(const void* G, const void* Y, const float* rstd, void* dZ, int64_t M,
+                      int64_t N, void* stream);
+int fng_rmsnorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M,
+                    int64_t N, int h_is_input, void* stream);
 /* Y = X @ W in bf16 with fp32 accumulation (same mainloop as the fused GEMMs). */
 int fng_gemm(const void* X, const void* W, void* Y, int64_t M, int64_t N, int64_t K,
              void* stream);

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for must in ("fng_prenorm_rms_gemm", "fng_gemm_postnorm_ln", "fng_gemm_postnorm_rms",
                  "fng_norm_attention", "fng_rmsnorm", "fng_layernorm", "fng_gemm", "fng_attention",
-                 "fng_flash_norm_attention", "fng_jagged_attention"):
+                 "fng_flash_norm_attention", "fng_jagged_attention", "fng_gemm_postnorm_ln_bwd",
+                 "fng_gemm_postnorm_rms_bwd", "fng_prenorm_rms_bwd_dx", "fng_layernorm_bwd", "fng_rmsnorm_bwd"):
         assert must in names
 
 
@@ -159,6 +160,34 @@ def test_flash_norm_attention_validation(lib):
     assert j(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 8, 2, 128, 0.0, 5, None) == B.FNG_ERR_INVALID_ARG
     assert j(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, 8, 8, 2, 96, 0.0, S, None) == B.FNG_ERR_UNSUPPORTED
     assert j(None, None, None, None, None, 2, 0, 8, 8, 2, 128, 0.0, S, None) == B.FNG_OK
+
+
+def test_backward_validation(lib):
+    # (function, whether its N and K name the product's output and reduction
+    # sizes in that order: the pre-norm input gradient takes the forward's)
+    for f, swap in ((lib.fng_gemm_postnorm_ln_bwd, False), (lib.fng_gemm_postnorm_rms_bwd, False),
+                    (lib.fng_prenorm_rms_bwd_dx, True)):
+        def call(G=FAKE, Wt=FAKE, H=FAKE, r=FAKE, dZ=FAKE, M=4, N=8, K=8, ws=None, wsb=0, path=0):
+            # N = the norm axis, K = the reduction, whatever the entry point calls them
+            return f(G, Wt, H, r, dZ, M, K, N, ws, wsb, path, None) if swap else \
+                f(G, Wt, H, r, dZ, M, N, K, ws, wsb, path, None)
+        assert call(K=0) == B.FNG_ERR_INVALID_ARG
+        assert call(path=9) == B.FNG_ERR_INVALID_ARG
+        assert call(H=None) == B.FNG_ERR_INVALID_ARG
+        assert call(r=None) == B.FNG_ERR_INVALID_ARG
+        assert call(H=MIS) == B.FNG_ERR_MISALIGNED
+        assert call(r=FAKE + 2) == B.FNG_ERR_MISALIGNED
+        assert call(N=12, K=12) == B.FNG_ERR_MISALIGNED                          # rows of whole 16-B vectors
+        assert call(path=B.FNG_PATH_TWOPASS) == B.FNG_ERR_UNSUPPORTED            # no two-pass backward
+        assert call(M=4, N=4096, K=4096, path=B.FNG_PATH_FULLN) == B.FNG_ERR_UNSUPPORTED
+        assert call(M=4, N=4096, K=4096, path=B.FNG_PATH_SPLITN) == B.FNG_ERR_WORKSPACE
+        assert call(M=1 << 20, N=4096, K=8) == B.FNG_ERR_UNSUPPORTED            # saved tensor over 2 GiB
+        assert call(G=None, Wt=None, H=None, r=None, dZ=None, M=0) == B.FNG_OK
+    assert lib.fng_layernorm_bwd(FAKE, FAKE, FAKE, FAKE, 4, 12, None) == B.FNG_ERR_MISALIGNED
+    assert lib.fng_layernorm_bwd(FAKE, None, FAKE, FAKE, 4, 8, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_rmsnorm_bwd(FAKE, FAKE, FAKE + 1, FAKE, 4, 8, 1, None) == B.FNG_ERR_MISALIGNED
+    assert lib.fng_rmsnorm_bwd(FAKE, FAKE, FAKE, FAKE, 4, 0, 0, None) == B.FNG_ERR_INVALID_ARG
+    assert lib.fng_rmsnorm_bwd(None, None, None, None, 0, 8, 0, None) == B.FNG_OK
 
 
 def test_norm_and_gemm_validation(lib):
