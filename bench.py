@@ -12,7 +12,8 @@ Beside it, the same JSON line carries every fused kernel of the hot path at its
 workload shape (post-LayerNorm GEMM with one workgroup across N, the affine
 pre-RMSNorm variant, post-RMSNorm GEMM with the split-N exchange and its
 two-pass fallback, the norm-sandwiched attention, and the full
-FlashNormAttention on jagged queries with short keys) with the unfused
+FlashNormAttention on jagged queries with short keys, and the backward by
+fusion regrouping on the same shapes) with the unfused
 baselines they replace, timed interleaved, and the "norm latency hidden"
 figure (T_gemm + T_norm - T_fused) / T_norm of the pages; and the pages'
 ads-shape sweep of the post-LayerNorm GEMM (M = 256k rows, K and N from 64 to
@@ -21,7 +22,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|ads|copy]
+       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|bwd|ads|copy]
 """
 
 import argparse
@@ -270,6 +271,42 @@ def main():
             "speedup_vs_unfused": round(base / t["fused"], 2),
         }
         del sets6, O6, st6, ln6, at6, y6
+
+    # ---------------- backward by fusion regrouping --------------------------------
+    # dZ = norm_bwd(G @ Wt) fused (full-N / split-N epilogue) against the plain
+    # GEMM followed by the standalone row norm backward; the pre-RMSNorm input
+    # gradient rebuilds xhat from X and rstd in the same epilogue
+    if args.only in (None, "bwd"):
+        res = {}
+        for wname, kind in (("postnorm_ln_smalln_bwd", "ln"), ("postnorm_rms_largen_bwd", "rms"),
+                            ("prenorm_rms_mlp_bwd_dx", "prenorm")):
+            sb, db = inputs.make_inputs(wname)
+            Mb, Kb, Nb = sb["M"], sb["K"], sb["N"]   # product [Mb, Kb] @ [Kb, Nb], norm over Nb
+            Gb, Wb, Hb = dev(db["G"]), dev(db["Wt"]), dev(db["H"])
+            rb = torch.from_numpy(db["rstd"]).to("cuda")
+            sets = [(Gb, Hb), (Gb.flip(0).contiguous(), Hb.flip(0).contiguous())]
+            dZ = torch.empty(Mb, Nb, dtype=torch.bfloat16, device="cuda")
+            gtmp = torch.empty_like(dZ)
+            nbw = B.fng_gemm_postnorm_workspace_bytes(Mb, Nb, Kb, B.FNG_PATH_SPLITN)
+            wsb = torch.zeros(max(nbw, 16), dtype=torch.uint8, device="cuda")
+            if kind == "ln":
+                fused = lambda i: B.fng_gemm_postnorm_ln_bwd(sets[i % 2][0], Wb, sets[i % 2][1], rb, dZ, wsb)
+                normb = lambda i: B.fng_layernorm_bwd(gtmp, sets[i % 2][1], rb, dZ)
+            elif kind == "rms":
+                fused = lambda i: B.fng_gemm_postnorm_rms_bwd(sets[i % 2][0], Wb, sets[i % 2][1], rb, dZ, wsb)
+                normb = lambda i: B.fng_rmsnorm_bwd(gtmp, sets[i % 2][1], rb, dZ)
+            else:
+                fused = lambda i: B.fng_prenorm_rms_bwd_dx(sets[i % 2][0], Wb, sets[i % 2][1], rb, dZ, wsb)
+                normb = lambda i: B.fng_rmsnorm_bwd(gtmp, sets[i % 2][1], rb, dZ, h_is_input=True)
+            t = time_batches({"fused": fused, "gemm": lambda i: B.fng_gemm(sets[i % 2][0], Wb, gtmp),
+                              "norm_bwd": normb}, args.reps, args.batch)
+            assert B.fng_get_kernel_status(wsb) == B.FNG_OK
+            fl = 2.0 * Mb * Nb * Kb
+            res[wname] = {"M": Mb, "K": Kb, "N": Nb, "fused_us": round(t["fused"], 2), "gemm_us": round(t["gemm"], 2),
+                          "norm_bwd_us": round(t["norm_bwd"], 2), "fused_tflops": round(fl / t["fused"] / 1e6, 1),
+                          "norm_hidden_pct": round(100.0 * (t["gemm"] + t["norm_bwd"] - t["fused"]) / t["norm_bwd"], 1)}
+            del sets, Gb, Wb, Hb, dZ, gtmp, wsb
+        kernels["backward_regrouped"] = res
 
     # ---------------- ads-shape sweep: post-LayerNorm GEMM, M = 256k rows ---------
     # K and N from 64 to 2048 (the pages' sweep of the naive full-N regime at small
