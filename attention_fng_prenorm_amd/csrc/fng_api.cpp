@@ -47,7 +47,8 @@ struct Workspace {
   size_t bytes;
 };
 
-// layout: [status (256 B)] [cnt: tiles_m u32] [done: tiles_m u32] (256-B aligned) [partials]
+// layout: [status (256 B): timeout flag, epoch, finished row blocks] [cnt: tiles_m u32, unused]
+// [done: tiles_m u32] (256-B aligned) [partials]
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 Workspace layout(void* base, int64_t M, int64_t N) {
@@ -62,7 +63,9 @@ Workspace layout(void* base, int64_t M, int64_t N) {
   w.done = reinterpret_cast<uint32_t*>(b + off);
   off += align256((size_t)tm * 4);
   w.part = reinterpret_cast<float*>(b + off);
-  off += (size_t)tm * tn * bm * 2 * sizeof(float);
+  // split-N: two 64-bit (value, epoch tag) entries per row and tile; the
+  // two-pass path uses the same region as plain floats
+  off += (size_t)tm * tn * bm * 2 * sizeof(uint64_t);
   w.bytes = off;
   return w;
 }

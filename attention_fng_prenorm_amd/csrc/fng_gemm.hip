@@ -186,6 +186,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   const int M = p.M, N = p.N, K = p.K;
   const int ktiles = (K + BK - 1) / BK;
 
+  // split-N: this call's tag = the last call's epoch + 1 (constant during the
+  // call: the epoch only advances after every row block has been merged)
+  uint32_t ep = 0;
+  if constexpr (IS_SPLIT) ep = __hip_atomic_load(p.status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+
   // persistent loop for split-N, one tile per workgroup otherwise
   const uint32_t G = gridDim.x;
   const uint32_t slot = xcd_remap(blockIdx.x, G);
@@ -542,22 +547,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           rs_rstd[i] = s2[i] / (float)N;
         }
       } else {
-        // publish partials: part[tm][tn][row][2]
         if constexpr (EPI == EPI_PARTIAL) {
+          // two-pass: plain float partials part[tm][tn][row][2] for the finalize kernel
 #pragma unroll
           for (int i = 0; i < FM; ++i) rs_mean[i] = s1[i];
-        }
-        float* pp = p.part + ((size_t)tm * p.tiles_n + tn) * (BM * 2);
-        if (wn == 0 && hi == 0) {
+          float* pp = p.part + ((size_t)tm * p.tiles_n + tn) * (BM * 2);
+          if (wn == 0 && hi == 0) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int row = lrow(i);
-            if constexpr (IS_SPLIT) {
-              // device-scope stores: written through to the device-coherent
-              // level, visible to every XCD without a cache-wide write-back
-              __hip_atomic_store(pp + row * 2 + 0, s1[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(pp + row * 2 + 1, s2[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
+            for (int i = 0; i < FM; ++i) {
+              const int row = lrow(i);
               pp[row * 2 + 0] = s1[i];
               pp[row * 2 + 1] = s2[i];
             }
@@ -565,72 +563,79 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         }
         if constexpr (IS_SPLIT) {
           // Exchange (section 3's multi-CTA reduction, without clusters).
-          // Every access to the exchanged data is a device-scope atomic, which
-          // the hardware performs at the device-coherent level (past the
-          // per-XCD L2s), so no cache-wide release/acquire fence is needed:
-          //  - each writer wave waits until its partial stores are acknowledged
-          //    (vmcnt 0) before the workgroup barrier;
-          //  - one thread then arrives on the row block's counter and polls it;
-          //  - after a second barrier all threads read the partials with
-          //    device-scope loads, issued only once the poll has returned.
-          wait_vmcnt<0>();
-          __syncthreads();
-          FNG_LDS float* stats = (FNG_LDS float*)(lds + RED);  // [BM][2]: mean, rstd
-          if (tid == 0) {
-            __hip_atomic_fetch_add(p.cnt + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t target = (uint32_t)p.tiles_n;
-            uint32_t spins = 0;
-            while (__hip_atomic_load(p.cnt + tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-              __builtin_amdgcn_s_sleep(1);
-              if (++spins > p.spin_limit) {
-                __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-              }
-            }
-            // every workgroup of the row block has finished waiting once the
-            // last one arrives here: it resets the counters for the next call
-            const uint32_t prev =
-                __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (prev == target - 1u) {
-              __hip_atomic_store(p.cnt + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // Each partial is one 64-bit device-scope store of (value, tag): the
+          // tag is this call's epoch, so a reader that sees the tag has the
+          // value, and readers poll the partials themselves -- one memory
+          // round trip when the peers are done, no counter on the critical
+          // path.  Device-scope accesses are performed at the device-coherent
+          // level (past the per-XCD L2s): no cache-wide write-back needed.
+          // part: [tm][tn][row][2] x 64 bit; status[1]: epoch of the last call.
+          constexpr bool NEED1 = LN;  // LayerNorm needs the first partial too
+          uint64_t* pt = reinterpret_cast<uint64_t*>(p.part);
+          if (wn == 0 && hi == 0) {
+            uint64_t* q = pt + ((size_t)tm * p.tiles_n + tn) * (BM * 2);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              const int row = lrow(i);
+              if constexpr (NEED1)
+                __hip_atomic_store(q + row * 2 + 0, ((uint64_t)ep << 32) | __float_as_uint(s1[i]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(q + row * 2 + 1, ((uint64_t)ep << 32) | __float_as_uint(s2[i]), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
             }
           }
-          __syncthreads();
-          // merge the tiles_n slices of row tid in a fixed order; the
-          // device-scope loads are issued in batches of 16 independent loads
-          // (one at a time they would be serialized memory round trips)
+          FNG_LDS float* stats = (FNG_LDS float*)(lds + RED);  // [BM][2]
+          // merge the tiles_n slices of row tid in a fixed order (bitwise
+          // reproducible); loads in batches of 8 independent loads, a batch
+          // re-polled until every tag in it is this call's
           if (tid < BM) {
-            float* pb = p.part + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
+            const uint64_t* pb = pt + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
             const int nt = p.tiles_n;
-            constexpr int BATCH = 16;
+            constexpr int BATCH = 8;
             float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f, gsum = 0.f;
+            uint32_t spins = 0;
             for (int q0 = 0; q0 < nt; q0 += BATCH) {
-              float mb[BATCH], vb[BATCH];
+              uint64_t mb[BATCH], vb[BATCH];
+              for (;;) {
 #pragma unroll
-              for (int u = 0; u < BATCH; ++u) {
-                const int q = min(q0 + u, nt - 1);  // clamped: always a valid slice
-                float* a = pb + (size_t)q * BM * 2;
-                if constexpr (LN) mb[u] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                vb[u] = __hip_atomic_load(a + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int u = 0; u < BATCH; ++u) {
+                  const int q = min(q0 + u, nt - 1);  // clamped: always a valid slice
+                  const uint64_t* a = pb + (size_t)q * BM * 2;
+                  if constexpr (NEED1) mb[u] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  vb[u] = __hip_atomic_load(a + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                bool ready = true;
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) {
+                  if constexpr (NEED1) ready = ready && (uint32_t)(mb[u] >> 32) == ep;
+                  ready = ready && (uint32_t)(vb[u] >> 32) == ep;
+                }
+                if (ready) break;
+                if (++spins > p.spin_limit) {
+                  __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  break;
+                }
+                __builtin_amdgcn_s_sleep(1);
               }
 #pragma unroll
               for (int u = 0; u < BATCH; ++u) {
                 if (q0 + u >= nt) break;
+                const float v1 = NEED1 ? __uint_as_float((uint32_t)mb[u]) : 0.f;
+                const float v2 = __uint_as_float((uint32_t)vb[u]);
                 if constexpr (IS_BWD) {
-                  // backward: plain sums of g and g * xhat, fixed order
-                  if constexpr (LN) gsum += mb[u];
-                  ssum += vb[u];
+                  // backward: plain sums of g and g * xhat
+                  gsum += v1;
+                  ssum += v2;
                 } else if constexpr (LN) {
                   // Chan et al. pairwise merge of (count, mean, M2)
                   const float nb = (float)min(BN, N - (q0 + u) * BN);
                   const float tot = cn + nb;
-                  const float d = mb[u] - mean;
+                  const float d = v1 - mean;
                   mean += d * (nb / tot);
-                  m2 += vb[u] + d * d * (cn * nb / tot);
+                  m2 += v2 + d * d * (cn * nb / tot);
                   cn = tot;
                 } else {
-                  ssum += vb[u];
+                  ssum += v2;
                 }
               }
             }
@@ -650,6 +655,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           for (int i = 0; i < FM; ++i) {
             rs_mean[i] = stats[lrow(i) * 2 + 0];
             rs_rstd[i] = stats[lrow(i) * 2 + 1];
+          }
+          // The epoch advances once every row block has been read (the call's
+          // last workgroup to merge): done[tm] counts the row block's readers,
+          // status[2] the finished row blocks.  Off the critical path.
+          if (tid == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (prev == (uint32_t)p.tiles_n - 1u) {
+              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const uint32_t f = __hip_atomic_fetch_add(p.status + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (f == (uint32_t)p.tiles_m - 1u) {
+                __hip_atomic_store(p.status + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p.status + 1, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
           }
         }
       }

@@ -295,7 +295,7 @@ def test_splitn_workspace_reuse_and_determinism():
     ws = None
     shapes = [(1100, 256, 4096), (300, 128, 1024), (1100, 256, 4096)]
     first = None
-    for (M, K, N) in shapes:
+    for call, (M, K, N) in enumerate(shapes, start=1):
         spec, d = inputs.make_inputs("postnorm_rms_largen", M=M, K=K, N=N, seed=5)
         need = B.fng_gemm_postnorm_workspace_bytes(M, N, K, B.FNG_PATH_SPLITN)
         if ws is None:
@@ -311,8 +311,12 @@ def test_splitn_workspace_reuse_and_determinism():
             first = Y.clone()
         elif (M, K, N) == shapes[0]:
             assert torch.equal(first.view(torch.int16), Y.view(torch.int16)), "not bitwise reproducible"
-        # counters are back to zero after every call (status word + cnt + done arrays)
-        head = ws[:256 + 2 * 256].view(torch.int32)
+        # after every call: timeout flag 0, the epoch word counts the calls on
+        # this workspace, the finished-row-block and per-row-block reader
+        # counters are back to zero
+        head = ws[:256 + 2 * 256].view(torch.int32).cpu()
+        assert int(head[0]) == 0 and int(head[1]) == call, head[:4]
+        head[1] = 0
         assert int(head.abs().sum()) == 0
 
 
