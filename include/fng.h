@@ -92,11 +92,15 @@ int fng_prenorm_rms_gemm(const void* X, const void* W, const void* gamma, void* 
  *
  * workspace: caller-owned device memory of at least
  * fng_gemm_postnorm_workspace_bytes(M, N, K, path) bytes, zero-filled ONCE
- * when allocated; the kernels leave it zeroed again for the next call.  It may
+ * when allocated; the kernels keep it consistent for the next call.  It may
  * be NULL only when that size is 0.  Calls sharing one workspace must be
- * ordered (same stream).  If a call reports FNG_ERR_TIMEOUT through
- * fng_get_kernel_status, its Y is invalid and the workspace must be
- * zero-filled again.
+ * ordered (same stream).  The split-N grid is sized to what the GPU holds at
+ * once (one workgroup per CU) and launched normally: its workgroups wait for
+ * each other with a bounded wait.  On a GPU shared with other work that keeps
+ * CUs busy past that bound, or after a fault, a call reports FNG_ERR_TIMEOUT
+ * through fng_get_kernel_status; its Y is then invalid and the workspace must
+ * be zero-filled again.  Between calls the workspace holds an epoch word
+ * (bytes 4..7) that counts the split-N calls made on it.
  * ------------------------------------------------------------------------- */
 size_t fng_gemm_postnorm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path);
 int64_t fng_fulln_max_n(void);
