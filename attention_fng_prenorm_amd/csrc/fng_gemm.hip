@@ -247,7 +247,39 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     }
     // Out-of-range copies (K tail, N tail, tiles past the end) set bit 31 of
     // the offset: both descriptors' ranges are below 2^31, so they read zeros.
+    // norm backward: the refills past the last K tile bring in the saved
+    // [BM, BN] tile instead of zeros -- each LDS block of a freed stage gets
+    // the block of the tile (output staging layout) that lives at that
+    // address, so the tile is in LDS when the mainloop ends.  Same number of
+    // copies per refill, so the vmcnt accounting does not change.
+    i32x4_t hr;
+    if constexpr (IS_BWD) hr = dma_rsrc(p.H, (uint32_t)((int64_t)M * N * 2));
+    auto saved_block = [&](int off) __attribute__((always_inline)) {
+      constexpr int NCH = BN / 8;
+      constexpr int TB = BM * BN * 2 / 1024;  // blocks of the saved tile
+      const int blk = off / 1024;
+      if (blk >= TB) return kOOB;
+      const int idx = blk * 1024 + lane * 16;
+      const int row = idx / (BN * 2), pc = (idx % (BN * 2)) / 16;
+      const int ch = (pc ^ row) & (NCH - 1);
+      return (uint32_t)(((int64_t)(m0 + row) * N + n0 + ch * 8) * 2);
+    };
     auto issue = [&](int kt, int s) {
+      if constexpr (IS_BWD) {
+        if (kt >= ktiles) {
+#pragma unroll
+          for (int i = 0; i < A_PER_WAVE; ++i) {
+            const int off = S::a(s) + (wave * A_PER_WAVE + i) * 1024;
+            dma16(hr, lds + off, saved_block(off));
+          }
+#pragma unroll
+          for (int i = 0; i < B_PER_WAVE; ++i) {
+            const int off = S::b(s) + (wave * B_PER_WAVE + i) * 1024;
+            dma16(hr, lds + off, saved_block(off));
+          }
+          return;
+        }
+      }
       const uint32_t kt_live = kt < ktiles ? 0u : kOOB;
 #pragma unroll
       for (int i = 0; i < A_PER_WAVE; ++i) {
@@ -395,30 +427,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       }
     }
 
-    // norm backward: the saved tile (xhat or the norm's input) goes to LDS in
-    // the output staging layout below, the forward rstd to registers
+    // norm backward: the saved tile (xhat or the norm's input) is in LDS in
+    // the output staging layout (copied by the last refills); the forward
+    // rstd goes to registers
     float bw_r[FM], bw_hs[FM];
     if constexpr (IS_BWD) {
-      constexpr int HB = BM * BN * 2 / 1024 / NWAVES;  // 1 KB copies per wave
-      static_assert(HB * NWAVES * 1024 == BM * BN * 2, "saved tile split evenly over the waves");
-      constexpr int NCH = BN / 8;
-      const i32x4_t hr = dma_rsrc(p.H, (uint32_t)((int64_t)M * N * 2));
-#pragma unroll
-      for (int i = 0; i < HB; ++i) {
-        const int blk = wave * HB + i;
-        const int idx = blk * 1024 + lane * 16;
-        const int row = idx / (BN * 2), pc = (idx % (BN * 2)) / 16;
-        const int ch = (pc ^ row) & (NCH - 1);
-        dma16(hr, lds + blk * 1024, (uint32_t)(((int64_t)(m0 + row) * N + n0 + ch * 8) * 2));
-      }
+      static_assert(S::A_STAGE % 1024 == 0 && S::B_STAGE % 1024 == 0, "whole 1 KB blocks per stage");
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int m = row_of(i);
         bw_r[i] = m < M ? p.rstd_in[m] : 1.f;
         bw_hs[i] = p.h_raw ? bw_r[i] : 1.f;
       }
-      wait_vmcnt<0>();
-      __syncthreads();
     }
     // 8 B of the staged tile at this lane's (row slot i, columns col_of(j, r4) ..)
     auto stage_addr = [&](int i, int j, int r4) __attribute__((always_inline)) {
