@@ -50,6 +50,13 @@ Readings of points the page leaves open (each also listed in the design notes):
     of the next layer's output gradient with that layer's weight; the
     normalized values come from the forward (the norm's output, or for the
     lazy pre-norm rebuilt as x * rstd from its input and statistic).
+  * FlashNormAttention backward (section 4, "Backward implementation"): the
+    gradients of the forward above with respect to q, k and v, by the chain
+    rule (RMSNorm backward, the two residuals, the attention backward with
+    the softmax Jacobian or the derivative of the tanh-form GELU, LayerNorm
+    backward across all heads).  The page keeps the norm statistics from the
+    forward and recomputes the LayerNorm output and the RMSNorm output and
+    input; the oracle recomputes the whole forward from q, k and v in fp64.
 """
 
 import numpy as np
@@ -338,6 +345,87 @@ def flash_norm_attention(q, offsets, k, v, eps_ln, eps_rms, sm_scale, act):
         ln_rstd[r0:r1] = rs1
         rms_rstd[r0:r1] = rs2
     return out, ln_mean, ln_rstd, rms_rstd
+
+
+def gelu_tanh_grad(x):
+    """Derivative of gelu_tanh: with u = sqrt(2/pi) (x + 0.044715 x^3) and
+    t = tanh(u), d/dx [0.5 x (1 + t)] = 0.5 (1 + t) + 0.5 x (1 - t^2) u'(x),
+    u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.sqrt(2.0 / np.pi)
+    t = np.tanh(a * (x + 0.044715 * x ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * a * (1.0 + 3.0 * 0.044715 * x * x)
+
+
+def activation_backward(s, p, dp, act):
+    """Gradient at the scores s of p = act(s), given dp, the gradient at p.
+    softmax over the last axis: ds = p * (dp - sum(p * dp)) (the softmax
+    Jacobian diag(p) - p p^T applied to dp); GELU, elementwise: dp * gelu'(s).
+    """
+    if act == "softmax":
+        return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+    if act == "gelu":
+        return dp * gelu_tanh_grad(s)
+    raise ValueError(act)
+
+
+def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
+    """Gradients of flash_norm_attention with respect to q, k and v, given the
+    gradient dout [T, H, D] at its output (section 4, "Backward
+    implementation": the norm statistics come from the forward, the LayerNorm
+    output and the RMSNorm input and output are recomputed; here the whole
+    forward is recomputed in fp64 from q, k and v).
+
+    The chain, for every query row (x = q, all H*D values):
+        forward   ln = layernorm(x); s_h = ln_h k_h^T sm_scale; p_h = act(s_h)
+                  o_h = p_h v_h + ln_h; y = rmsnorm(o); out = y + x
+        backward  do   = rmsnorm_backward(dout, y, rstd_rms)
+                  dln  = do + sum over heads of (d/d ln_h of p_h v_h) . do_h
+                         with dp_h = do_h v_h^T, ds_h = act_backward(dp_h),
+                         dln_h += sm_scale ds_h k_h
+                  dv_h += p_h^T do_h, dk_h += sm_scale ds_h^T ln_h  (summed over
+                         the batch's rows)
+                  dq   = dout + layernorm_backward(dln, ln, rstd_ln)
+    Returns (dq [T, H, D], dk [B, Skv, H, D], dv [B, Skv, H, D]); rows outside
+    every batch get dq = 0, batches without rows dk = dv = 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    T, H, D = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        L = r1 - r0
+        x = q[r0:r1].reshape(L, H * D)
+        ln, _, rs1 = layernorm_rows(x, eps_ln)
+        ln = ln.reshape(L, H, D)
+        s = np.empty((H, L, k.shape[1]))
+        p = np.empty_like(s)
+        o = np.empty_like(ln)
+        for h in range(H):
+            s[h] = (ln[:, h, :] @ k[b, :, h, :].T) * sm_scale
+            p[h] = _activation(s[h], act)
+            o[:, h, :] = p[h] @ v[b, :, h, :] + ln[:, h, :]
+        y, rs2 = rmsnorm_rows(o.reshape(L, H * D), eps_rms)
+        g = dout[r0:r1].reshape(L, H * D)
+        do = rmsnorm_backward_rows(g, y, rs2).reshape(L, H, D)
+        dln = do.copy()                                   # first residual
+        for h in range(H):
+            dv[b, :, h, :] = p[h].T @ do[:, h, :]
+            dp = do[:, h, :] @ v[b, :, h, :].T
+            ds = activation_backward(s[h], p[h], dp, act) * sm_scale
+            dln[:, h, :] += ds @ k[b, :, h, :]
+            dk[b, :, h, :] = ds.T @ ln[:, h, :]
+        dx = layernorm_backward_rows(dln.reshape(L, H * D), ln.reshape(L, H * D), rs1)
+        dq[r0:r1] = (g + dx).reshape(L, H, D)             # second residual
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

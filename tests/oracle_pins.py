@@ -657,6 +657,98 @@ def check_prenorm_backward_torch(O):
            "lazy pre-RMS dx vs autograd")
 
 
+def _fna_torch_forward(q, off, k, v, eps_ln, eps_rms, scale, act):
+    """FlashNormAttention from torch library routines (fp64), differentiable
+    in q, k and v: layer_norm and rms_norm across all heads, softmax or the
+    tanh GELU, matrix products."""
+    import torch
+    import torch.nn.functional as F
+    T, H, D = q.shape
+    outs = []
+    for b in range(len(off) - 1):
+        x = q[off[b]:off[b + 1]].reshape(-1, H * D)
+        ln = F.layer_norm(x, (H * D,), eps=eps_ln).reshape(-1, H, D)
+        heads = []
+        for h in range(H):
+            s = ln[:, h, :] @ k[b, :, h, :].T * scale
+            p = torch.softmax(s, dim=-1) if act == "softmax" else F.gelu(s, approximate="tanh")
+            heads.append(p @ v[b, :, h, :])
+        o = torch.stack(heads, dim=1) + ln
+        outs.append((F.rms_norm(o.reshape(-1, H * D), (H * D,), eps=eps_rms) + x).reshape(-1, H, D))
+    return torch.cat(outs)
+
+
+def check_fna_backward_torch(O):
+    import torch
+    q, off, k, v = _fna_case(81, [4, 6], 5, 3, 8, qscale=1.7)
+    dout = _rng(82).standard_normal(q.shape)
+    for act in ("softmax", "gelu"):
+        tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+        _fna_torch_forward(tq, off, tk, tv, 1e-5, 1e-6, 0.45, act).backward(torch.from_numpy(dout))
+        dq, dk, dv = O.flash_norm_attention_backward(q, off, k, v, dout, 1e-5, 1e-6, 0.45, act)
+        _close(dq, tq.grad.numpy(), 1e-11, f"fna backward dq ({act}) vs autograd")
+        _close(dk, tk.grad.numpy(), 1e-11, f"fna backward dk ({act}) vs autograd")
+        _close(dv, tv.grad.numpy(), 1e-11, f"fna backward dv ({act}) vs autograd")
+
+
+def _bf_gelu_tanh(x):
+    return 0.5 * x * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def check_fna_backward_finite_differences(O):
+    # directional derivatives of L = sum(dout * out) with the brute-force forward
+    q, off, k, v = _fna_case(83, [2, 3], 3, 2, 3)
+    rng = _rng(84)
+    dout = rng.standard_normal(q.shape)
+    h = 1e-6
+
+    def loss(qq, kk, vv, act):
+        f = "softmax" if act == "softmax" else _bf_gelu_tanh
+        out = bf_flash_norm_attention(qq.tolist(), off.tolist(), kk.tolist(), vv.tolist(), 1e-5, 1e-6, 0.8, f)
+        return sum(dout[r][a][d] * out[r][a][d] for r in range(len(out)) for a in range(2) for d in range(3))
+
+    for act in ("softmax", "gelu"):
+        dq, dk, dv = O.flash_norm_attention_backward(q, off, k, v, dout, 1e-5, 1e-6, 0.8, act)
+        for _ in range(3):
+            eq, ek, ev = (rng.standard_normal(a.shape) for a in (q, k, v))
+            fd = (loss(q + h * eq, k + h * ek, v + h * ev, act) - loss(q - h * eq, k - h * ek, v - h * ev, act)) / (2 * h)
+            an = float(np.sum(dq * eq) + np.sum(dk * ek) + np.sum(dv * ev))
+            assert abs(fd - an) <= 1e-6 * (1.0 + abs(fd)), (act, fd, an)
+            # and each input alone, so that a mistake in one gradient cannot hide
+            for which, (a, e, g) in enumerate(((q, eq, dq), (k, ek, dk), (v, ev, dv))):
+                args_p = [q, k, v]; args_m = [q, k, v]
+                args_p[which] = a + h * e; args_m[which] = a - h * e
+                fd1 = (loss(*args_p, act) - loss(*args_m, act)) / (2 * h)
+                assert abs(fd1 - float(np.sum(g * e))) <= 1e-6 * (1.0 + abs(fd1)), (act, which, fd1)
+
+
+def check_fna_backward_invariants(O):
+    q, off, k, v = _fna_case(85, [3, 5, 0], 6, 2, 4)
+    T, H, D = q.shape
+    dout = _rng(86).standard_normal(q.shape)
+    x = q.reshape(T, H * D)
+    for act in ("softmax", "gelu"):
+        dq, dk, dv = O.flash_norm_attention_backward(q, off, k, v, dout, 0.0, 1e-6, 0.6, act)
+        # out - x depends on x only through layernorm(x): shifting x by a
+        # constant, or scaling it (eps_ln = 0), leaves it unchanged
+        dx = (dq - dout).reshape(T, H * D)
+        _close(np.sum(dx, axis=1), np.zeros(T), 1e-11, f"{act}: LN part of dq sums to zero")
+        _close(np.sum(dx * (x - x.mean(axis=1, keepdims=True)), axis=1), np.zeros(T), 1e-11,
+               f"{act}: LN part of dq orthogonal to the centred row")
+        # the empty batch gets no key or value gradient
+        assert np.all(dk[2] == 0.0) and np.all(dv[2] == 0.0)
+        # dout = 0: no gradient anywhere
+        z = O.flash_norm_attention_backward(q, off, k, v, np.zeros_like(dout), 0.0, 1e-6, 0.6, act)
+        assert all(np.all(a == 0.0) for a in z)
+    # softmax: adding one vector to every key shifts each score row by a
+    # constant, which softmax ignores, so the key gradients sum to zero
+    dq, dk, dv = O.flash_norm_attention_backward(q, off, k, v, dout, 1e-5, 1e-6, 0.6, "softmax")
+    _close(np.sum(dk, axis=1), np.zeros((3, H, D)), 1e-11, "softmax: key gradients sum to zero")
+    # V = 0 with GELU: the attention output is zero whatever the keys, so dk = 0
+    dq, dk, dv = O.flash_norm_attention_backward(q, off, k, np.zeros_like(v), dout, 1e-5, 1e-6, 0.6, "gelu")
+    _close(dk, np.zeros_like(dk), 0.0, "V = 0: no key gradient")
+
+
 def check_compare(O):
     e = O.compare(np.array([1.0, 2.0]), np.array([1.0, 3.0]))
     assert abs(e["normwise_rel"] - 1.0 / 3.0) < 1e-15, e
@@ -693,6 +785,9 @@ ALL_CHECKS = [
     check_norm_backward_invariants,
     check_gemm_postnorm_backward_torch,
     check_prenorm_backward_torch,
+    check_fna_backward_torch,
+    check_fna_backward_finite_differences,
+    check_fna_backward_invariants,
     check_compare,
 ]
 

@@ -61,7 +61,17 @@ def _ns(**over):
         r = np.asarray(rstd, dtype=np.float64)
         return ns.rmsnorm_backward_rows(ns.gemm(dy, w), np.asarray(x, dtype=np.float64) * r[..., None], r)
 
-    for name, fn in (("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
+    def activation_backward(s_, p, dp, act):
+        if act == "softmax":
+            return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+        return dp * ns.gelu_tanh_grad(s_)
+
+    def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
+        return _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act)
+
+    for name, fn in (("activation_backward", activation_backward),
+                     ("flash_norm_attention_backward", flash_norm_attention_backward),
+                     ("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
                      ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
                      ("jagged_attention", jagged_attention),
                      ("gemm_postnorm_backward", gemm_postnorm_backward),
@@ -126,6 +136,61 @@ def _fna(ns, q, offsets, k, v, eps_ln, eps_rms, sm_scale, act, ln_per_head=False
             y = ns.rmsnorm_rows(o.reshape(-1, H * D), eps_rms)[0].reshape(-1, H, D)
         out[r0:r1] = y + (x if res2 == "q" else ln if res2 == "ln" else 0.0)
     return out, mu_a, r1_a, r2_a
+
+
+def _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act, res1=True, res2=True,
+             dk_scaled=True, dp_from_k=False, dv_from_ds=False, rms_xhat_is_o=False, ln_xhat_raw=False):
+    """The FlashNormAttention backward from the (possibly mutated) pieces in
+    ns, with switches that plant structural mistakes."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    T, H, D = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        L = r1 - r0
+        x = q[r0:r1].reshape(L, H * D)
+        ln, _, rs1 = ns.layernorm_rows(x, eps_ln)
+        ln = ln.reshape(L, H, D)
+        s, p, o = [], [], np.empty_like(ln)
+        for h in range(H):
+            s.append((ln[:, h, :] @ k[b, :, h, :].T) * sm_scale)
+            p.append(ns.softmax_rows(s[h]) if act == "softmax" else ns.gelu_tanh(s[h]))
+            o[:, h, :] = p[h] @ v[b, :, h, :] + ln[:, h, :]
+        y, rs2 = ns.rmsnorm_rows(o.reshape(L, H * D), eps_rms)
+        g = dout[r0:r1].reshape(L, H * D)
+        do = ns.rmsnorm_backward_rows(g, o.reshape(L, H * D) if rms_xhat_is_o else y, rs2).reshape(L, H, D)
+        dln = do.copy() if res1 else np.zeros_like(do)
+        for h in range(H):
+            dp = do[:, h, :] @ (k if dp_from_k else v)[b, :, h, :].T
+            ds = ns.activation_backward(s[h], p[h], dp, act)
+            dv[b, :, h, :] = (ds if dv_from_ds else p[h]).T @ do[:, h, :]
+            dln[:, h, :] += sm_scale * ds @ k[b, :, h, :]
+            dk[b, :, h, :] = (sm_scale if dk_scaled else 1.0) * ds.T @ ln[:, h, :]
+        dx = ns.layernorm_backward_rows(dln.reshape(L, H * D), x if ln_xhat_raw else ln.reshape(L, H * D), rs1)
+        dq[r0:r1] = ((g if res2 else 0.0) + dx).reshape(L, H, D)
+    return dq, dk, dv
+
+
+def _fna_bwd_mutant(**switches):
+    def f(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
+        return _fna_bwd(F, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act, **switches)
+    return f
+
+
+def _softmax_bwd_no_row_term(s, p, dp, act):
+    if act == "softmax":
+        return p * dp
+    return F.activation_backward(s, p, dp, act)
+
+
+def _gelu_grad_first_term_only(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
 
 
 def _fna_mutant(**switches):
@@ -297,6 +362,15 @@ MUTANTS = {
     "rms_backward_subtracts_mean": dict(rmsnorm_backward_rows=_rms_bwd_with_mean),
     "rms_backward_missing_rstd": dict(rmsnorm_backward_rows=_rms_bwd_no_rstd),
     "prenorm_dx_xhat_not_rebuilt": dict(prenorm_rms_backward_dx=_prenorm_dx_raw_xhat),
+    "fna_bwd_missing_residual_1": dict(flash_norm_attention_backward=_fna_bwd_mutant(res1=False)),
+    "fna_bwd_missing_residual_2": dict(flash_norm_attention_backward=_fna_bwd_mutant(res2=False)),
+    "fna_bwd_dk_unscaled": dict(flash_norm_attention_backward=_fna_bwd_mutant(dk_scaled=False)),
+    "fna_bwd_dp_from_keys": dict(flash_norm_attention_backward=_fna_bwd_mutant(dp_from_k=True)),
+    "fna_bwd_dv_from_ds": dict(flash_norm_attention_backward=_fna_bwd_mutant(dv_from_ds=True)),
+    "fna_bwd_rms_xhat_is_its_input": dict(flash_norm_attention_backward=_fna_bwd_mutant(rms_xhat_is_o=True)),
+    "fna_bwd_ln_xhat_is_raw_x": dict(flash_norm_attention_backward=_fna_bwd_mutant(ln_xhat_raw=True)),
+    "softmax_backward_drops_row_term": dict(activation_backward=_softmax_bwd_no_row_term),
+    "gelu_grad_first_term_only": dict(gelu_tanh_grad=_gelu_grad_first_term_only),
     "jagged_kv_of_next_batch": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
         oracle, q, o, k, v, s, a, kv_batch_shift=1)),
     "jagged_scale_after_activation": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
