@@ -1,0 +1,731 @@
+// FlashNormAttention backward for gfx950, after section 4 of "Towards Free
+// Normalization: Fusing Normalization into GEMM and Attention Kernels"
+// ("Backward implementation").  Forward, for every query row x (H heads x 128):
+//   n   = LayerNorm(x) across all H*128 values      (mean mu, rstd r1 saved)
+//   s_h = n_h K_h^T * scale,  p_h = act(s_h)         (softmax or tanh GELU)
+//   o_h = p_h V_h + n_h,  y = RMSNorm(o) (rstd r2 saved),  out = y + x
+// Backward, given g = d out:
+//   do  = r2 (g - y * mean(g y))                     (RMSNorm backward)
+//   dp_h = do_h V_h^T,  ds_h = act'(dp_h) * scale
+//   dn  = do + sum_h ds_h K_h                        (first residual)
+//   dq  = g + r1 (dn - mean(dn) - n * mean(dn n))    (LayerNorm backward, second residual)
+//   dV_h = sum over the batch's rows of p_h^T do_h,  dK_h = sum of ds_h^T n_h
+// As on the page, nothing beyond the three per-row statistics is saved: n is
+// rebuilt from x, mu and r1 and the RMSNorm output as y = out - x.  The
+// softmax's row term delta = sum_keys p dp comes from the recomputed P and dP
+// (the page rebuilds the attention output for it, which here would carry the
+// bf16 output's rounding into every ds).
+//
+// Two kernels.  The norms couple all heads of a row and the key/value
+// gradients sum over all rows of a batch; a batch's dK and dV for every head
+// (512 KB in fp32) do not fit one compute unit, so:
+//  * fna_bwd_rows_kernel: one workgroup = 32 x (4/H) rows of every head (wave
+//    (g, h) owns 32 rows of head h, exactly the forward's split), so the
+//    cross-head sums are LDS exchanges.  Key and value tiles of 32 keys stream
+//    through LDS; the softmax first makes one pass for the row's log-sum-exp
+//    and delta.
+//    Writes dq, and do (fp16) and the log-sum-exp for the second kernel.
+//  * fna_bwd_kv_kernel: one workgroup per (batch, head); wave w owns keys
+//    32w .. 32w + 31 with their K, V fragments in registers and accumulates
+//    dK^T, dV^T over the batch's row blocks, whose n and do are staged in LDS.
+//    Its softmax terms are made consistent within the kernel: per row it sums
+//    (through LDS, across the four key-tile waves) L = sum_keys p and
+//    W = sum_keys p dp of its own P and dP and uses p / L and delta = W / L, so
+//    its ds sums to zero over the keys up to fp32 rounding, as the exact one
+//    does (with one key the exact dK is zero).
+//
+// Arithmetic: MFMA 32x32x16 with fp32 accumulation.  The rows kernel takes K
+// and V as stored (bf16, copied HBM -> LDS) and splits n * scale, do and ds
+// into bf16 high and low parts (x = hi + lo to about 16 significant bits; one
+// MFMA per part, as the forward does); its epilogue re-reads q and takes do in
+// fp16, so the LayerNorm backward sees them at full precision.  The key/value kernel
+// multiplies in fp16 (n, do, p and ds are O(1) quantities; K and V converted
+// from bf16, exact in the fp16 normal range).  Every 32 x 256-byte tile in LDS stores 16-byte chunk c
+// of row r at chunk c ^ swz(r % 16), swz(r) = 4 (r % 4) + (r / 4) % 4: both
+// the 16-byte fragment reads (16 rows, one chunk) and the transposing reads
+// (4 rows x 4 chunks per 16 lanes) then hit distinct banks.
+#include "fng_device.h"
+#include "fng_internal.h"
+
+namespace fng {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kKT = 32;                 // keys (or rows) per tile
+constexpr int kRowB = kD * 2;           // bytes of one head's row
+constexpr int kTileB = kKT * kRowB;     // one head's 32-row tile
+
+enum : int { ACT_SOFTMAX = 0, ACT_GELU = 1 };
+
+struct FnaBwdParams {
+  const uint16_t* Q;
+  const int32_t* off;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* O;
+  const uint16_t* dO;
+  const float* ln_mean;
+  const float* ln_rstd;
+  const float* rms_rstd;
+  uint16_t* dQ;
+  uint16_t* dK;
+  uint16_t* dV;
+  uint16_t* do16;   // [T, H, 128] fp16: the RMSNorm input gradient
+  float* lse;       // [T, H] log2-domain log-sum-exp of the scores (softmax)
+  int B, H, max_len, Skv, T;
+  int qblocks;
+  float scale;
+};
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// query/key order of an MFMA operand whose result registers must hand rows
+// 16c + 8hi + j to the next MFMA's B operand: bits 2 and 3 swapped
+__device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// tanh-form GELU through sigma = 0.5 (1 + tanh u) = 1 / (1 + 2^w),
+// u = sqrt(2/pi) (s + 0.044715 s^3), w = -2 u log2(e); with 1 - tanh^2 u =
+// 4 sigma (1 - sigma) its derivative is
+//   sigma + 2 s sigma (1 - sigma) sqrt(2/pi) (1 + 3 * 0.044715 s^2)
+constexpr float kK0 = 0.7978845608028654f;
+constexpr float kK1 = 3.0f * 0.044715f * kK0;
+constexpr float kG0 = -2.0f * kK0 * 1.4426950408889634f;
+constexpr float kG1 = kG0 * 0.044715f;
+__device__ __forceinline__ float gelu_sigma(float s) {
+  const float w = s * fmaf(kG1, s * s, kG0);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
+}
+__device__ __forceinline__ float gelu_grad(float s, float sg) {
+  return fmaf(2.0f * s * sg * (1.0f - sg), fmaf(kK1, s * s, kK0), sg);
+}
+
+__device__ __forceinline__ float f16lo(uint32_t w) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return (float)v[0];
+}
+__device__ __forceinline__ float f16hi(uint32_t w) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return (float)v[1];
+}
+
+// ---------------------------------------------------------------------------
+// rows: dq, do, log-sum-exp, delta
+// ---------------------------------------------------------------------------
+template <int H, int ACT>
+__global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
+  constexpr int G = 4 / H;                 // row groups
+  constexpr int BM = 32 * G;               // query rows per workgroup
+  constexpr int RB = H * kRowB;            // bytes per query row (all heads)
+  constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
+  constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one tile
+  constexpr int KREG = 0, VREG = KVB, XCH = 2 * KVB;
+  static_assert(XCH + BM * H * 16 <= 80 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) char smem[XCH + BM * H * 16];
+  FNG_LDS char* lds = (FNG_LDS char*)smem;
+  FNG_LDS float* xch = (FNG_LDS float*)(lds + XCH);  // [BM][H][4] per-head partial sums
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = wave % H;
+  const int g = wave / H;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const uint32_t t0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = (int)(t0 / (uint32_t)p.qblocks);
+  const int qb = (int)(t0 % (uint32_t)p.qblocks);
+  const int r0 = p.off[b];
+  const int len = min(p.off[b + 1] - r0, p.max_len);
+  if (r0 < 0 || qb * BM >= len) return;  // whole workgroup: no work in this block
+
+  const int lrow = g * 32 + l32;
+  const int qi = qb * BM + lrow;
+  const int row = r0 + qi;
+  const bool valid = qi < len && row < p.T;
+  const int brows = max(0, min(len, p.T - r0));
+  const uint32_t rbytes = (uint32_t)(brows * RB);
+  const auto qrs = make_rsrc_uniform(p.Q + (size_t)r0 * H * kD, rbytes);
+  const auto ors = make_rsrc_uniform(p.O + (size_t)r0 * H * kD, rbytes);
+  const auto grs = make_rsrc_uniform(p.dO + (size_t)r0 * H * kD, rbytes);
+  const i32x4_t kr = dma_rsrc(p.K + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
+  const i32x4_t vr = dma_rsrc(p.V + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
+
+  // key or value tile kt of every head into LDS: block j is head j / 8, keys
+  // 4 (j % 8) .. +3; position c of row r holds the row's chunk c ^ swz(r)
+  auto copy_tile = [&](bool isv, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int blk = wave * NK + i;
+      const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
+      const uint32_t src = (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2 + ((pc ^ swz(r)) * 16));
+      dma16(isv ? vr : kr, lds + (isv ? VREG : KREG) + blk * 1024, src);
+    }
+  };
+  copy_tile(false, 0);
+
+  // ---- prologue: the row's values for this head, lane layout of the MFMA B
+  // operand (lane holds d = 16kk + 8hi + 0..7 of its row) --------------------
+  const float mu = valid ? p.ln_mean[row] : 0.f;
+  const float r1 = valid ? p.ln_rstd[row] : 0.f;
+  const float r2 = valid ? p.rms_rstd[row] : 0.f;
+  const uint32_t rbase = (uint32_t)(qi * RB + h * kRowB + hi * 16);
+  float gy = 0.f;
+  {
+    u32x4_t xq[8], xo[8], xg[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      xq[kk] = buffer_load16(qrs, rbase + kk * 32);
+      xo[kk] = buffer_load16(ors, rbase + kk * 32);
+      xg[kk] = buffer_load16(grs, rbase + kk * 32);
+    }
+    // sum of g * y over this head, y = out - x (the RMSNorm output)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wq = xq[kk][e], wo = xo[kk][e], wg = xg[kk][e];
+        gy = fmaf(bf16lo(wg), bf16lo(wo) - bf16lo(wq), gy);
+        gy = fmaf(bf16hi(wg), bf16hi(wo) - bf16hi(wq), gy);
+      }
+    gy = half_swap_sum(gy);
+    if (hi == 0) xch[(lrow * H + h) * 4 + 0] = gy;
+    __syncthreads();
+    float c2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < H; ++j) c2 += xch[(lrow * H + j) * 4 + 0];
+    c2 *= 1.0f / (H * kD);
+    // do = r2 (g - y c2).  do goes to the MFMA as bf16 high and low parts and
+    // to the key/value kernel (and this kernel's epilogue) as fp16
+    u32x4_t dob[8], dol[8];
+    uint16_t* dodst = p.do16 + (size_t)row * H * kD + h * kD + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4_t df;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wq = xq[kk][e], wo = xo[kk][e], wg = xg[kk][e];
+        float d2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float x = u ? bf16hi(wq) : bf16lo(wq);
+          const float y = (u ? bf16hi(wo) : bf16lo(wo)) - x;
+          const float gv = u ? bf16hi(wg) : bf16lo(wg);
+          d2[u] = r2 * fmaf(-y, c2, gv);
+        }
+        const uint32_t hw = pack_bf16(d2[0], d2[1]);
+        dob[kk][e] = hw;
+        dol[kk][e] = pack_bf16(d2[0] - bf16lo(hw), d2[1] - bf16hi(hw));
+        df[e] = pack_f16(d2[0], d2[1]);
+      }
+      if (valid) *reinterpret_cast<u32x4_t*>(dodst + 16 * kk) = df;
+    }
+
+    // ---- the scores' B operand: n * scale (* log2 e for the softmax), bf16
+    // high and low parts --------------------------------------------------------
+    const float cq = (ACT == ACT_SOFTMAX) ? p.scale * 1.4426950408889634f : p.scale;
+    u32x4_t nb[8], nl[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wq = xq[kk][e];
+        const float a0 = (bf16lo(wq) - mu) * r1 * cq, a1 = (bf16hi(wq) - mu) * r1 * cq;
+        const uint32_t hw = pack_bf16(a0, a1);
+        nb[kk][e] = hw;
+        nl[kk][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
+      }
+
+    // ---- fragment addresses ------------------------------------------------
+    // 16-byte reads (A operand of S^T = K n^T and dP^T = V do^T): key row
+    // kappa(l32), chunk 2kk + hi
+    const int krow = kappa(l32);
+    int koff[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) koff[kk] = h * kTileB + krow * kRowB + (((2 * kk + hi) ^ swz(krow)) * 16);
+    // transposing reads (A operand of dn^T = K^T ds^T): lane (g4, li) reads
+    // key 16c + 8 (g4 / 2) + li / 4 (+4 for the second read), d = 32 dt +
+    // 16 (g4 % 2) + 4 (li % 4)
+    const int g4 = lane >> 4, li = lane & 15;
+    const int tkey = 8 * (g4 >> 1) + (li >> 2);
+    int toff[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kq = tkey + 4 * s2;
+        toff[dt][s2] = KREG + h * kTileB + kq * kRowB + (((d >> 3) ^ swz(kq)) * 16) + (d & 7) * 2;
+      }
+    }
+    const int ntiles = (p.Skv + kKT - 1) / kKT;
+
+    auto scores = [&](f32x16_t& sa, int reg) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const u32x4_t kf = lds_read16(lds + reg + koff[kk]);
+        sa = mfma_bf16(kf, nb[kk], sa);
+        sa = mfma_bf16(kf, nl[kk], sa);
+      }
+    };
+
+    auto dprod = [&](f32x16_t& dp) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const u32x4_t vf = lds_read16(lds + VREG + koff[kk]);
+        dp = mfma_bf16(vf, dob[kk], dp);
+        dp = mfma_bf16(vf, dol[kk], dp);
+      }
+    };
+
+    // ---- pass 1 (softmax): the row's log-sum-exp over all keys and the row
+    // term delta = sum_keys p dp, both accumulated online (running max m,
+    // l = sum 2^(s - m), w = sum 2^(s - m) dp; delta = w / l).  delta from the
+    // recomputed P and dP, not from the attention output rebuilt out of the
+    // bf16 forward output: that one carries the output's rounding (with one
+    // key, p = 1 and the exact ds is zero, the rebuilt one is not).
+    float lse2 = 0.f, dl = 0.f;
+    if constexpr (ACT == ACT_SOFTMAX) {
+      float mrun = -INFINITY, lrun = 0.f, wrun = 0.f;
+      for (int kt = 0; kt < ntiles; ++kt) {
+        copy_tile(true, kt);
+        wait_vmcnt<0>();
+        lds_barrier();  // K and V tile kt are in LDS
+        f32x16_t sa, dp;
+        scores(sa, KREG);
+        dprod(dp);
+        const int kvalid = p.Skv - kt * kKT;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (16 * (r >> 3) + 8 * hi + (r & 7) >= kvalid) sa[r] = -INFINITY;
+          mx = fmaxf(mx, sa[r]);
+        }
+        // a lane whose keys are all masked so far keeps mrun = -inf, l = w = 0
+        const float mnew = fmaxf(mrun, mx);
+        const float msafe = mnew == -INFINITY ? 0.f : mnew;
+        float ls = 0.f, ws = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(sa[r] - msafe);
+          ls += e;
+          ws = fmaf(e, dp[r], ws);
+        }
+        const float alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - msafe);
+        lrun = fmaf(lrun, alpha, ls);
+        wrun = fmaf(wrun, alpha, ws);
+        mrun = mnew;
+        lds_barrier();  // every wave has read K and V tile kt
+        copy_tile(false, kt + 1 < ntiles ? kt + 1 : 0);
+      }
+      const float m = half_swap_max(mrun);
+      const float a = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - m);
+      const float l = half_swap_sum(lrun * a);
+      dl = half_swap_sum(wrun * a) / l;
+      lse2 = m + __builtin_amdgcn_logf(l);  // v_log_f32: log2
+      if (valid && hi == 0) p.lse[(size_t)row * H + h] = lse2;
+    }
+
+    // ---- pass 2: dP, ds and dn^T += K^T ds^T over the key tiles -------------
+    f32x16_t dn[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dn[i][r] = 0.f;
+    for (int kt = 0; kt < ntiles; ++kt) {
+      copy_tile(true, kt);
+      wait_vmcnt<0>();
+      lds_barrier();  // K and V tile kt are in LDS
+      f32x16_t sa, dp;
+      scores(sa, KREG);
+      dprod(dp);
+      const int kvalid = p.Skv - kt * kKT;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (ACT == ACT_SOFTMAX) {
+          const float pr = (16 * (r >> 3) + 8 * hi + (r & 7) < kvalid) ? __builtin_amdgcn_exp2f(sa[r] - lse2) : 0.f;
+          ds[r] = pr * (dp[r] - dl) * p.scale;
+        } else {
+          // keys past Skv: zero V rows give dp = 0
+          ds[r] = dp[r] * gelu_grad(sa[r], gelu_sigma(sa[r])) * p.scale;
+        }
+      }
+      u32x4_t dsb[2], dsl[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = ds[8 * c + 2 * e], a1 = ds[8 * c + 2 * e + 1];
+          const uint32_t hw = pack_bf16(a0, a1);
+          dsb[c][e] = hw;
+          dsl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x2_t lo = lds_read_tr16(lds + toff[dt][0] + c * 16 * kRowB);
+          const u32x2_t hi2 = lds_read_tr16(lds + toff[dt][1] + c * 16 * kRowB);
+          const u32x4_t kf = {lo[0], lo[1], hi2[0], hi2[1]};
+          dn[dt] = mfma_bf16(kf, dsb[c], dn[dt]);
+          dn[dt] = mfma_bf16(kf, dsl[c], dn[dt]);
+        }
+      lds_barrier();  // every wave has read K and V tile kt
+      if (kt + 1 < ntiles) copy_tile(false, kt + 1);
+    }
+
+    // ---- epilogue: LayerNorm backward across heads, dq = g + dx -------------
+    // dn^T holds, in register 4 r4 + e of dn[dt], d = 32 dt + 8 r4 + 4 hi + e;
+    // swapping lane halves (v_permlane32_swap) of the 8-blocks 2kk and 2kk + 1
+    // gives the B layout d = 16kk + 8hi + j: j = e from the first result, 4 + e
+    // from the second
+    // q and the fp16 do again (L2 hits): n and do at full precision, not
+    // from the bf16 MFMA operands
+    u32x4_t dof[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      xq[kk] = buffer_load16(qrs, rbase + kk * 32);
+      dof[kk] = valid ? *reinterpret_cast<const u32x4_t*>(dodst + 16 * kk) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    float s1 = 0.f, s2 = 0.f;
+    float dnb[8][8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int m0 = 2 * kk, m1 = 2 * kk + 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(dn[m0 >> 2][4 * (m0 & 3) + e]),
+                                                         __float_as_uint(dn[m1 >> 2][4 * (m1 & 3) + e]), false, false);
+        dnb[kk][e] = __uint_as_float(sw[0]);
+        dnb[kk][4 + e] = __uint_as_float(sw[1]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wq = xq[kk][e], wd = dof[kk][e];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * e + u;
+          const float v = dnb[kk][j] + (u ? f16hi(wd) : f16lo(wd));
+          const float n = ((u ? bf16hi(wq) : bf16lo(wq)) - mu) * r1;
+          dnb[kk][j] = v;
+          s1 += v;
+          s2 = fmaf(v, n, s2);
+        }
+      }
+    }
+    s1 = half_swap_sum(s1);
+    s2 = half_swap_sum(s2);
+    if (hi == 0) {
+      xch[(lrow * H + h) * 4 + 1] = s1;
+      xch[(lrow * H + h) * 4 + 2] = s2;
+    }
+    __syncthreads();
+    float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      m1 += xch[(lrow * H + j) * 4 + 1];
+      m2 += xch[(lrow * H + j) * 4 + 2];
+    }
+    m1 *= 1.0f / (H * kD);
+    m2 *= 1.0f / (H * kD);
+    if (valid) {
+      uint16_t* dst = p.dQ + (size_t)row * H * kD + h * kD + hi * 8;
+      // dout again (an L2 hit, cheaper than holding it in 32 registers throughout)
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) xg[kk] = buffer_load16(grs, rbase + kk * 32);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wq = xq[kk][e], wg = xg[kk][e];
+          float v[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float n = ((u ? bf16hi(wq) : bf16lo(wq)) - mu) * r1;
+            const float dx = r1 * (dnb[kk][2 * e + u] - m1 - n * m2);
+            v[u] = (u ? bf16hi(wg) : bf16lo(wg)) + dx;
+          }
+          w[e] = pack_bf16(v[0], v[1]);
+        }
+        *reinterpret_cast<u32x4_t*>(dst + 16 * kk) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// keys and values: dK, dV for one (batch, head)
+// ---------------------------------------------------------------------------
+template <int ACT>
+__global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
+  constexpr int RS = 129;  // row stride (floats) of the per-(row, key) reduction arrays
+  constexpr int NREG = 0, DREG = kTileB, SREG = 2 * kTileB, RREG = SREG + 3 * 32 * 4;
+  constexpr int LDSB = ACT == ACT_SOFTMAX ? RREG + 2 * 32 * RS * 4 : RREG;
+  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
+  FNG_LDS char* lds = (FNG_LDS char*)smem;
+  FNG_LDS float* lse_s = (FNG_LDS float*)(lds + SREG);  // [32] per row: log-sum-exp
+  FNG_LDS float* il_s = lse_s + 32;                     // [32] 1 / L
+  FNG_LDS float* dl_s = lse_s + 64;                     // [32] delta = W / L
+  FNG_LDS float* red_l = (FNG_LDS float*)(lds + RREG);  // [32][RS] p of (row, key)
+  FNG_LDS float* red_w = red_l + 32 * RS;               // [32][RS] p dp
+
+  const int H = p.H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int b = (int)(blockIdx.x / (uint32_t)H);
+  const int h = (int)(blockIdx.x % (uint32_t)H);
+  const int r0 = p.off[b];
+  const int len = r0 < 0 ? 0 : max(0, min(p.off[b + 1] - r0, p.max_len));
+  const int brows = max(0, min(len, p.T - r0));
+  const int key = 32 * wave + l32;        // this lane's key (result column)
+  const bool active = 32 * wave < p.Skv;  // wave-uniform
+
+  // this wave's K and V rows as the B operand (lane: key, d = 16kk + 8hi + 0..7), fp16
+  u32x4_t kf[8], vf[8];
+  {
+    const uint32_t kvbytes = (uint32_t)(p.Skv * H * kRowB);
+    const auto krs = make_rsrc_uniform(p.K + (size_t)b * p.Skv * H * kD, kvbytes);
+    const auto vrs = make_rsrc_uniform(p.V + (size_t)b * p.Skv * H * kD, kvbytes);
+    const uint32_t base = (uint32_t)((key * H + h) * kRowB + hi * 16);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4_t a = buffer_load16(krs, base + kk * 32);
+      const u32x4_t v = buffer_load16(vrs, base + kk * 32);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[kk][e] = bf16x2_to_f16x2(a[e]);
+        vf[kk][e] = bf16x2_to_f16x2(v[e]);
+      }
+    }
+  }
+  f32x16_t dk[4], dv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[i][r] = 0.f;
+      dv[i][r] = 0.f;
+    }
+
+  // fragment addresses in the n and do tiles
+  const int arow = kappa(l32);
+  int aoff[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) aoff[kk] = arow * kRowB + (((2 * kk + hi) ^ swz(arow)) * 16);
+  const int g4 = lane >> 4, li = lane & 15;
+  const int trow = 8 * (g4 >> 1) + (li >> 2);
+  int toff[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int rq = trow + 4 * s2;
+      toff[dt][s2] = rq * kRowB + (((d >> 3) ^ swz(rq)) * 16) + (d & 7) * 2;
+    }
+  }
+  const float cq = (ACT == ACT_SOFTMAX) ? p.scale * 1.4426950408889634f : p.scale;
+
+  // staging split: thread t covers row t / 8, d = 16 (t % 8) .. + 15
+  const int srow = tid >> 3, spart = tid & 7;
+  const size_t qstride = (size_t)H * kD;
+  const int nblk = (brows + 31) / 32;
+  for (int blk = 0; blk < nblk; ++blk) {
+    {
+      const int qrow = blk * 32 + srow;
+      const bool ok = qrow < brows;
+      const size_t grow = (size_t)(r0 + (ok ? qrow : 0));
+      u32x4_t nq[2] = {}, dq[2] = {};
+      if (ok) {
+        const float mu = p.ln_mean[grow], r1 = p.ln_rstd[grow];
+        const uint16_t* qs = p.Q + grow * qstride + h * kD + spart * 16;
+        const uint16_t* ds = p.do16 + grow * qstride + h * kD + spart * 16;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
+          dq[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = x[e];
+            nq[u][e] = pack_f16((bf16lo(w) - mu) * r1, (bf16hi(w) - mu) * r1);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = srow * kRowB + (((2 * spart + u) ^ swz(srow)) * 16);
+        lds_write16(lds + NREG + pos, nq[u]);
+        lds_write16(lds + DREG + pos, dq[u]);
+      }
+      if (spart == 0) {
+        // rows past the batch: p = exp2(-inf) = 0 (softmax), n = do = 0
+        lse_s[srow] = (ok && ACT == ACT_SOFTMAX) ? p.lse[grow * H + h] : INFINITY;
+      }
+    }
+    __syncthreads();
+    // S = n K^T (rows x keys) and dP = do V^T; register r <-> row 16 (r / 8) + 8 hi + r % 8
+    f32x16_t sa, dp;
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sa[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        sa = mfma_f16(lds_read16(lds + NREG + aoff[kk]), kf[kk], sa);
+        dp = mfma_f16(lds_read16(lds + DREG + aoff[kk]), vf[kk], dp);
+      }
+    }
+    if constexpr (ACT == ACT_SOFTMAX) {
+      // p (unnormalized: exp2 of the scores less the rows kernel's log-sum-exp)
+      // and p dp of every (row, key) to LDS, then per row L and W over all keys
+      if (active) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qr = 16 * (r >> 3) + 8 * hi + (r & 7);
+          sa[r] = key < p.Skv ? __builtin_amdgcn_exp2f(sa[r] * cq - lse_s[qr]) : 0.f;
+          red_l[qr * RS + key] = sa[r];
+          red_w[qr * RS + key] = sa[r] * dp[r];
+        }
+      }
+      __syncthreads();
+      {
+        float l = 0.f, w = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = spart * 16 + i;
+          if (k < p.Skv) {
+            l += red_l[srow * RS + k];
+            w += red_w[srow * RS + k];
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+          l = xor_sum(l, m);
+          w = xor_sum(w, m);
+        }
+        if (spart == 0) {
+          const float il = l > 0.f ? 1.0f / l : 0.f;
+          il_s[srow] = il;
+          dl_s[srow] = w * il;
+        }
+      }
+      __syncthreads();
+    }
+    if (active) {
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = 16 * (r >> 3) + 8 * hi + (r & 7);
+        if constexpr (ACT == ACT_SOFTMAX) {
+          pr[r] = sa[r] * il_s[qr];
+          ds[r] = pr[r] * (dp[r] - dl_s[qr]) * p.scale;
+        } else {
+          const float s = sa[r] * cq;
+          const float sg = gelu_sigma(s);
+          pr[r] = s * sg;
+          ds[r] = dp[r] * gelu_grad(s, sg) * p.scale;
+        }
+      }
+      u32x4_t pb[2], dsb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[c][e] = pack_f16(pr[8 * c + 2 * e], pr[8 * c + 2 * e + 1]);
+          dsb[c][e] = pack_f16(ds[8 * c + 2 * e], ds[8 * c + 2 * e + 1]);
+        }
+      // dV^T += do^T P, dK^T += n^T dS (d x keys), A operands by transposing reads
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int o0 = toff[dt][0] + c * 16 * kRowB, o1 = toff[dt][1] + c * 16 * kRowB;
+          const u32x2_t a0 = lds_read_tr16(lds + DREG + o0), a1 = lds_read_tr16(lds + DREG + o1);
+          dv[dt] = mfma_f16(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb[c], dv[dt]);
+          const u32x2_t n0 = lds_read_tr16(lds + NREG + o0), n1 = lds_read_tr16(lds + NREG + o1);
+          dk[dt] = mfma_f16(u32x4_t{n0[0], n0[1], n1[0], n1[1]}, dsb[c], dk[dt]);
+        }
+    }
+    __syncthreads();  // the tiles are rewritten by the next block
+  }
+
+  // dK, dV [b, key, h, d]: register r of tile dt holds d = 32 dt + 8 (r / 4) + 4 hi + r % 4
+  if (key < p.Skv) {
+    const size_t o = (((size_t)b * p.Skv + key) * H + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * dt + 8 * r4 + 4 * hi;
+        *reinterpret_cast<u32x2_t*>(p.dK + o + d) =
+            u32x2_t{pack_bf16(dk[dt][4 * r4], dk[dt][4 * r4 + 1]), pack_bf16(dk[dt][4 * r4 + 2], dk[dt][4 * r4 + 3])};
+        *reinterpret_cast<u32x2_t*>(p.dV + o + d) =
+            u32x2_t{pack_bf16(dv[dt][4 * r4], dv[dt][4 * r4 + 1]), pack_bf16(dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3])};
+      }
+  }
+}
+
+template <int H>
+void launch_rows_h(const FnaBwdParams& p, int act, hipStream_t s) {
+  const dim3 grid((unsigned)(p.B * p.qblocks)), block(256);
+  if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_GELU>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_SOFTMAX>), grid, block, 0, s, p);
+}
+
+}  // namespace
+
+int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
+  FnaBwdParams p{};
+  p.Q = static_cast<const uint16_t*>(c.Q);
+  p.off = c.offsets;
+  p.K = static_cast<const uint16_t*>(c.K);
+  p.V = static_cast<const uint16_t*>(c.V);
+  p.O = static_cast<const uint16_t*>(c.O);
+  p.dO = static_cast<const uint16_t*>(c.dO);
+  p.ln_mean = c.ln_mean;
+  p.ln_rstd = c.ln_rstd;
+  p.rms_rstd = c.rms_rstd;
+  p.dQ = static_cast<uint16_t*>(c.dQ);
+  p.dK = static_cast<uint16_t*>(c.dK);
+  p.dV = static_cast<uint16_t*>(c.dV);
+  char* ws = static_cast<char*>(c.workspace);
+  p.do16 = reinterpret_cast<uint16_t*>(ws);
+  p.lse = reinterpret_cast<float*>(ws + (size_t)c.T * c.H * kD * 2);
+  p.B = (int)c.B;
+  p.H = (int)c.H;
+  p.max_len = (int)c.max_len;
+  p.Skv = (int)c.Skv;
+  p.T = (int)c.T;
+  p.scale = c.sm_scale;
+  const int bm = 32 * (4 / (int)c.H);
+  p.qblocks = (int)((c.max_len + bm - 1) / bm);
+  const int act = c.act == FNG_ACT_GELU ? ACT_GELU : ACT_SOFTMAX;
+  if (p.qblocks > 0 && p.T > 0) {  // else no query row: dK = dV = 0 from the second kernel alone
+    switch (c.H) {
+      case 1: launch_rows_h<1>(p, act, s); break;
+      case 2: launch_rows_h<2>(p, act, s); break;
+      case 4: launch_rows_h<4>(p, act, s); break;
+      default: return FNG_ERR_UNSUPPORTED;
+    }
+    if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
+  }
+  const dim3 grid((unsigned)(c.B * c.H)), block(256);
+  if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_GELU>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_SOFTMAX>), grid, block, 0, s, p);
+  return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
+}
+
+size_t fna_bwd_workspace_bytes(int64_t T, int64_t H) { return (size_t)(T * H) * (kD * 2 + 4); }
+
+}  // namespace fng

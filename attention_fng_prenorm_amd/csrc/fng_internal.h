@@ -85,4 +85,26 @@ struct FnaCall {
 };
 int launch_fna(const FnaCall& c, bool norm, hipStream_t s);
 
+// fng_fna_bwd.hip
+struct FnaBwdCall {
+  const void* Q;
+  const int32_t* offsets;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* ln_mean;
+  const float* ln_rstd;
+  const float* rms_rstd;
+  void* dQ;
+  void* dK;
+  void* dV;
+  void* workspace;   // fna_bwd_workspace_bytes(T, H) bytes
+  int64_t B, T, max_len, Skv, H;
+  float sm_scale;
+  int act;
+};
+int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s);
+size_t fna_bwd_workspace_bytes(int64_t T, int64_t H);
+
 }  // namespace fng

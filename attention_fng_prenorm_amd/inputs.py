@@ -23,6 +23,8 @@ sides).  "N(mu, v)" is mean and *variance*:
                       the maximum length); Q [sum of lengths, 4, 128] jagged,
                       K, V [768, 128, 4, 128] dense, all ~ N(0,1); eps_ln 1e-5,
                       eps_rms 1e-6, sm_scale 1/sqrt(128), GELU activation
+  flash_norm_attention_bwd  as flash_norm_attention (seed 1016), plus the
+                      output gradient dOut [T, 4, 128] ~ N(0,1) drawn after V
 
 Backward (section 3's fusion regrouping; shapes of the forward workloads):
   postnorm_ln_smalln_bwd   G[8192,256] ~ N(0,1), Wt[256,256] ~ N(0,1/256),
@@ -38,7 +40,7 @@ Backward (section 3's fusion regrouping; shapes of the forward workloads):
 
 Draw order inside one generator: X (row scales first when present), W,
 gamma; for attention Q, K, V; for the jagged attention the lengths, then Q,
-K, V.
+K, V (then dOut for the backward).
 """
 
 import math
@@ -69,6 +71,8 @@ WORKLOADS = {
                                    h_dist="lognormal_rows", seed=1023),
     "flash_norm_attention": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
                                  D=128, eps_ln=1e-5, eps_rms=1e-6, act="gelu", seed=1006),
+    "flash_norm_attention_bwd": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
+                                     D=128, eps_ln=1e-5, eps_rms=1e-6, act="gelu", dout=True, seed=1016),
 }
 
 
@@ -154,7 +158,10 @@ def make_jagged_attention_inputs(spec):
     q = f32_to_bf16_bits(_normal(rng, (T, H, D)))
     k = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
     v = f32_to_bf16_bits(_normal(rng, (B, Skv, H, D)))
-    return {"Q": q, "K": k, "V": v, "offsets": offsets}
+    out = {"Q": q, "K": k, "V": v, "offsets": offsets}
+    if spec.get("dout"):
+        out["dOut"] = f32_to_bf16_bits(_normal(rng, (T, H, D)))
+    return out
 
 
 def make_norm_bwd_inputs(spec):

@@ -11,9 +11,9 @@ step warmed.
 Beside it, the same JSON line carries every fused kernel of the hot path at its
 workload shape (post-LayerNorm GEMM with one workgroup across N, the affine
 pre-RMSNorm variant, post-RMSNorm GEMM with the split-N exchange and its
-two-pass fallback, the norm-sandwiched attention, and the full
-FlashNormAttention on jagged queries with short keys, and the backward by
-fusion regrouping on the same shapes) with the unfused
+two-pass fallback, the norm-sandwiched attention, the full
+FlashNormAttention on jagged queries with short keys and its backward, and the
+backward by fusion regrouping on the GEMM shapes) with the unfused
 baselines they replace, timed interleaved, and the "norm latency hidden"
 figure (T_gemm + T_norm - T_fused) / T_norm of the pages; and the pages'
 ads-shape sweep of the post-LayerNorm GEMM (M = 256k rows, K and N from 64 to
@@ -22,7 +22,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|bwd|ads|copy]
+       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|ads|copy]
 """
 
 import argparse
@@ -271,6 +271,63 @@ def main():
             "speedup_vs_unfused": round(base / t["fused"], 2),
         }
         del sets6, O6, st6, ln6, at6, y6
+
+    # ---------------- FlashNormAttention backward ---------------------------------
+    # dQ, dK, dV of the jagged FlashNormAttention from the forward's output and
+    # statistics; beside it the forward, and the separate norm/residual backward
+    # kernels an unfused chain would run on top of its attention backward
+    # (RMSNorm backward and LayerNorm backward over all heads, two residual adds)
+    if args.only in (None, "fnabwd"):
+        s7, d7 = inputs.make_inputs("flash_norm_attention_bwd")
+        Q7, K7, V7, G7 = dev(d7["Q"]), dev(d7["K"]), dev(d7["V"]), dev(d7["dOut"])
+        off7 = torch.from_numpy(d7["offsets"]).to("cuda")
+        T7, H7, D7 = Q7.shape
+        ml7 = s7["max_len"]
+        res7 = {}
+        for act in ("gelu", "softmax"):
+            sets7 = []
+            for flip in (False, True):
+                q, k, v, g = ((x.flip(0).contiguous() if flip else x) for x in (Q7, K7, V7, G7))
+                o = torch.empty_like(q)
+                st = [torch.empty(T7, dtype=torch.float32, device="cuda") for _ in range(3)]
+                B.fng_flash_norm_attention(q, off7, k, v, o, ml7, s7["eps_ln"], s7["eps_rms"], 0.0, act, *st)
+                sets7.append((q, k, v, g, o, st))
+            dQ7, dK7, dV7 = torch.empty_like(Q7), torch.empty_like(K7), torch.empty_like(V7)
+            ws7 = torch.empty(B.fng_flash_norm_attention_bwd_workspace_bytes(T7, H7), dtype=torch.uint8,
+                              device="cuda")
+            O7 = torch.empty_like(Q7)
+            tmp7 = torch.empty_like(Q7)
+            r7 = torch.ones(T7, dtype=torch.float32, device="cuda")
+
+            def bwd(i):
+                q, k, v, g, o, st = sets7[i % 2]
+                B.fng_flash_norm_attention_bwd(q, off7, k, v, o, g, st[0], st[1], st[2], dQ7, dK7, dV7, ml7,
+                                               workspace=ws7, act=act)
+
+            def fwd(i):
+                q, k, v, g, o, st = sets7[i % 2]
+                B.fng_flash_norm_attention(q, off7, k, v, O7, ml7, s7["eps_ln"], s7["eps_rms"], 0.0, act, *st)
+
+            def norms(i):
+                q, k, v, g, o, st = sets7[i % 2]
+                B.fng_rmsnorm_bwd(g.view(T7, -1), o.view(T7, -1), r7, tmp7.view(T7, -1))
+                torch.add(tmp7, q, out=dQ7)   # stands in for the first residual's add
+                B.fng_layernorm_bwd(dQ7.view(T7, -1), q.view(T7, -1), r7, tmp7.view(T7, -1))
+                torch.add(tmp7, g, out=dQ7)   # second residual
+            t = time_batches({"bwd": bwd, "fwd": fwd, "norms": norms}, args.reps, args.batch)
+            # algorithmic: read Q, out, dOut, K, V and the statistics, write dQ, dK, dV
+            bytes7 = 2.0 * (4 * T7 * H7 * D7 + 4 * s7["B"] * s7["Skv"] * H7 * D7) + 12.0 * T7
+            flops7 = 10.0 * T7 * H7 * s7["Skv"] * D7   # S again, dP, dS K, dS^T n, P^T dO
+            res7[act] = {"bwd_us": round(t["bwd"], 2), "fwd_us": round(t["fwd"], 2),
+                         "bwd_over_fwd": round(t["bwd"] / t["fwd"], 2),
+                         "norm_residual_bwd_kernels_us": round(t["norms"], 2),
+                         "bwd_gbs": round(bytes7 / t["bwd"] / 1e3, 1),
+                         "bwd_frac_hbm": round(bytes7 / t["bwd"] / 1e3 / PEAK_HBM_GBS, 4),
+                         "bwd_tflops": round(flops7 / t["bwd"] / 1e6, 1)}
+            log(f"fna backward ({act}): {t['bwd']:.1f} us (forward {t['fwd']:.1f} us; separate norm/residual "
+                f"backward kernels {t['norms']:.1f} us)")
+            del sets7, dQ7, dK7, dV7, ws7, O7, tmp7
+        kernels["flash_norm_attention_backward"] = {"T": T7, "B": s7["B"], "Skv": s7["Skv"], "H": H7, **res7}
 
     # ---------------- backward by fusion regrouping --------------------------------
     # dZ = norm_bwd(G @ Wt) fused (full-N / split-N epilogue) against the plain

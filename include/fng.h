@@ -185,9 +185,10 @@ int fng_norm_attention(const void* Q, const void* K, const void* V, void* out,
  *   the statistics buffers whatever they hold, but rows a batch owns beyond
  *   max_len_q, and rows no batch owns, are left unwritten.
  * H must be 1, 2 or 4 and D 128; Skv >= 1.  Optional fp32 [T] statistics:
- * ln mean and rstd, rms rstd.  K and V below 65504 in magnitude (fp16 MFMA
- * operands; the normalized queries are pre-multiplied by sm_scale (times
- * log2(e) for softmax) before their fp16 rounding).
+ * ln mean and rstd, rms rstd (the backward below takes them).  Products are
+ * bf16 MFMAs with fp32 accumulation: K and V as stored, the normalized
+ * queries (pre-multiplied by sm_scale, times log2(e) for softmax) and the
+ * activations split into bf16 high and low parts (about 16 significant bits).
  * ------------------------------------------------------------------------- */
 typedef enum { FNG_ACT_SOFTMAX = 0, FNG_ACT_GELU = 1 } fng_act_t;
 
@@ -197,6 +198,37 @@ int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void
                              int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
                              int64_t D, float sm_scale, float eps_ln, float eps_rms,
                              int act, void* stream);
+
+/* Backward of fng_flash_norm_attention (section 4, "Backward implementation"):
+ * given dout = d loss / d out [T, H, D], writes dQ [T, H, D] and dK, dV
+ * [B, Skv, H, D] (bf16), the exact gradients of the forward above.  As on the
+ * page only per-row statistics are kept from the forward: the LayerNorm
+ * output is rebuilt from Q, ln_mean and ln_rstd and the RMSNorm output as
+ * out - Q (out = the forward's output); the softmax's row term
+ * sum_keys P * dP comes from the recomputed scores.
+ *   Q, out, dout: [T, H, D] bf16; K, V: [B, Skv, H, D] bf16;
+ *   ln_mean, ln_rstd, rms_rstd: fp32 [T], the forward's statistics outputs;
+ *   q_offsets, B, T, max_len_q, H, D, sm_scale, act: as in the forward call.
+ * dQ rows a batch owns beyond max_len_q, and rows no batch owns, are left
+ * unwritten; those rows contribute nothing to dK and dV.  Every dK, dV entry
+ * is written (zero for batches without rows).
+ * workspace: caller-owned device memory of
+ * fng_flash_norm_attention_bwd_workspace_bytes(T, H) bytes, no initial
+ * contents needed (the first kernel writes per-row intermediates that the
+ * second reads: the gradient at the RMSNorm input in fp16, and for the
+ * softmax the log-sum-exp per (row, head)); FNG_ERR_WORKSPACE if NULL or
+ * smaller.  Limits: H 1, 2 or 4; D 128; 1 <= Skv <= 128 (the page's short-KV
+ * case: a query row's scores over all keys stay in registers).  Products are
+ * fp16 MFMAs with fp32 accumulation (K and V converted from bf16, so below
+ * 65504 in magnitude).  Two kernel launches on `stream`. */
+size_t fng_flash_norm_attention_bwd_workspace_bytes(int64_t T, int64_t H);
+int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K,
+                                 const void* V, const void* out, const void* dout,
+                                 const float* ln_mean, const float* ln_rstd,
+                                 const float* rms_rstd, void* dQ, void* dK, void* dV,
+                                 void* workspace, size_t workspace_bytes, int64_t B,
+                                 int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
+                                 int64_t D, float sm_scale, int act, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Unfused baselines (the separate kernels the fusions replace; section 1

@@ -162,6 +162,39 @@ def test_flash_norm_attention_validation(lib):
     assert j(None, None, None, None, None, 2, 0, 8, 8, 2, 128, 0.0, S, None) == B.FNG_OK
 
 
+def test_flash_norm_attention_bwd_validation(lib):
+    f = lib.fng_flash_norm_attention_bwd
+    S = B.FNG_ACT_SOFTMAX
+    need = B.fng_flash_norm_attention_bwd_workspace_bytes(16, 2)
+    assert need == 16 * 2 * (128 * 2 + 4)
+    assert B.fng_flash_norm_attention_bwd_workspace_bytes(0, 2) == 0
+
+    def call(Q=FAKE, off=FAKE, K=FAKE, V=FAKE, O=FAKE, dO=FAKE, st=FAKE, dQ=FAKE, dK=FAKE, dV=FAKE,
+             ws=FAKE, wsb=None, b=2, T=16, L=8, skv=8, H=2, D=128, scale=0.0, act=S):
+        return f(Q, off, K, V, O, dO, st, st, st, dQ, dK, dV, ws, need if wsb is None else wsb,
+                 b, T, L, skv, H, D, scale, act, None)
+
+    assert call(skv=129) == B.FNG_ERR_UNSUPPORTED        # short KV: at most 128 keys
+    assert call(D=64) == B.FNG_ERR_UNSUPPORTED
+    assert call(H=3) == B.FNG_ERR_UNSUPPORTED
+    assert call(act=7) == B.FNG_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.FNG_ERR_INVALID_ARG
+    assert call(ws=None) == B.FNG_ERR_WORKSPACE
+    assert call(wsb=need - 1) == B.FNG_ERR_WORKSPACE
+    assert call(ws=MIS) == B.FNG_ERR_MISALIGNED
+    assert call(dO=None) == B.FNG_ERR_INVALID_ARG
+    assert call(dK=None) == B.FNG_ERR_INVALID_ARG
+    assert call(st=None) == B.FNG_ERR_INVALID_ARG
+    assert call(st=FAKE + 2) == B.FNG_ERR_MISALIGNED
+    assert call(dV=MIS) == B.FNG_ERR_MISALIGNED
+    assert call(dQ=MIS) == B.FNG_ERR_MISALIGNED
+    # no batch or no head: nothing to write
+    assert call(Q=None, off=None, K=None, V=None, O=None, dO=None, dK=None, dV=None, b=0) == B.FNG_OK
+    # no query row: dK, dV still written (zeros), so they and K, V, offsets are checked
+    assert call(Q=None, O=None, dO=None, st=None, dQ=None, ws=None, T=0, dK=None) == B.FNG_ERR_INVALID_ARG
+    assert call(Q=None, O=None, dO=None, st=None, dQ=None, ws=None, T=0, K=MIS) == B.FNG_ERR_MISALIGNED
+
+
 def test_backward_validation(lib):
     # (function, whether its N and K name the product's output and reduction
     # sizes in that order: the pre-norm input gradient takes the forward's)
