@@ -20,19 +20,20 @@
 // gradients sum over all rows of a batch; a batch's dK and dV for every head
 // (512 KB in fp32) do not fit one compute unit, so:
 //  * fna_bwd_rows_kernel: one workgroup = 32 x (4/H) rows of every head (wave
-//    (g, h) owns 32 rows of head h, exactly the forward's split), so the
-//    cross-head sums are LDS exchanges.  Key and value tiles of 32 keys stream
-//    through LDS; the softmax first makes one pass for the row's log-sum-exp
-//    and delta.
+//    (g, h) owns 32 rows of head h, as in the forward), so the cross-head sums
+//    are LDS exchanges.  Key and value tiles of 32 keys stream through LDS;
+//    the softmax first makes one pass for the row's log-sum-exp and delta.
 //    Writes dq, and do (fp16) and the log-sum-exp for the second kernel.
-//  * fna_bwd_kv_kernel: one workgroup per (batch, head); wave w owns keys
-//    32w .. 32w + 31 with their K, V fragments in registers and accumulates
-//    dK^T, dV^T over the batch's row blocks, whose n and do are staged in LDS.
-//    Its softmax terms are made consistent within the kernel: per row it sums
-//    (through LDS, across the four key-tile waves) L = sum_keys p and
-//    W = sum_keys p dp of its own P and dP and uses p / L and delta = W / L, so
-//    its ds sums to zero over the keys up to fp32 rounding, as the exact one
-//    does (with one key the exact dK is zero).
+//  * fna_bwd_kv_kernel: one workgroup per (batch, head) with that head's K
+//    and V in LDS (fp16); 8 waves in two groups that take alternate 32-row
+//    blocks (one group's loads overlap the other's products); wave w of a
+//    group owns keys 32w .. 32w + 31 and accumulates dK^T, dV^T over its
+//    blocks, whose n and do are staged in LDS; the groups' sums are added at
+//    the end.  Its softmax terms are made consistent within the kernel: per
+//    row it sums L = sum_keys p and W = sum_keys p dp of its own P and dP
+//    (across the key lanes, then the four waves) and uses p / L and
+//    delta = W / L, so its ds sums to zero over the keys up to fp32 rounding,
+//    as the exact one does (with one key the exact dK is zero).
 //
 // Arithmetic: MFMA 32x32x16 with fp32 accumulation.  The rows kernel takes K
 // and V as stored (bf16, copied HBM -> LDS) and splits n * scale, do and ds
@@ -111,6 +112,11 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 // ---------------------------------------------------------------------------
 // rows: dq, do, log-sum-exp, delta
 // ---------------------------------------------------------------------------
+// rows kernel: 4 waves = (4 / H) row groups x H heads, two workgroups per CU
+// (one workgroup's copies overlap the other's products).  With four heads every
+// wave copies, and alone reads, its own head's K and V tiles, so the tile loop
+// needs no workgroup barrier: the waves only meet at the two cross-head
+// exchanges.
 template <int H, int ACT>
 __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
   constexpr int G = 4 / H;                 // row groups
@@ -118,8 +124,15 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
   constexpr int RB = H * kRowB;            // bytes per query row (all heads)
   constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
   constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one tile
-  constexpr int KREG = 0, VREG = KVB, XCH = 2 * KVB;
+  constexpr bool OWN = H == 4;             // wave w copies exactly head w's tiles
+  constexpr int XCH = 2 * KVB;
   static_assert(XCH + BM * H * 16 <= 80 * 1024, "two workgroups per CU");
+  // hand-off of the K / V tiles: workgroup barrier, or for OWN this wave's
+  // own LDS reads done (the copies' own wait is its vmcnt)
+  auto tile_sync = [&]() __attribute__((always_inline)) {
+    if constexpr (OWN) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else lds_barrier();
+  };
   __shared__ __attribute__((aligned(1024))) char smem[XCH + BM * H * 16];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
   FNG_LDS float* xch = (FNG_LDS float*)(lds + XCH);  // [BM][H][4] per-head partial sums
@@ -151,18 +164,20 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
   const i32x4_t kr = dma_rsrc(p.K + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
   const i32x4_t vr = dma_rsrc(p.V + (size_t)b * p.Skv * H * kD, (uint32_t)(p.Skv * RB));
 
-  // key or value tile kt of every head into LDS: block j is head j / 8, keys
-  // 4 (j % 8) .. +3; position c of row r holds the row's chunk c ^ swz(r)
-  auto copy_tile = [&](bool isv, int kt) __attribute__((always_inline)) {
+  // key and value tile kt of every head into LDS (K at 0, V at KVB): block j
+  // is head j / 8, keys 4 (j % 8) .. +3; position c of row r holds the row's
+  // chunk c ^ swz(r)
+  auto copy_tiles = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int blk = wave * NK + i;
       const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
       const uint32_t src = (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2 + ((pc ^ swz(r)) * 16));
-      dma16(isv ? vr : kr, lds + (isv ? VREG : KREG) + blk * 1024, src);
+      dma16(kr, lds + blk * 1024, src);
+      dma16(vr, lds + KVB + blk * 1024, src);
     }
   };
-  copy_tile(false, 0);
+  copy_tiles(0);
 
   // ---- prologue: the row's values for this head, lane layout of the MFMA B
   // operand (lane holds d = 16kk + 8hi + 0..7 of its row) --------------------
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int kq = tkey + 4 * s2;
-        toff[dt][s2] = KREG + h * kTileB + kq * kRowB + (((d >> 3) ^ swz(kq)) * 16) + (d & 7) * 2;
+        toff[dt][s2] = h * kTileB + kq * kRowB + (((d >> 3) ^ swz(kq)) * 16) + (d & 7) * 2;
       }
     }
     const int ntiles = (p.Skv + kKT - 1) / kKT;
@@ -271,12 +286,12 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       }
     };
 
-    auto dprod = [&](f32x16_t& dp) __attribute__((always_inline)) {
+    auto dprod = [&](f32x16_t& dp, int reg) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t vf = lds_read16(lds + VREG + koff[kk]);
+        const u32x4_t vf = lds_read16(lds + reg + koff[kk]);
         dp = mfma_bf16(vf, dob[kk], dp);
         dp = mfma_bf16(vf, dol[kk], dp);
       }
@@ -292,12 +307,11 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
     if constexpr (ACT == ACT_SOFTMAX) {
       float mrun = -INFINITY, lrun = 0.f, wrun = 0.f;
       for (int kt = 0; kt < ntiles; ++kt) {
-        copy_tile(true, kt);
         wait_vmcnt<0>();
-        lds_barrier();  // K and V tile kt are in LDS
+        tile_sync();  // K and V tile kt are in LDS
         f32x16_t sa, dp;
-        scores(sa, KREG);
-        dprod(dp);
+        scores(sa, 0);
+        dprod(dp, KVB);
         const int kvalid = p.Skv - kt * kKT;
         float mx = -INFINITY;
 #pragma unroll
@@ -319,8 +333,8 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
         lrun = fmaf(lrun, alpha, ls);
         wrun = fmaf(wrun, alpha, ws);
         mrun = mnew;
-        lds_barrier();  // every wave has read K and V tile kt
-        copy_tile(false, kt + 1 < ntiles ? kt + 1 : 0);
+        tile_sync();  // K and V tile kt have been read
+        copy_tiles(kt + 1 < ntiles ? kt + 1 : 0);  // the next tile, or tile 0 for the second pass
       }
       const float m = half_swap_max(mrun);
       const float a = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - m);
@@ -337,12 +351,11 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dn[i][r] = 0.f;
     for (int kt = 0; kt < ntiles; ++kt) {
-      copy_tile(true, kt);
       wait_vmcnt<0>();
-      lds_barrier();  // K and V tile kt are in LDS
+      tile_sync();  // K and V tile kt are in LDS
       f32x16_t sa, dp;
-      scores(sa, KREG);
-      dprod(dp);
+      scores(sa, 0);
+      dprod(dp, KVB);
       const int kvalid = p.Skv - kt * kKT;
       float ds[16];
 #pragma unroll
@@ -375,8 +388,8 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
           dn[dt] = mfma_bf16(kf, dsb[c], dn[dt]);
           dn[dt] = mfma_bf16(kf, dsl[c], dn[dt]);
         }
-      lds_barrier();  // every wave has read K and V tile kt
-      if (kt + 1 < ntiles) copy_tile(false, kt + 1);
+      tile_sync();  // K and V tile kt have been read
+      if (kt + 1 < ntiles) copy_tiles(kt + 1);
     }
 
     // ---- epilogue: LayerNorm backward across heads, dq = g + dx -------------
@@ -462,23 +475,41 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
 // ---------------------------------------------------------------------------
 // keys and values: dK, dV for one (batch, head)
 // ---------------------------------------------------------------------------
+// sum over the 32 key lanes (same lane half) of 16 per-row values v[r] (row
+// 16 (r / 8) + 8 hi + r % 8): a butterfly that halves the values at each step;
+// afterwards lanes l32 and l32 ^ 1 both hold the sum for register
+// j = (l32 / 2) % 16
+__device__ __forceinline__ float key_lane_sum(const float (&v)[16], int l32) {
+  float a[8], b[4], c[2];
+  const bool b4 = (l32 >> 4) & 1, b3 = (l32 >> 3) & 1, b2 = (l32 >> 2) & 1, b1 = (l32 >> 1) & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (b4 ? v[i + 8] : v[i]) + __shfl_xor(b4 ? v[i] : v[i + 8], 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (b3 ? a[i + 4] : a[i]) + __shfl_xor(b3 ? a[i] : a[i + 4], 8);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) c[i] = (b2 ? b[i + 2] : b[i]) + __shfl_xor(b2 ? b[i] : b[i + 2], 4);
+  const float d = (b1 ? c[1] : c[0]) + __shfl_xor(b1 ? c[0] : c[1], 2);
+  return d + __shfl_xor(d, 1);
+}
+
+// 8 waves = two groups of four; group q takes the row blocks q, q + 2, ...
+// and wave w of a group owns keys 32 w .. 32 w + 31.  K and V of the (batch,
+// head) sit in LDS as fp16 for the whole loop.
 template <int ACT>
-__global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
-  constexpr int RS = 129;  // row stride (floats) of the per-(row, key) reduction arrays
-  constexpr int NREG = 0, DREG = kTileB, SREG = 2 * kTileB, RREG = SREG + 3 * 32 * 4;
-  constexpr int LDSB = ACT == ACT_SOFTMAX ? RREG + 2 * 32 * RS * 4 : RREG;
-  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
+__global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
+  constexpr int KVT = 128 * kRowB;                   // K (or V) of one head, 128 keys
+  constexpr int KREG = 0, VREG = KVT;                // fp16 [key][d], rows swizzled
+  constexpr int GREG = 2 * KVT;                      // per group: n tile, do tile, row data
+  constexpr int GSZ = 2 * kTileB + 3 * 32 * 4 + 2 * 32 * 4 * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[GREG + 2 * GSZ];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
-  FNG_LDS float* lse_s = (FNG_LDS float*)(lds + SREG);  // [32] per row: log-sum-exp
-  FNG_LDS float* il_s = lse_s + 32;                     // [32] 1 / L
-  FNG_LDS float* dl_s = lse_s + 64;                     // [32] delta = W / L
-  FNG_LDS float* red_l = (FNG_LDS float*)(lds + RREG);  // [32][RS] p of (row, key)
-  FNG_LDS float* red_w = red_l + 32 * RS;               // [32][RS] p dp
 
   const int H = p.H;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, kw = wave & 3;
+  const int gtid = tid & 255;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int b = (int)(blockIdx.x / (uint32_t)H);
@@ -486,27 +517,40 @@ __global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   const int r0 = p.off[b];
   const int len = r0 < 0 ? 0 : max(0, min(p.off[b + 1] - r0, p.max_len));
   const int brows = max(0, min(len, p.T - r0));
-  const int key = 32 * wave + l32;        // this lane's key (result column)
-  const bool active = 32 * wave < p.Skv;  // wave-uniform
+  const int key = 32 * kw + l32;           // this lane's key (result column)
+  const bool active = 32 * kw < p.Skv;     // wave-uniform
 
-  // this wave's K and V rows as the B operand (lane: key, d = 16kk + 8hi + 0..7), fp16
-  u32x4_t kf[8], vf[8];
+  FNG_LDS char* gl = lds + GREG + grp * GSZ;
+  FNG_LDS char* nt = gl;                   // n tile [32 rows][128 d] fp16, swizzled
+  FNG_LDS char* dt_ = gl + kTileB;         // do tile
+  FNG_LDS float* lse_s = (FNG_LDS float*)(gl + 2 * kTileB);  // [32] log-sum-exp
+  FNG_LDS float* il_s = lse_s + 32;        // [32] 1 / L
+  FNG_LDS float* dl_s = lse_s + 64;        // [32] delta = W / L
+  FNG_LDS float* part = lse_s + 96;        // [32 rows][4 waves][2] per-wave L, W
+
+  // ---- K and V of this (batch, head) to LDS as fp16 ------------------------
   {
     const uint32_t kvbytes = (uint32_t)(p.Skv * H * kRowB);
     const auto krs = make_rsrc_uniform(p.K + (size_t)b * p.Skv * H * kD, kvbytes);
     const auto vrs = make_rsrc_uniform(p.V + (size_t)b * p.Skv * H * kD, kvbytes);
-    const uint32_t base = (uint32_t)((key * H + h) * kRowB + hi * 16);
+    const int kr_ = tid >> 2, q4 = tid & 3;  // key row, quarter of the row
+    const uint32_t base = (uint32_t)((kr_ * H + h) * kRowB + q4 * 64);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const u32x4_t a = buffer_load16(krs, base + kk * 32);
-      const u32x4_t v = buffer_load16(vrs, base + kk * 32);
+    for (int u = 0; u < 4; ++u) {
+      const u32x4_t a = buffer_load16(krs, base + u * 16);
+      const u32x4_t v = buffer_load16(vrs, base + u * 16);
+      u32x4_t ka, va;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[kk][e] = bf16x2_to_f16x2(a[e]);
-        vf[kk][e] = bf16x2_to_f16x2(v[e]);
+        ka[e] = bf16x2_to_f16x2(a[e]);
+        va[e] = bf16x2_to_f16x2(v[e]);
       }
+      const int pos = kr_ * kRowB + (((4 * q4 + u) ^ swz(kr_)) * 16);
+      lds_write16(lds + KREG + pos, ka);
+      lds_write16(lds + VREG + pos, va);
     }
   }
+
   f32x16_t dk[4], dv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -516,65 +560,84 @@ __global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
       dv[i][r] = 0.f;
     }
 
-  // fragment addresses in the n and do tiles
+  // fragment addresses: n / do tiles (A of S and dP: row kappa(l32), chunk
+  // 2kk + hi; transposing reads for dV^T, dK^T), K / V (B of S and dP: key row,
+  // chunk 2kk + hi)
   const int arow = kappa(l32);
-  int aoff[8];
+  int aoff[8], boff[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) aoff[kk] = arow * kRowB + (((2 * kk + hi) ^ swz(arow)) * 16);
+  for (int kk = 0; kk < 8; ++kk) {
+    aoff[kk] = arow * kRowB + (((2 * kk + hi) ^ swz(arow)) * 16);
+    boff[kk] = key * kRowB + (((2 * kk + hi) ^ swz(key)) * 16);
+  }
   const int g4 = lane >> 4, li = lane & 15;
   const int trow = 8 * (g4 >> 1) + (li >> 2);
   int toff[4][2];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
+  for (int d4 = 0; d4 < 4; ++d4) {
+    const int d = 32 * d4 + 16 * (g4 & 1) + 4 * (li & 3);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int rq = trow + 4 * s2;
-      toff[dt][s2] = rq * kRowB + (((d >> 3) ^ swz(rq)) * 16) + (d & 7) * 2;
+      toff[d4][s2] = rq * kRowB + (((d >> 3) ^ swz(rq)) * 16) + (d & 7) * 2;
     }
   }
   const float cq = (ACT == ACT_SOFTMAX) ? p.scale * 1.4426950408889634f : p.scale;
 
-  // staging split: thread t covers row t / 8, d = 16 (t % 8) .. + 15
-  const int srow = tid >> 3, spart = tid & 7;
+  // staging split within a group: thread covers row gtid / 8, d = 16 (gtid % 8) .. + 15
+  const int srow = gtid >> 3, spart = gtid & 7;
   const size_t qstride = (size_t)H * kD;
   const int nblk = (brows + 31) / 32;
-  for (int blk = 0; blk < nblk; ++blk) {
-    {
-      const int qrow = blk * 32 + srow;
-      const bool ok = qrow < brows;
-      const size_t grow = (size_t)(r0 + (ok ? qrow : 0));
-      u32x4_t nq[2] = {}, dq[2] = {};
-      if (ok) {
-        const float mu = p.ln_mean[grow], r1 = p.ln_rstd[grow];
-        const uint16_t* qs = p.Q + grow * qstride + h * kD + spart * 16;
-        const uint16_t* ds = p.do16 + grow * qstride + h * kD + spart * 16;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
-          dq[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = x[e];
-            nq[u][e] = pack_f16((bf16lo(w) - mu) * r1, (bf16hi(w) - mu) * r1);
-          }
-        }
-      }
+  const int npair = (nblk + 1) / 2;
+  // the next block's raw values (register prefetch)
+  u32x4_t pq[2], pd[2];
+  float pmu = 0.f, pr1 = 0.f, plse = INFINITY;
+  auto fetch = [&](int blk) __attribute__((always_inline)) {
+    const int qrow = blk * 32 + srow;
+    const bool ok = blk < nblk && qrow < brows;
+    pq[0] = pq[1] = pd[0] = pd[1] = u32x4_t{0u, 0u, 0u, 0u};
+    pmu = 0.f;
+    pr1 = 0.f;
+    plse = INFINITY;
+    if (ok) {
+      const size_t grow = (size_t)(r0 + qrow);
+      const uint16_t* qs = p.Q + grow * qstride + h * kD + spart * 16;
+      const uint16_t* ds = p.do16 + grow * qstride + h * kD + spart * 16;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int pos = srow * kRowB + (((2 * spart + u) ^ swz(srow)) * 16);
-        lds_write16(lds + NREG + pos, nq[u]);
-        lds_write16(lds + DREG + pos, dq[u]);
+        pq[u] = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
+        pd[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
       }
-      if (spart == 0) {
-        // rows past the batch: p = exp2(-inf) = 0 (softmax), n = do = 0
-        lse_s[srow] = (ok && ACT == ACT_SOFTMAX) ? p.lse[grow * H + h] : INFINITY;
-      }
+      pmu = p.ln_mean[grow];
+      pr1 = p.ln_rstd[grow];
+      if (ACT == ACT_SOFTMAX && spart == 0) plse = p.lse[grow * H + h];
     }
-    __syncthreads();
-    // S = n K^T (rows x keys) and dP = do V^T; register r <-> row 16 (r / 8) + 8 hi + r % 8
+  };
+  fetch(grp);
+
+  for (int it = 0; it < npair; ++it) {
+    const int blk = 2 * it + grp;
+    const bool has = blk < nblk;  // wave-uniform (per group)
+    // the prefetched block to the group's LDS tiles (rows past the batch are
+    // zeros, log-sum-exp +inf: p = 0)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4_t nq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = pq[u][e];
+        nq[e] = pack_f16((bf16lo(w) - pmu) * pr1, (bf16hi(w) - pmu) * pr1);
+      }
+      const int pos = srow * kRowB + (((2 * spart + u) ^ swz(srow)) * 16);
+      lds_write16(nt + pos, nq);
+      lds_write16(dt_ + pos, pd[u]);
+    }
+    if (spart == 0) lse_s[srow] = plse;
+    __syncthreads();  // tiles (and, the first time, K and V) are in LDS
+    fetch(blk + 2);   // overlaps with this block's products
+
     f32x16_t sa, dp;
-    if (active) {
+    if (has && active) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sa[r] = 0.f;
@@ -582,47 +645,45 @@ __global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
       }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        sa = mfma_f16(lds_read16(lds + NREG + aoff[kk]), kf[kk], sa);
-        dp = mfma_f16(lds_read16(lds + DREG + aoff[kk]), vf[kk], dp);
+        sa = mfma_f16(lds_read16(nt + aoff[kk]), lds_read16(lds + KREG + boff[kk]), sa);
+        dp = mfma_f16(lds_read16(dt_ + aoff[kk]), lds_read16(lds + VREG + boff[kk]), dp);
       }
     }
     if constexpr (ACT == ACT_SOFTMAX) {
-      // p (unnormalized: exp2 of the scores less the rows kernel's log-sum-exp)
-      // and p dp of every (row, key) to LDS, then per row L and W over all keys
-      if (active) {
+      // p unnormalized (the rows kernel's log-sum-exp), then per row
+      // L = sum_keys p and W = sum_keys p dp over the four waves
+      if (has && active) {
+        float ev[16], wv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qr = 16 * (r >> 3) + 8 * hi + (r & 7);
           sa[r] = key < p.Skv ? __builtin_amdgcn_exp2f(sa[r] * cq - lse_s[qr]) : 0.f;
-          red_l[qr * RS + key] = sa[r];
-          red_w[qr * RS + key] = sa[r] * dp[r];
+          ev[r] = sa[r];
+          wv[r] = sa[r] * dp[r];
+        }
+        const float ls = key_lane_sum(ev, l32), ws = key_lane_sum(wv, l32);
+        if ((l32 & 1) == 0) {
+          const int j = (l32 >> 1) & 15;
+          const int qr = 16 * (j >> 3) + 8 * hi + (j & 7);
+          part[(qr * 4 + kw) * 2 + 0] = ls;
+          part[(qr * 4 + kw) * 2 + 1] = ws;
         }
       }
       __syncthreads();
-      {
+      if (has && gtid < 32) {
         float l = 0.f, w = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = spart * 16 + i;
-          if (k < p.Skv) {
-            l += red_l[srow * RS + k];
-            w += red_w[srow * RS + k];
+        for (int k = 0; k < 4; ++k)
+          if (32 * k < p.Skv) {
+            l += part[(gtid * 4 + k) * 2 + 0];
+            w += part[(gtid * 4 + k) * 2 + 1];
           }
-        }
-#pragma unroll
-        for (int m = 1; m < 8; m <<= 1) {
-          l = xor_sum(l, m);
-          w = xor_sum(w, m);
-        }
-        if (spart == 0) {
-          const float il = l > 0.f ? 1.0f / l : 0.f;
-          il_s[srow] = il;
-          dl_s[srow] = w * il;
-        }
+        const float il = l > 0.f ? 1.0f / l : 0.f;
+        il_s[gtid] = il;
+        dl_s[gtid] = w * il;
       }
       __syncthreads();
     }
-    if (active) {
+    if (has && active) {
       float pr[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -649,30 +710,54 @@ __global__ __launch_bounds__(256, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int o0 = toff[dt][0] + c * 16 * kRowB, o1 = toff[dt][1] + c * 16 * kRowB;
-          const u32x2_t a0 = lds_read_tr16(lds + DREG + o0), a1 = lds_read_tr16(lds + DREG + o1);
-          dv[dt] = mfma_f16(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb[c], dv[dt]);
-          const u32x2_t n0 = lds_read_tr16(lds + NREG + o0), n1 = lds_read_tr16(lds + NREG + o1);
-          dk[dt] = mfma_f16(u32x4_t{n0[0], n0[1], n1[0], n1[1]}, dsb[c], dk[dt]);
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const int o0 = toff[d4][0] + c * 16 * kRowB, o1 = toff[d4][1] + c * 16 * kRowB;
+          const u32x2_t a0 = lds_read_tr16(dt_ + o0), a1 = lds_read_tr16(dt_ + o1);
+          dv[d4] = mfma_f16(u32x4_t{a0[0], a0[1], a1[0], a1[1]}, pb[c], dv[d4]);
+          const u32x2_t n0 = lds_read_tr16(nt + o0), n1 = lds_read_tr16(nt + o1);
+          dk[d4] = mfma_f16(u32x4_t{n0[0], n0[1], n1[0], n1[1]}, dsb[c], dk[d4]);
         }
     }
-    __syncthreads();  // the tiles are rewritten by the next block
+    __syncthreads();  // the tiles are rewritten by the next pair of blocks
   }
 
-  // dK, dV [b, key, h, d]: register r of tile dt holds d = 32 dt + 8 (r / 4) + 4 hi + r % 4
-  if (key < p.Skv) {
-    const size_t o = (((size_t)b * p.Skv + key) * H + h) * kD;
+  // ---- the two groups' sums, through LDS (the K / V region is free now), in
+  // two halves of d: group 1 puts out its dK, group 0 its dV; group 0 stores
+  // dK = its own + group 1's, group 1 stores dV = group 0's + its own (fixed
+  // order: bitwise reproducible)
+  const int slot = (kw * 64 + lane) * 32;  // 32 floats per lane and half, per group
+  FNG_LDS float* mine = (FNG_LDS float*)lds + grp * (256 * 32) + slot;
+  const FNG_LDS float* theirs = (FNG_LDS float*)lds + (1 - grp) * (256 * 32) + slot;
+  uint16_t* dst = (grp ? p.dV : p.dK) + (((size_t)b * p.Skv + (key < p.Skv ? key : 0)) * H + h) * kD;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the region is free (K / V, or the previous half, read)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * dt + 8 * r4 + 4 * hi;
-        *reinterpret_cast<u32x2_t*>(p.dK + o + d) =
-            u32x2_t{pack_bf16(dk[dt][4 * r4], dk[dt][4 * r4 + 1]), pack_bf16(dk[dt][4 * r4 + 2], dk[dt][4 * r4 + 3])};
-        *reinterpret_cast<u32x2_t*>(p.dV + o + d) =
-            u32x2_t{pack_bf16(dv[dt][4 * r4], dv[dt][4 * r4 + 1]), pack_bf16(dv[dt][4 * r4 + 2], dv[dt][4 * r4 + 3])};
+    for (int i = 0; i < 2; ++i) {
+      const int d4 = 2 * half + i;
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const f32x16_t& src = grp ? dk[d4] : dv[d4];
+        *reinterpret_cast<FNG_LDS f32x4_t*>(mine + i * 16 + r) = f32x4_t{src[r], src[r + 1], src[r + 2], src[r + 3]};
       }
+    }
+    __syncthreads();
+    if (key < p.Skv) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int d4 = 2 * half + i;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t o = *reinterpret_cast<const FNG_LDS f32x4_t*>(theirs + i * 16 + 4 * r4);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = grp ? o[e] + dv[d4][4 * r4 + e] : dk[d4][4 * r4 + e] + o[e];
+          // register r of tile d4 holds d = 32 d4 + 8 (r / 4) + 4 hi + r % 4
+          *reinterpret_cast<u32x2_t*>(dst + 32 * d4 + 8 * r4 + 4 * hi) =
+              u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        }
+      }
+    }
   }
 }
 
@@ -720,7 +805,7 @@ int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
     }
     if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
   }
-  const dim3 grid((unsigned)(c.B * c.H)), block(256);
+  const dim3 grid((unsigned)(c.B * c.H)), block(512);
   if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_GELU>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_SOFTMAX>), grid, block, 0, s, p);
   return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
