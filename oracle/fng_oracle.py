@@ -28,6 +28,9 @@ Readings of points the page leaves open (each also listed in the design notes):
   * LayerNorm uses the biased (population) variance and no affine, as
     torch.nn.LayerNorm does (linked from the introduction's note on affines;
     benchmarks there disable affines).
+  * lazy LayerNorm pre-norm (an extension the page rules out for lazy
+    application): the plain definition layernorm(X) @ W; the kernel applies
+    it as the rank-1 correction diag(rstd) (X W - mu colsum(W)).
   * the optional RMSNorm gain gamma multiplies after normalisation
     (y = rmsnorm(x) * gamma), then the product with W follows.
   * attention: per (batch, head) LayerNorm of each query row over head_dim,
@@ -129,6 +132,19 @@ def prenorm_rms_gemm(x, w, eps, gamma=None):
     """
     xn, r = rmsnorm_rows(x, eps, gamma)
     return xn @ np.asarray(w, dtype=np.float64), r
+
+
+def prenorm_ln_gemm(x, w, eps):
+    """Y = layernorm(X) @ W over K (no affine; the lazy LayerNorm pre-norm).
+
+    The page keeps lazy application to RMSNorm, whose elementwise part is a
+    pure row scale; LayerNorm's subtraction of the row mean is a rank-1 term,
+    layernorm(X) W = diag(rstd) (X W - mu 1^T W), which a kernel can apply
+    after the product.  The oracle is the plain definition.  Returns
+    (Y, mean[M], rstd[M]).
+    """
+    xn, mu, r = layernorm_rows(x, eps)
+    return xn @ np.asarray(w, dtype=np.float64), mu, r
 
 
 def gemm(x, w):

@@ -325,6 +325,32 @@ def check_prenorm_gemm_torch(O):
     _close(y, ref, 1e-12, "prenorm gemm vs torch fp64")
 
 
+def check_prenorm_ln_gemm(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(34)
+    # brute force on a tiny case
+    x = rng.standard_normal((4, 6)) * 1.5 + 0.7
+    w = rng.standard_normal((6, 3))
+    y, mu, r = O.prenorm_ln_gemm(x, w, 1e-4)
+    xn, bmu, br = bf_layernorm(x.tolist(), 1e-4)
+    _close(y, bf_matmul(xn, w.tolist()), 1e-13, "lazy LN pre-norm vs brute force")
+    _close(mu, bmu, 1e-14, "lazy LN mean")
+    _close(r, br, 1e-13, "lazy LN rstd")
+    # torch fp64 library routines, rows shifted far from zero mean
+    x = rng.standard_normal((20, 64)) * 2.0 + 5.0 * rng.standard_normal((20, 1))
+    w = rng.standard_normal((64, 24)) / 8.0
+    ref = (F.layer_norm(torch.from_numpy(x), (64,), eps=1e-5) @ torch.from_numpy(w)).numpy()
+    y, mu, r = O.prenorm_ln_gemm(x, w, 1e-5)
+    _close(y, ref, 1e-12, "lazy LN pre-norm vs torch fp64")
+    # the rank-1 form the kernel applies: diag(rstd) (X W - mu colsum(W))
+    rank1 = r[:, None] * (x @ w - mu[:, None] * w.sum(axis=0)[None, :])
+    _close(y, rank1, 1e-11, "lazy LN pre-norm rank-1 identity")
+    # W = I reduces it to the LayerNorm itself
+    y, _, _ = O.prenorm_ln_gemm(x[:, :24], np.eye(24), 1e-5)
+    _close(y, F.layer_norm(torch.from_numpy(x[:, :24]), (24,), eps=1e-5).numpy(), 1e-12, "lazy LN, W = I")
+
+
 def check_postnorm_bruteforce(O):
     rng = _rng(41)
     M, K, N = 3, 5, 6
@@ -769,6 +795,7 @@ ALL_CHECKS = [
     check_prenorm_gemm_bruteforce,
     check_prenorm_gemm_identities,
     check_prenorm_gemm_torch,
+    check_prenorm_ln_gemm,
     check_postnorm_bruteforce,
     check_postnorm_identities,
     check_postnorm_torch,

@@ -61,6 +61,10 @@ def _ns(**over):
         r = np.asarray(rstd, dtype=np.float64)
         return ns.rmsnorm_backward_rows(ns.gemm(dy, w), np.asarray(x, dtype=np.float64) * r[..., None], r)
 
+    def prenorm_ln_gemm(x, w, eps):
+        xn, mu, r = ns.layernorm_rows(x, eps)
+        return xn @ np.asarray(w, dtype=np.float64), mu, r
+
     def activation_backward(s_, p, dp, act):
         if act == "softmax":
             return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
@@ -69,7 +73,7 @@ def _ns(**over):
     def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
         return _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act)
 
-    for name, fn in (("activation_backward", activation_backward),
+    for name, fn in (("prenorm_ln_gemm", prenorm_ln_gemm), ("activation_backward", activation_backward),
                      ("flash_norm_attention_backward", flash_norm_attention_backward),
                      ("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
                      ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
@@ -174,6 +178,18 @@ def _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act, res1=Tr
         dx = ns.layernorm_backward_rows(dln.reshape(L, H * D), x if ln_xhat_raw else ln.reshape(L, H * D), rs1)
         dq[r0:r1] = ((g if res2 else 0.0) + dx).reshape(L, H, D)
     return dq, dk, dv
+
+
+def _ln_lazy_no_mean(x, w, eps):
+    # the row scale alone, as if LayerNorm were lazy like RMSNorm
+    xn, mu, r = F.layernorm_rows(x, eps)
+    return (np.asarray(x, dtype=np.float64) * r[:, None]) @ np.asarray(w, dtype=np.float64), mu, r
+
+
+def _ln_lazy_rank1_unscaled(x, w, eps):
+    x = np.asarray(x, dtype=np.float64); w = np.asarray(w, dtype=np.float64)
+    xn, mu, r = F.layernorm_rows(x, eps)
+    return r[:, None] * (x @ w) - mu[:, None] * w.sum(axis=0)[None, :], mu, r
 
 
 def _fna_bwd_mutant(**switches):
@@ -370,6 +386,8 @@ MUTANTS = {
     "fna_bwd_rms_xhat_is_its_input": dict(flash_norm_attention_backward=_fna_bwd_mutant(rms_xhat_is_o=True)),
     "fna_bwd_ln_xhat_is_raw_x": dict(flash_norm_attention_backward=_fna_bwd_mutant(ln_xhat_raw=True)),
     "softmax_backward_drops_row_term": dict(activation_backward=_softmax_bwd_no_row_term),
+    "ln_lazy_without_mean_correction": dict(prenorm_ln_gemm=_ln_lazy_no_mean),
+    "ln_lazy_rank1_term_unscaled": dict(prenorm_ln_gemm=_ln_lazy_rank1_unscaled),
     "gelu_grad_first_term_only": dict(gelu_tanh_grad=_gelu_grad_first_term_only),
     "jagged_kv_of_next_batch": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
         oracle, q, o, k, v, s, a, kv_batch_shift=1)),
