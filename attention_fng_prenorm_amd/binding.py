@@ -41,6 +41,8 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "fng_prenorm_rms_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp]),
     "fng_gemm_postnorm_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "fng_prenorm_ln_workspace_bytes": (_sz, [_i64, _i64]),
+    "fng_prenorm_ln_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _vp]),
     "fng_fulln_max_n": (_i64, []),
     "fng_gemm_postnorm_ln": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _int, _vp]),
     "fng_gemm_postnorm_rms": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _int, _vp]),
@@ -136,6 +138,21 @@ def fng_prenorm_rms_gemm(X, W, Y, eps, gamma=None, rstd_out=None, stream=None):
     _check("fng_prenorm_rms_gemm", lib().fng_prenorm_rms_gemm(
         _bf(X, "X"), _bf(W, "W"), _bf(gamma, "gamma"), _bf(Y, "Y"), _f(rstd_out, "rstd_out"),
         M, N, K, eps, _stream(stream)))
+
+
+def fng_prenorm_ln_workspace_bytes(N, K):
+    return int(lib().fng_prenorm_ln_workspace_bytes(N, K))
+
+
+def fng_prenorm_ln_gemm(X, W, Y, eps, workspace, mean_out=None, rstd_out=None, stream=None):
+    M, K = X.shape
+    N = W.shape[1]
+    if W.shape[0] != K or tuple(Y.shape) != (M, N):
+        raise ValueError("shapes: X [M,K], W [K,N], Y [M,N]")
+    wp, wb = _ws(workspace)
+    _check("fng_prenorm_ln_gemm", lib().fng_prenorm_ln_gemm(
+        _bf(X, "X"), _bf(W, "W"), _bf(Y, "Y"), _f(mean_out, "mean_out"), _f(rstd_out, "rstd_out"),
+        M, N, K, eps, wp, wb, _stream(stream)))
 
 
 def fng_gemm_postnorm_workspace_bytes(M, N, K, path=FNG_PATH_AUTO):

@@ -186,6 +186,23 @@ FNG_EXPORT int fng_prenorm_rms_gemm(const void* X, const void* W, const void* ga
   return fng::launch_prenorm(c, as_stream(stream));
 }
 
+FNG_EXPORT size_t fng_prenorm_ln_workspace_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)fng::prenorm_ln_parts(K) * (size_t)N * 4;
+}
+
+FNG_EXPORT int fng_prenorm_ln_gemm(const void* X, const void* W, void* Y, float* mean_out, float* rstd_out,
+                                   int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const int st = check_gemm(X, W, Y, M, N, K, eps, true);
+  if (st != FNG_OK || m_or_n_empty(M, N)) return st;
+  if ((mean_out && !aligned16(mean_out)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < fng_prenorm_ln_workspace_bytes(N, K)) return FNG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
+  GemmCall c{X, W, nullptr, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
+  return fng::launch_prenorm_ln(c, static_cast<float*>(workspace), as_stream(stream));
+}
+
 FNG_EXPORT int fng_gemm_postnorm_ln(const void* X, const void* W, void* Y, float* mean_out, float* rstd_out,
                                     int64_t M, int64_t N, int64_t K, float eps, void* workspace,
                                     size_t workspace_bytes, int path, void* stream) {

@@ -119,6 +119,18 @@ __device__ __forceinline__ void sumsq_bf16x8_2(u32x4_t v, float& a0, float& a1) 
   }
 }
 
+// the same for the plain sum (dots with ones; exact products, fp32 accumulation)
+__device__ __forceinline__ void sum_bf16x8_2(u32x4_t v, float& a0, float& a1) {
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    const bf16x2_t p = __builtin_bit_cast(bf16x2_t, w);
+    if (i % 2 == 0) a0 = __builtin_amdgcn_fdot2_f32_bf16(p, ones, a0, false);
+    else a1 = __builtin_amdgcn_fdot2_f32_bf16(p, ones, a1, false);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS access
 // ---------------------------------------------------------------------------

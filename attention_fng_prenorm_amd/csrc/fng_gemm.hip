@@ -62,6 +62,8 @@ struct GemmParams {
   int h_raw;
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
   uint32_t spin_limit;
+  const float* colsum;  // lazy LayerNorm: [cs_parts][N] partial column sums of W
+  int cs_parts;
 };
 
 // LDS layout: the W parts of all ring stages, then the X parts, then the
@@ -306,8 +308,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     float ss[SS_SLOTS][2];  // two partial sums per slot: two short dependency chains
+    float sx[SS_SLOTS][2];  // lazy LayerNorm: the plain sums
 #pragma unroll
-    for (int s = 0; s < SS_SLOTS; ++s) ss[s][0] = ss[s][1] = 0.f;
+    for (int s = 0; s < SS_SLOTS; ++s) ss[s][0] = ss[s][1] = sx[s][0] = sx[s][1] = 0.f;
 
     // one k16 slice of fragments: X rows of this wave, W columns of this wave
     // (and the matching gamma slice)
@@ -332,7 +335,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       if constexpr (EPI == EPI_PRENORM) {
         if (ss_owner) {
 #pragma unroll
-          for (int s = 0; s < SS_SLOTS; ++s) sumsq_bf16x8_2(f.x[s], ss[s][0], ss[s][1]);
+          for (int s = 0; s < SS_SLOTS; ++s) {
+            sumsq_bf16x8_2(f.x[s], ss[s][0], ss[s][1]);
+            if constexpr (LN) sum_bf16x8_2(f.x[s], sx[s][0], sx[s][1]);
+          }
         }
       }
       if constexpr (GAMMA) {
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         // the sum-of-squares dots go ahead of the slice's MFMAs: placed
         // between MFMAs they cost more (measured on gfx950, where a dot
         // issued behind an MFMA stalls the next MFMA of the wave)
-        __builtin_amdgcn_sched_group_barrier(0x002, 4 * SS_SLOTS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (LN ? 8 : 4) * SS_SLOTS, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);
       }
     };
@@ -413,18 +419,46 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 
     float rs_mean[FM], rs_rstd[FM];
     if constexpr (EPI == EPI_PRENORM) {
+      // lazy LayerNorm: mean = sum / K, var = sumsq / K - mean^2 (both sums of
+      // the raw X; the subtraction loses digits only when |mean| >> spread)
       FNG_LDS float* red = (FNG_LDS float*)lds;
 #pragma unroll
       for (int s = 0; s < SS_SLOTS; ++s) {
         const float tot = xor_sum(ss[s][0] + ss[s][1], 32);
         if (ss_owner && hi == 0) red[lrow(s)] = tot;
+        if constexpr (LN) {
+          const float t1 = xor_sum(sx[s][0] + sx[s][1], 32);
+          if (ss_owner && hi == 0) red[BM + lrow(s)] = t1;
+        }
       }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        rs_mean[i] = 0.f;
-        rs_rstd[i] = __builtin_amdgcn_rsqf(red[lrow(i)] / (float)K + p.eps);
+        if constexpr (LN) {
+          rs_mean[i] = red[BM + lrow(i)] / (float)K;
+          const float var = fmaxf(red[lrow(i)] / (float)K - rs_mean[i] * rs_mean[i], 0.f);
+          rs_rstd[i] = __builtin_amdgcn_rsqf(var + p.eps);
+        } else {
+          rs_mean[i] = 0.f;
+          rs_rstd[i] = __builtin_amdgcn_rsqf(red[lrow(i)] / (float)K + p.eps);
+        }
       }
+    }
+    // lazy LayerNorm: the column sums of W at this lane's columns, the
+    // partials merged in a fixed order
+    float csum[EPI == EPI_PRENORM && LN ? FN : 1][4][4];
+    if constexpr (EPI == EPI_PRENORM && LN) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int c = col_of(j, r4);
+          f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+          if (c < N)
+            for (int q = 0; q < p.cs_parts; ++q) v += *reinterpret_cast<const f32x4_t*>(p.colsum + (size_t)q * N + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) csum[j][r4][e] = v[e];
+        }
     }
 
     // norm backward: the saved tile (xhat or the norm's input) is in LDS in
@@ -740,7 +774,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               float a = acc[i][j][4 * r4 + e];
               // dz = rstd (g - mean(g) - xhat mean(g xhat))
               if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
-              if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
+              if constexpr (EPI == EPI_PRENORM && LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
+              else if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
               if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
               // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
               // mean, so rows whose mean dwarfs their spread keep their precision
@@ -860,16 +895,48 @@ int64_t tail_split_column(int64_t M, int64_t N) {
   return split + 0.25 < single ? nb_main * 256 : N;
 }
 
-template <int EPI, bool GAMMA>
+template <int EPI, bool GAMMA, bool LN = false>
 int launch_big(const GemmParams& p0, hipStream_t s) {
   const int64_t ns = tail_split_column(p0.M, p0.N);
   GemmParams p = p0;
   p.n_end = (int)ns;
-  int st = launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI, false, GAMMA>(p, 0, false, s);
+  int st = launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI, LN, GAMMA>(p, 0, false, s);
   if (st != FNG_OK || ns >= p0.N) return st;
   p.n_off = (int)ns;
   p.n_end = p0.N;
-  return launch<kBigBM, 128, kBigBK, kBigWM, kBigWN, EPI, false, GAMMA>(p, 0, false, s);
+  return launch<kBigBM, 128, kBigBK, kBigWM, kBigWN, EPI, LN, GAMMA>(p, 0, false, s);
+}
+
+// column sums of W [K, N] for the lazy LayerNorm, in fixed order: block
+// (x, y) sums rows [y kchunk, (y + 1) kchunk) of columns [256 x, 256 x + 256)
+// into part[y][n] (8 row lanes per column chunk, then the lanes in order)
+__global__ __launch_bounds__(256) void colsum_kernel(const uint16_t* W, float* part, int K, int N, int kchunk) {
+  __shared__ float red[8][256];
+  const int t = threadIdx.x;
+  const int c8 = t & 31, rl = t >> 5;
+  const int n = blockIdx.x * 256 + c8 * 8;
+  const int k0 = blockIdx.y * kchunk, k1 = min(K, k0 + kchunk);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (n < N) {  // N % 8 == 0: the whole 8-column chunk is in range
+#pragma unroll 4
+    for (int k = k0 + rl; k < k1; k += 8) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(W + (size_t)k * N + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = v[e];
+        acc[2 * e] += bf16lo(w);
+        acc[2 * e + 1] += bf16hi(w);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rl][c8 * 8 + j] = acc[j];
+  __syncthreads();
+  const int col = blockIdx.x * 256 + t;
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) s += red[r][t];
+  if (col < N) part[(size_t)blockIdx.y * N + col] = s;
 }
 
 }  // namespace
@@ -898,6 +965,21 @@ int launch_prenorm(const GemmCall& c, hipStream_t s) {
              : launch<64, 64, 64, 2, 2, EPI_PRENORM, false, false>(p, 0, false, s);
   }
   return g ? launch_big<EPI_PRENORM, true>(p, s) : launch_big<EPI_PRENORM, false>(p, s);
+}
+
+int prenorm_ln_parts(int64_t K) { return K >= 8 * 64 ? 8 : (int)((K + 63) / 64); }
+
+int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s) {
+  const int parts = prenorm_ln_parts(c.K);
+  const int kchunk = (int)((c.K + parts - 1) / parts);
+  hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((c.N + 255) / 256), (unsigned)parts), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(c.W), colsum, (int)c.K, (int)c.N, kchunk);
+  if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
+  GemmParams p = base_params(c);
+  p.colsum = colsum;
+  p.cs_parts = parts;
+  if (small_problem(c)) return launch<64, 64, 64, 2, 2, EPI_PRENORM, true, false>(p, 0, false, s);
+  return launch_big<EPI_PRENORM, false, true>(p, s);
 }
 
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {

@@ -27,6 +27,9 @@ struct GemmCall {
 // fng_gemm.hip
 int launch_gemm(const GemmCall& c, hipStream_t s);
 int launch_prenorm(const GemmCall& c, hipStream_t s);
+// lazy LayerNorm pre-norm: colsum receives prenorm_ln_parts(K) x N fp32 partial column sums of W
+int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s);
+int prenorm_ln_parts(int64_t K);
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s);

@@ -14,6 +14,10 @@ sides).  "N(mu, v)" is mean and *variance*:
   prenorm_rms_mlp     X[4096,4096] = exp(xi_m) * z[m,k], xi, z ~ N(0,1);
                       W[4096,14336] ~ N(0,1/4096), eps 1e-6
   prenorm_rms_mlp_gamma  as above plus gamma[4096] ~ N(1, 0.1)
+  prenorm_ln_mlp      lazy LayerNorm pre-norm (an extension, not a page workload):
+                      X[4096,4096] = exp(xi_m) * (z[m,k] + mu_m), xi, z ~ N(0,1),
+                      mu ~ N(0, 4) (rows off zero mean, |mu|/spread up to ~8);
+                      W[4096,14336] ~ N(0,1/4096), eps 1e-5
   postnorm_rms_largen X[16384,1024] ~ N(0,1), W[1024,4096] ~ N(0,1/1024),
                       eps 1e-6
   norm_attention      Q, K, V [32,1024,4,128] (BSHD) ~ N(0,1),
@@ -38,7 +42,8 @@ Backward (section 3's fusion regrouping; shapes of the forward workloads):
   The saved tensors and statistics are drawn independently of each other:
   the backward is a function of them, whatever produced them.
 
-Draw order inside one generator: X (row scales first when present), W,
+Draw order inside one generator: X (row scales, then row shifts, first when
+present), W,
 gamma; for attention Q, K, V; for the jagged attention the lengths, then Q,
 K, V (then dOut for the backward).
 """
@@ -59,6 +64,8 @@ WORKLOADS = {
                             x_dist="lognormal_rows", gamma=False, seed=1003),
     "prenorm_rms_mlp_gamma": dict(kind="prenorm_rms", M=4096, K=4096, N=14336, eps=1e-6,
                                   x_dist="lognormal_rows", gamma=True, seed=1013),
+    "prenorm_ln_mlp": dict(kind="prenorm_ln", M=4096, K=4096, N=14336, eps=1e-5,
+                           x_dist="lognormal_rows_shifted", gamma=False, seed=1024),
     "postnorm_rms_largen": dict(kind="postnorm_rms", M=16384, K=1024, N=4096, eps=1e-6,
                                 x_dist="normal", gamma=False, seed=1004),
     "norm_attention": dict(kind="norm_attention", B=32, Sq=1024, Skv=1024, H=4, D=128,
@@ -122,6 +129,10 @@ def make_gemm_inputs(spec):
     elif spec["x_dist"] == "lognormal_rows":
         s = np.exp(_normal(rng, (M, 1)))
         x = s * _normal(rng, (M, K))
+    elif spec["x_dist"] == "lognormal_rows_shifted":
+        s = np.exp(_normal(rng, (M, 1)))
+        mu = _normal(rng, (M, 1), var=spec.get("shift_var", 4.0))
+        x = s * (_normal(rng, (M, K)) + mu)
     else:
         raise ValueError(spec["x_dist"])
     w = _normal(rng, (K, N), var=1.0 / K)

@@ -10,7 +10,8 @@ step warmed.
 
 Beside it, the same JSON line carries every fused kernel of the hot path at its
 workload shape (post-LayerNorm GEMM with one workgroup across N, the affine
-pre-RMSNorm variant, post-RMSNorm GEMM with the split-N exchange and its
+pre-RMSNorm variant, the lazy LayerNorm pre-norm (an extension beyond the
+pages), post-RMSNorm GEMM with the split-N exchange and its
 two-pass fallback, the norm-sandwiched attention, the full
 FlashNormAttention on jagged queries with short keys and its backward, and the
 backward by fusion regrouping on the GEMM shapes) with the unfused
@@ -22,7 +23,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|ads|copy]
+       [--only prenorm|prenorm_gamma|prenorm_ln|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|ads|copy]
 """
 
 import argparse
@@ -158,6 +159,23 @@ def main():
             "norm": lambda i: B.fng_rmsnorm(sets[i % 2][0], Xn, eps, gamma=G0),
         }, args.reps, args.batch)
         kernels["prenorm_rms_mlp_gamma"] = summarize(t, flops, norm_bytes=4.0 * M * K)
+
+    # lazy LayerNorm pre-norm (rank-1 epilogue correction; an extension beyond
+    # the page) on the same shape, rows off zero mean, against LayerNorm + GEMM
+    if args.only in (None, "prenorm_ln"):
+        sl, dl = inputs.make_inputs("prenorm_ln_mlp")
+        XL = dev(dl["X"])
+        setsl = [(XL, sets[0][1], sets[0][2]), (XL.flip(0).contiguous(), sets[1][1], sets[1][2])]
+        wsl = torch.empty(B.fng_prenorm_ln_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
+        Xn = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+        t = time_batches({
+            "fused": lambda i: B.fng_prenorm_ln_gemm(setsl[i % 2][0], setsl[i % 2][1], setsl[i % 2][2],
+                                                     sl["eps"], wsl),
+            "gemm": lambda i: B.fng_gemm(setsl[i % 2][0], setsl[i % 2][1], setsl[i % 2][2]),
+            "norm": lambda i: B.fng_layernorm(setsl[i % 2][0], Xn, sl["eps"]),
+        }, args.reps, args.batch)
+        kernels["prenorm_ln_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K)
+        del setsl, XL, wsl
 
     del sets
     torch.cuda.empty_cache()

@@ -82,6 +82,24 @@ int fng_prenorm_rms_gemm(const void* X, const void* W, const void* gamma, void* 
                          float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
                          void* stream);
 
+/* Lazy LayerNorm pre-norm (NOT on the page, which keeps lazy application to
+ * RMSNorm because LayerNorm's elementwise part subtracts the mean): Y =
+ * layernorm(X) @ W over K (biased variance, eps inside the root, no affine),
+ * computed as diag(rstd) (X W - mean colsum(W)), a rank-1 correction in the
+ * epilogue.  The row sums and sums of squares of the raw X are accumulated
+ * beside the K loop (var = sumsq/K - mean^2, which loses digits when |mean|
+ * is much larger than the row's spread); colsum(W) comes from a separate pass
+ * over W (fixed-order fp32 partial sums).  Shapes, alignment and limits as
+ * fng_prenorm_rms_gemm; optional fp32 [M] mean_out, rstd_out.  workspace:
+ * caller-owned device memory of fng_prenorm_ln_workspace_bytes(N, K) bytes
+ * (no initial contents needed; overwritten by each call), FNG_ERR_WORKSPACE if
+ * NULL or smaller.  Two kernel launches (three with the tail split) on
+ * `stream`. */
+size_t fng_prenorm_ln_workspace_bytes(int64_t N, int64_t K);
+int fng_prenorm_ln_gemm(const void* X, const void* W, void* Y, float* mean_out,
+                        float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * GEMM + post-norm (section 1 naive fusion and section 3 multi-CTA norm):
  *   Z = X @ W  (fp32 accumulation);  Y = norm(Z) over each row of N,

@@ -162,6 +162,20 @@ def test_flash_norm_attention_validation(lib):
     assert j(None, None, None, None, None, 2, 0, 8, 8, 2, 128, 0.0, S, None) == B.FNG_OK
 
 
+def test_prenorm_ln_validation(lib):
+    f = lib.fng_prenorm_ln_gemm
+    need = B.fng_prenorm_ln_workspace_bytes(1024, 4096)
+    assert need == 8 * 1024 * 4
+    assert B.fng_prenorm_ln_workspace_bytes(1024, 100) == 2 * 1024 * 4
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 1024, 4096, 1e-5, None, 0, None) == B.FNG_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 1024, 4096, 1e-5, FAKE, need - 4, None) == B.FNG_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 1024, 4096, 1e-5, MIS, need, None) == B.FNG_ERR_MISALIGNED
+    assert f(FAKE, FAKE, FAKE, MIS, None, 4, 1024, 4096, 1e-5, FAKE, need, None) == B.FNG_ERR_MISALIGNED
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 1024, 4096, 0.0, FAKE, need, None) == B.FNG_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, None, None, 4, 1024, 12, 1e-5, FAKE, need, None) == B.FNG_ERR_MISALIGNED
+    assert f(None, None, None, None, None, 0, 1024, 4096, 1e-5, None, 0, None) == B.FNG_OK
+
+
 def test_flash_norm_attention_bwd_validation(lib):
     f = lib.fng_flash_norm_attention_bwd
     S = B.FNG_ACT_SOFTMAX
