@@ -134,6 +134,17 @@ def prenorm_rms_gemm(x, w, eps, gamma=None):
     return xn @ np.asarray(w, dtype=np.float64), r
 
 
+def gemm_postnorm_affine(x, w, eps, kind, gamma, beta=None):
+    """Y = norm(X @ W) * gamma + beta over the N axis (the post-norm with its
+    affine; section 1 notes the page's benchmarks run the norms without it).
+    gamma [N]; beta [N] or None.  Returns (Y, mean[M] or None, rstd[M])."""
+    y, mu, r = gemm_postnorm(x, w, eps, kind)
+    y = y * np.asarray(gamma, dtype=np.float64)[None, :]
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)[None, :]
+    return y, mu, r
+
+
 def prenorm_ln_gemm(x, w, eps):
     """Y = layernorm(X) @ W over K (no affine; the lazy LayerNorm pre-norm).
 

@@ -351,6 +351,29 @@ def check_prenorm_ln_gemm(O):
     _close(y, F.layer_norm(torch.from_numpy(x[:, :24]), (24,), eps=1e-5).numpy(), 1e-12, "lazy LN, W = I")
 
 
+def check_postnorm_affine(O):
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(44)
+    x = rng.standard_normal((9, 40)) + 0.6
+    w = rng.standard_normal((40, 24)) / 6.0
+    g = 1.0 + 0.3 * rng.standard_normal(24)
+    b = 0.5 * rng.standard_normal(24)
+    z = torch.from_numpy(x @ w)
+    y, _, _ = O.gemm_postnorm_affine(x, w, 1e-5, "ln", g, b)
+    _close(y, F.layer_norm(z, (24,), torch.from_numpy(g), torch.from_numpy(b), eps=1e-5).numpy(), 1e-12,
+           "post-LN affine vs torch")
+    y, _, _ = O.gemm_postnorm_affine(x, w, 1e-6, "rms", g, None)
+    _close(y, F.rms_norm(z, (24,), torch.from_numpy(g), eps=1e-6).numpy(), 1e-12, "post-RMS gain vs torch")
+    y, _, _ = O.gemm_postnorm_affine(x, w, 1e-6, "rms", g, b)
+    _close(y, (F.rms_norm(z, (24,), torch.from_numpy(g), eps=1e-6) + torch.from_numpy(b)).numpy(), 1e-12,
+           "post-RMS gain and bias vs torch")
+    # gamma = 1, beta = 0 is the plain post-norm
+    y0, _, _ = O.gemm_postnorm(x, w, 1e-5, "ln")
+    y1, _, _ = O.gemm_postnorm_affine(x, w, 1e-5, "ln", np.ones(24), np.zeros(24))
+    _close(y1, y0, 0.0, "identity affine")
+
+
 def check_postnorm_bruteforce(O):
     rng = _rng(41)
     M, K, N = 3, 5, 6
@@ -799,6 +822,7 @@ ALL_CHECKS = [
     check_postnorm_bruteforce,
     check_postnorm_identities,
     check_postnorm_torch,
+    check_postnorm_affine,
     check_attention_bruteforce,
     check_attention_torch,
     check_attention_closed_forms,

@@ -61,6 +61,11 @@ def _ns(**over):
         r = np.asarray(rstd, dtype=np.float64)
         return ns.rmsnorm_backward_rows(ns.gemm(dy, w), np.asarray(x, dtype=np.float64) * r[..., None], r)
 
+    def gemm_postnorm_affine(x, w, eps, kind, gamma, beta=None):
+        y, mu, r = gemm_postnorm(x, w, eps, kind)
+        y = y * np.asarray(gamma, dtype=np.float64)[None, :]
+        return (y + np.asarray(beta, dtype=np.float64)[None, :] if beta is not None else y), mu, r
+
     def prenorm_ln_gemm(x, w, eps):
         xn, mu, r = ns.layernorm_rows(x, eps)
         return xn @ np.asarray(w, dtype=np.float64), mu, r
@@ -73,7 +78,7 @@ def _ns(**over):
     def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
         return _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act)
 
-    for name, fn in (("prenorm_ln_gemm", prenorm_ln_gemm), ("activation_backward", activation_backward),
+    for name, fn in (("gemm_postnorm_affine", gemm_postnorm_affine), ("prenorm_ln_gemm", prenorm_ln_gemm), ("activation_backward", activation_backward),
                      ("flash_norm_attention_backward", flash_norm_attention_backward),
                      ("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
                      ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
@@ -190,6 +195,13 @@ def _ln_lazy_rank1_unscaled(x, w, eps):
     x = np.asarray(x, dtype=np.float64); w = np.asarray(w, dtype=np.float64)
     xn, mu, r = F.layernorm_rows(x, eps)
     return r[:, None] * (x @ w) - mu[:, None] * w.sum(axis=0)[None, :], mu, r
+
+
+def _affine_before_norm(x, w, eps, kind, gamma, beta=None):
+    # the gain applied to the product before the norm (which then undoes much of it)
+    z = F.gemm(x, w) * np.asarray(gamma, dtype=np.float64)[None, :]
+    y, mu, r = (F.layernorm_rows(z, eps) if kind == "ln" else (F.rmsnorm_rows(z, eps)[0], None, F.rmsnorm_rows(z, eps)[1]))
+    return (y + np.asarray(beta, dtype=np.float64)[None, :] if beta is not None else y), mu, r
 
 
 def _fna_bwd_mutant(**switches):
@@ -387,6 +399,7 @@ MUTANTS = {
     "fna_bwd_ln_xhat_is_raw_x": dict(flash_norm_attention_backward=_fna_bwd_mutant(ln_xhat_raw=True)),
     "softmax_backward_drops_row_term": dict(activation_backward=_softmax_bwd_no_row_term),
     "ln_lazy_without_mean_correction": dict(prenorm_ln_gemm=_ln_lazy_no_mean),
+    "postnorm_affine_before_norm": dict(gemm_postnorm_affine=_affine_before_norm),
     "ln_lazy_rank1_term_unscaled": dict(prenorm_ln_gemm=_ln_lazy_rank1_unscaled),
     "gelu_grad_first_term_only": dict(gelu_tanh_grad=_gelu_grad_first_term_only),
     "jagged_kv_of_next_batch": dict(jagged_attention=lambda q, o, k, v, s, a: _jagged(
