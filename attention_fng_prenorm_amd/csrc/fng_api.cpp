@@ -86,14 +86,15 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K) {
 
 int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, float* rstd_out, int64_t M,
              int64_t N, int64_t K, float eps, void* workspace, size_t workspace_bytes, int path,
-             void* stream) {
+             void* stream, const void* gamma = nullptr, const void* beta = nullptr) {
   int st = check_gemm(X, W, Y, M, N, K, eps, true);
   if (st != FNG_OK) return st;
   if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
   if (m_or_n_empty(M, N)) return FNG_OK;
   if ((mean_out && !aligned16(mean_out)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
+  if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return FNG_ERR_MISALIGNED;
   path = resolve_path(path, M, N, K);
-  GemmCall c{X, W, nullptr, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
+  GemmCall c{X, W, gamma, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr, beta};
   if (path == FNG_PATH_FULLN) {
     if (N > fng::fulln_max_n()) return FNG_ERR_UNSUPPORTED;
     return fng::launch_postnorm_fulln(c, ln, as_stream(stream));
@@ -113,7 +114,7 @@ int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, fl
   st = fng::launch_postnorm_partial(c, ln, as_stream(stream));
   if (st != FNG_OK) return st;
   return fng::launch_postnorm_finalize(Y, w.part, mean_out, rstd_out, M, N, fng::splitn_tiles_n(N),
-                                       fng::splitn_bm(), 256, eps, ln, as_stream(stream));
+                                       fng::splitn_bm(), 256, eps, ln, gamma, beta, as_stream(stream));
 }
 
 int check_attn(const void* Q, const void* K, const void* V, const void* O, int64_t B, int64_t Sq,
@@ -207,6 +208,15 @@ FNG_EXPORT int fng_gemm_postnorm_ln(const void* X, const void* W, void* Y, float
                                     int64_t M, int64_t N, int64_t K, float eps, void* workspace,
                                     size_t workspace_bytes, int path, void* stream) {
   return postnorm(true, X, W, Y, mean_out, rstd_out, M, N, K, eps, workspace, workspace_bytes, path, stream);
+}
+
+FNG_EXPORT int fng_gemm_postnorm_affine(const void* X, const void* W, const void* gamma, const void* beta,
+                                        void* Y, float* mean_out, float* rstd_out, int64_t M, int64_t N,
+                                        int64_t K, float eps, int ln, void* workspace, size_t workspace_bytes,
+                                        int path, void* stream) {
+  if (!gamma && M > 0 && N > 0) return FNG_ERR_INVALID_ARG;
+  return postnorm(ln != 0, X, W, Y, ln ? mean_out : nullptr, rstd_out, M, N, K, eps, workspace, workspace_bytes,
+                  path, stream, gamma, beta);
 }
 
 FNG_EXPORT int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, float* rstd_out, int64_t M,

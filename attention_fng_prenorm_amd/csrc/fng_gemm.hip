@@ -64,6 +64,7 @@ struct GemmParams {
   uint32_t spin_limit;
   const float* colsum;  // lazy LayerNorm: [cs_parts][N] partial column sums of W
   int cs_parts;
+  const uint16_t* beta;  // post-norm affine: bias [N] (gamma [N] is the gain), or nullptr
 };
 
 // LDS layout: the W parts of all ring stages, then the X parts, then the
@@ -127,7 +128,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   static_assert(A_PER_WAVE * NWAVES * 1024 == BM * BK * 2 && B_PER_WAVE * NWAVES * 1024 == BK * BN * 2,
                 "tile bytes split evenly over the waves");
   static_assert(NC >= 8, "BN >= 64 for the W swizzle");
-  using S = Smem<BM, BN, BK, STAGES, GAMMA>;
+  // GAMMA: with the lazy pre-norm, the RMSNorm gain folded along K (PG); with
+  // the post-norms, their affine (per-column gain and bias) in the epilogue
+  constexpr bool PG = GAMMA && EPI == EPI_PRENORM;
+  constexpr bool AFF = GAMMA && (EPI == EPI_FULLN || EPI == EPI_SPLITN);
+  static_assert(!GAMMA || PG || AFF, "GAMMA only with the lazy pre-norm or the post-norms");
+  using S = Smem<BM, BN, BK, STAGES, PG>;
   static_assert(S::BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES == 4, "the ring below is written out for 4 stages");
 
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     const i32x4_t xr = dma_rsrc(p.X + (size_t)m0 * K, xbytes);
     const i32x4_t wr = dma_rsrc(p.W + n0, (uint32_t)((int64_t)K * N * 2 - (int64_t)n0 * 2));
     i32x4_t gr;
-    if constexpr (GAMMA) gr = dma_rsrc(p.gamma, (uint32_t)K * 2);
+    if constexpr (PG) gr = dma_rsrc(p.gamma, (uint32_t)K * 2);
 
     // ---- this lane's share of each K tile's copies ------------------------
     // X: copy i of this wave fills LDS bytes [(wave*A_PER_WAVE + i) KB, +1 KB)
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         dma16(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024,
               (b_off[i] + (uint32_t)(kt * BK) * (uint32_t)N * 2u) | dead);
       }
-      if constexpr (GAMMA) {
+      if constexpr (PG) {
         if (wave == 0 && lane < KC)
           dma16(gr, lds + S::gm(s), ((uint32_t)(kt * BK + lane * 8) * 2u) | kt_live);
       }
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         const u32x2_t hi2 = lds_read_tr16(wa + 4 * (BN * 2));
         f.w[j] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
       }
-      if constexpr (GAMMA) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
+      if constexpr (PG) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
     };
     auto mma = [&](Frags& f) {
       if constexpr (EPI == EPI_PRENORM) {
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           }
         }
       }
-      if constexpr (GAMMA) {
+      if constexpr (PG) {
         // the gain multiplies along K; the lane's 8 W values and its 8 X
         // values share the same k, so it is folded into the W fragments
         // (the statistic above used the raw X)
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(f.w[j], f.x[i], acc[i][j]);
-      if constexpr (EPI == EPI_PRENORM && !GAMMA) {
+      if constexpr (EPI == EPI_PRENORM && !PG) {
         // the sum-of-squares dots go ahead of the slice's MFMAs: placed
         // between MFMAs they cost more (measured on gfx950, where a dot
         // issued behind an MFMA stalls the next MFMA of the wave)
@@ -752,6 +758,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     {
       static_assert(BM * BN * 2 <= S::BYTES, "output tile fits in the ring");
       constexpr int NCH = BN / 8;  // 16-byte chunks per tile row
+      // post-norm affine (gain and optional bias per column, applied in fp32
+      // before the single rounding): 4 bf16 of each at this lane's columns
+      u32x2_t gq[AFF ? FN : 1][4], bq[AFF ? FN : 1][4];
+      if constexpr (AFF) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = col_of(j, r4);
+            const bool in = c < N;
+            gq[j][r4] = in ? *reinterpret_cast<const u32x2_t*>(p.gamma + c) : u32x2_t{0u, 0u};
+            bq[j][r4] = (in && p.beta) ? *reinterpret_cast<const u32x2_t*>(p.beta + c) : u32x2_t{0u, 0u};
+          }
+      }
       __syncthreads();             // statistics in LDS have been read
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -776,7 +796,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
               if constexpr (EPI == EPI_PRENORM && LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
               else if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
-              if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) a = (a - rs_mean[i]) * rs_rstd[i];
+              if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) {
+                a = (a - rs_mean[i]) * rs_rstd[i];
+                if constexpr (AFF) {
+                  const uint32_t gw = gq[j][r4][e >> 1], bw = bq[j][r4][e >> 1];
+                  a = fmaf(a, (e & 1) ? bf16hi(gw) : bf16lo(gw), (e & 1) ? bf16hi(bw) : bf16lo(bw));
+                }
+              }
               // two-pass LayerNorm keeps the bf16 intermediate centred on the tile
               // mean, so rows whose mean dwarfs their spread keep their precision
               if constexpr (EPI == EPI_PARTIAL && LN) a -= rs_mean[i];
@@ -847,6 +873,7 @@ GemmParams base_params(const GemmCall& c) {
   p.Y = static_cast<uint16_t*>(c.Y);
   p.mean_out = c.mean_out;
   p.rstd_out = c.rstd_out;
+  p.beta = static_cast<const uint16_t*>(c.beta);
   p.M = (int)c.M;
   p.N = (int)c.N;
   p.K = (int)c.K;
@@ -893,6 +920,15 @@ int64_t tail_split_column(int64_t M, int64_t N) {
   const double single = (double)((tm * tn + cus - 1) / cus);
   const double split = (double)(tm * nb_main / cus) + 0.5 * (double)((2 * tm * (tn - nb_main) + cus - 1) / cus);
   return split + 0.25 < single ? nb_main * 256 : N;
+}
+
+// post-norm launches: LayerNorm or RMSNorm, with or without the affine
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI>
+int launch_norm(const GemmParams& p, bool ln, bool aff, int grid, hipStream_t s) {
+  if (ln) return aff ? launch<BM, BN, BK, WAVES_M, WAVES_N, EPI, true, true>(p, grid, false, s)
+                     : launch<BM, BN, BK, WAVES_M, WAVES_N, EPI, true, false>(p, grid, false, s);
+  return aff ? launch<BM, BN, BK, WAVES_M, WAVES_N, EPI, false, true>(p, grid, false, s)
+             : launch<BM, BN, BK, WAVES_M, WAVES_N, EPI, false, false>(p, grid, false, s);
 }
 
 template <int EPI, bool GAMMA, bool LN = false>
@@ -991,19 +1027,14 @@ int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
   // the GPU.  N <= 512: 64 x 512 (taller accumulators would not fit).
   const bool tall = c.M >= 256 * 256;
   if (tall && c.N <= 64)
-    return ln ? launch<256, 64, 64, 4, 2, EPI_FULLN, true, false>(p, 0, false, s)
-              : launch<256, 64, 64, 4, 2, EPI_FULLN, false, false>(p, 0, false, s);
+    return launch_norm<256, 64, 64, 4, 2, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   if (tall && c.N <= 128)
-    return ln ? launch<256, 128, 32, 2, 4, EPI_FULLN, true, false>(p, 0, false, s)
-              : launch<256, 128, 32, 2, 4, EPI_FULLN, false, false>(p, 0, false, s);
+    return launch_norm<256, 128, 32, 2, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   if (tall && c.N <= 256)
-    return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN, true, false>(p, 0, false, s)
-              : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN, false, false>(p, 0, false, s);
+    return launch_norm<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   if (c.N <= 256)
-    return ln ? launch<32, 256, 64, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
-              : launch<32, 256, 64, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
-  return ln ? launch<64, 512, 32, 1, 4, EPI_FULLN, true, false>(p, 0, false, s)
-            : launch<64, 512, 32, 1, 4, EPI_FULLN, false, false>(p, 0, false, s);
+    return launch_norm<32, 256, 64, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
+  return launch_norm<64, 512, 32, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
 }
 
 int splitn_feasible(int64_t M, int64_t N) {
@@ -1018,8 +1049,13 @@ int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
   p.cnt = c.cnt;
   p.done = c.done;
   p.status = c.status;
-  const int cap = ln ? max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>()
-                     : max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>();
+  // co-resident capacity of the variant that runs
+  const bool aff = c.gamma != nullptr;
+  const int cap =
+      ln ? (aff ? max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, true>()
+                : max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>())
+         : (aff ? max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, true>()
+                : max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>());
   const int tn = (int)splitn_tiles_n(c.N);
   const int total = (int)(splitn_tiles_m(c.M) * tn);
   if (cap <= 0 || tn > cap) return FNG_ERR_UNSUPPORTED;
@@ -1032,8 +1068,7 @@ int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
   // work, but costs ~19 us per call on MI355X (measured); here a peer kept
   // out by other work only delays the wait, which is bounded and reports
   // FNG_ERR_TIMEOUT through the workspace status word.
-  return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, true, false>(p, grid, false, s)
-            : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>(p, grid, false, s);
+  return launch_norm<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN>(p, ln, aff, grid, s);
 }
 
 // norm backward by regrouping: dZ = norm_bwd(G @ Wt), whole rows per

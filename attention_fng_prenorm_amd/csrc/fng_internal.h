@@ -22,6 +22,7 @@ struct GemmCall {
   uint32_t* cnt;
   uint32_t* done;
   uint32_t* status;
+  const void* beta;   // post-norm affine: bf16 [N] bias (with gamma [N] as gain), or nullptr
 };
 
 // fng_gemm.hip
@@ -56,7 +57,7 @@ int launch_rownorm(const void* X, const void* gamma, void* Y, float* mean_out, f
 // second pass of the two-pass post-norm: merge per-tile partials, normalize Y in place
 int launch_postnorm_finalize(void* Y, const void* part, float* mean_out, float* rstd_out,
                              int64_t M, int64_t N, int64_t tiles_n, int64_t bm, int64_t bn,
-                             float eps, bool ln, hipStream_t s);
+                             float eps, bool ln, const void* gamma, const void* beta, hipStream_t s);
 
 // fng_attention.hip
 struct AttnCall {

@@ -356,6 +356,8 @@ struct FinalizeParams {
   int64_t M;
   int N, tiles_n, bm, bn;
   float eps;
+  const uint16_t* gamma;  // post-norm affine gain [N] and bias [N] (each may be nullptr)
+  const uint16_t* beta;
 };
 
 template <bool LN>
@@ -396,18 +398,25 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeParams p) {
     // LayerNorm intermediates were stored minus their tile mean
     float shift = -mean;
     if constexpr (LN) shift = pb[((size_t)(col / p.bn) * p.bm + r) * 2 + 0] - mean;
+    u32x4_t g = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}, b = {0u, 0u, 0u, 0u};
+    if (p.gamma) g = *reinterpret_cast<const u32x4_t*>(p.gamma + col);
+    if (p.beta) b = *reinterpret_cast<const u32x4_t*>(p.beta + col);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = pack_bf16((bf16lo(v[e]) + shift) * rstd, (bf16hi(v[e]) + shift) * rstd);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ge = g[e], be = b[e];
+      v[e] = pack_bf16(fmaf((bf16lo(v[e]) + shift) * rstd, bf16lo(ge), bf16lo(be)),
+                       fmaf((bf16hi(v[e]) + shift) * rstd, bf16hi(ge), bf16hi(be)));
+    }
     *reinterpret_cast<u32x4_t*>(y + col) = v;
   }
 }
 
 int launch_postnorm_finalize(void* Y, const void* part, float* mean_out, float* rstd_out, int64_t M,
                              int64_t N, int64_t tiles_n, int64_t bm, int64_t bn, float eps, bool ln,
-                             hipStream_t s) {
+                             const void* gamma, const void* beta, hipStream_t s) {
   FinalizeParams p{static_cast<uint16_t*>(Y), static_cast<const float*>(part), mean_out, rstd_out, M,
-                   (int)N, (int)tiles_n, (int)bm, (int)bn, eps};
+                   (int)N, (int)tiles_n, (int)bm, (int)bn, eps, static_cast<const uint16_t*>(gamma),
+                   static_cast<const uint16_t*>(beta)};
   const int64_t grid = (M + 3) / 4;
   if (ln)
     hipLaunchKernelGGL(finalize_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, p);

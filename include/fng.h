@@ -131,6 +131,17 @@ int fng_gemm_postnorm_rms(const void* X, const void* W, void* Y, float* rstd_out
                           int64_t M, int64_t N, int64_t K, float eps, void* workspace,
                           size_t workspace_bytes, int path, void* stream);
 
+/* The post-norm with its affine: Y = norm(X @ W) * gamma + beta over N
+ * (gamma, beta bf16 [N], 16-byte aligned; beta may be NULL, gamma may not).
+ * ln != 0: LayerNorm (mean_out used), else RMSNorm (mean_out ignored).  The
+ * gain and bias are applied in fp32 in the same epilogue as the
+ * normalization, before the single bf16 rounding (in the two-pass path, in its
+ * second pass).  Paths, workspace and limits as fng_gemm_postnorm_ln. */
+int fng_gemm_postnorm_affine(const void* X, const void* W, const void* gamma,
+                             const void* beta, void* Y, float* mean_out, float* rstd_out,
+                             int64_t M, int64_t N, int64_t K, float eps, int ln,
+                             void* workspace, size_t workspace_bytes, int path, void* stream);
+
 /* Reads the status word a split-N call leaves in `workspace` (synchronizes
  * `stream`).  Returns FNG_OK, FNG_ERR_TIMEOUT, or a validation/HIP error. */
 int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream);

@@ -460,3 +460,34 @@ def test_empty_calls_are_noops():
     Q = empty_bf16(0, 8, 2, 128)
     B.fng_norm_attention(Q, empty_bf16(0, 8, 2, 128), empty_bf16(0, 8, 2, 128), Q, 1e-5, 1e-6)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# post-norm with its affine (gain and bias per column), every path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [B.FNG_PATH_FULLN, B.FNG_PATH_SPLITN, B.FNG_PATH_TWOPASS],
+                         ids=["fulln", "splitn", "twopass"])
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_postnorm_affine(kind, path):
+    M, K, N = 600, 264, 256 if path == B.FNG_PATH_FULLN else 1320
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=61)
+    rng = np.random.Generator(np.random.PCG64(62))
+    g = inputs.f32_to_bf16_bits(1.0 + 0.3 * rng.standard_normal(N).astype(np.float32))
+    b = inputs.f32_to_bf16_bits(0.5 * rng.standard_normal(N).astype(np.float32))
+    X, W, G, Bb = dev(d["X"]), dev(d["W"]), dev(g), dev(b)
+    Y = empty_bf16(M, N)
+    ws = None
+    if path != B.FNG_PATH_FULLN:
+        ws = torch.zeros(B.fng_gemm_postnorm_workspace_bytes(M, N, K, path), dtype=torch.uint8, device="cuda")
+    r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"post-{kind} affine {M}x{K}x{N} path={path}")
+    for beta in (Bb, None):
+        B.fng_gemm_postnorm_affine(X, W, Y, spec["eps"], G, beta, ln=(kind == "ln"), workspace=ws, path=path,
+                                   rstd_out=r)
+        torch.cuda.synchronize()
+        ref, _, rr = oracle.gemm_postnorm_affine(f64(d["X"]), f64(d["W"]), spec["eps"], kind, f64(g),
+                                                 f64(b) if beta is not None else None)
+        assert_parity(host(Y), ref, f"post-{kind} affine path {path} beta={beta is not None}",
+                      mae=2e-3 * max(1.0, float(np.mean(np.abs(ref))) / 0.8))
+        assert_close_stats(r.cpu().numpy(), rr, "affine rstd")
