@@ -36,10 +36,11 @@
 //    as the exact one does (with one key the exact dK is zero).
 //
 // Arithmetic: MFMA 32x32x16 with fp32 accumulation.  The rows kernel takes K
-// and V as stored (bf16, copied HBM -> LDS) and splits n * scale, do and ds
-// into bf16 high and low parts (x = hi + lo to about 16 significant bits; one
-// MFMA per part, as the forward does); its epilogue re-reads q and takes do in
-// fp16, so the LayerNorm backward sees them at full precision.  The key/value kernel
+// and V as stored (bf16, copied HBM -> LDS) and rounds n * scale, do and ds to
+// bf16, for GELU split into high and low parts (x = hi + lo to about 16
+// significant bits; one MFMA per part, as the forward does); its epilogue
+// re-reads q and takes do in fp16, so the LayerNorm backward sees them at full
+// precision.  The key/value kernel
 // multiplies in fp16 (n, do, p and ds are O(1) quantities; K and V converted
 // from bf16, exact in the fp16 normal range).  Every 32 x 256-byte tile in LDS stores 16-byte chunk c
 // of row r at chunk c ^ swz(r % 16), swz(r) = 4 (r % 4) + (r / 4) % 4: both
@@ -125,6 +126,11 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
   constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
   constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one tile
   constexpr bool OWN = H == 4;             // wave w copies exactly head w's tiles
+  // bf16 high + low parts of the computed operands for GELU, whose dS = dP
+  // GELU'(S) passes their rounding on at full weight; with the softmax the
+  // rounding reaches dS scaled by P (about 1/Skv) and single parts keep dQ
+  // within 3e-5 of the bf16 rounding floor (measured on the full workload)
+  constexpr bool SPLIT = ACT == ACT_GELU;
   constexpr int XCH = 2 * KVB;
   static_assert(XCH + BM * H * 16 <= 80 * 1024, "two workgroups per CU");
   // hand-off of the K / V tiles: workgroup barrier, or for OWN this wave's
@@ -167,17 +173,36 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
   // key and value tile kt of every head into LDS (K at 0, V at KVB): block j
   // is head j / 8, keys 4 (j % 8) .. +3; position c of row r holds the row's
   // chunk c ^ swz(r)
+  auto tile_src = [&](int kt, int i) __attribute__((always_inline)) {
+    const int blk = wave * NK + i;
+    const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
+    return (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2 + ((pc ^ swz(r)) * 16));
+  };
   auto copy_tiles = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int blk = wave * NK + i;
-      const int hd = blk / 8, r = 4 * (blk % 8) + (lane >> 4), pc = lane & 15;
-      const uint32_t src = (uint32_t)((((kt * kKT + r) * H + hd) * kD) * 2 + ((pc ^ swz(r)) * 16));
-      dma16(kr, lds + blk * 1024, src);
-      dma16(vr, lds + KVB + blk * 1024, src);
+      dma16(kr, lds + (wave * NK + i) * 1024, tile_src(kt, i));
+      dma16(vr, lds + KVB + (wave * NK + i) * 1024, tile_src(kt, i));
     }
   };
-  copy_tiles(0);
+  // four heads: each wave's own K and V slices, copied separately (V first)
+  auto copy_k = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) dma16(kr, lds + (wave * NK + i) * 1024, tile_src(kt, i));
+  };
+  auto copy_v = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) dma16(vr, lds + KVB + (wave * NK + i) * 1024, tile_src(kt, i));
+  };
+  auto copy_first = [&]() __attribute__((always_inline)) {
+    if constexpr (OWN) {
+      copy_v(0);
+      copy_k(0);
+    } else {
+      copy_tiles(0);
+    }
+  };
+  copy_first();
 
   // ---- prologue: the row's values for this head, lane layout of the MFMA B
   // operand (lane holds d = 16kk + 8hi + 0..7 of its row) --------------------
@@ -230,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
         }
         const uint32_t hw = pack_bf16(d2[0], d2[1]);
         dob[kk][e] = hw;
-        dol[kk][e] = pack_bf16(d2[0] - bf16lo(hw), d2[1] - bf16hi(hw));
+        if constexpr (SPLIT) dol[kk][e] = pack_bf16(d2[0] - bf16lo(hw), d2[1] - bf16hi(hw));
         df[e] = pack_f16(d2[0], d2[1]);
       }
       if (valid) *reinterpret_cast<u32x4_t*>(dodst + 16 * kk) = df;
@@ -248,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
         const float a0 = (bf16lo(wq) - mu) * r1 * cq, a1 = (bf16hi(wq) - mu) * r1 * cq;
         const uint32_t hw = pack_bf16(a0, a1);
         nb[kk][e] = hw;
-        nl[kk][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
+        if constexpr (SPLIT) nl[kk][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
       }
 
     // ---- fragment addresses ------------------------------------------------
@@ -282,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       for (int kk = 0; kk < 8; ++kk) {
         const u32x4_t kf = lds_read16(lds + reg + koff[kk]);
         sa = mfma_bf16(kf, nb[kk], sa);
-        sa = mfma_bf16(kf, nl[kk], sa);
+        if constexpr (SPLIT) sa = mfma_bf16(kf, nl[kk], sa);
       }
     };
 
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       for (int kk = 0; kk < 8; ++kk) {
         const u32x4_t vf = lds_read16(lds + reg + koff[kk]);
         dp = mfma_bf16(vf, dob[kk], dp);
-        dp = mfma_bf16(vf, dol[kk], dp);
+        if constexpr (SPLIT) dp = mfma_bf16(vf, dol[kk], dp);
       }
     };
 
@@ -307,11 +332,27 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
     if constexpr (ACT == ACT_SOFTMAX) {
       float mrun = -INFINITY, lrun = 0.f, wrun = 0.f;
       for (int kt = 0; kt < ntiles; ++kt) {
-        wait_vmcnt<0>();
-        tile_sync();  // K and V tile kt are in LDS
+        const bool more = kt + 1 < ntiles;
         f32x16_t sa, dp;
-        scores(sa, 0);
-        dprod(dp, KVB);
+        if constexpr (OWN) {
+          // V(kt) landed (K(kt) may still be in flight); once V(kt) is read
+          // the next V is copied, then wait for K(kt)
+          wait_vmcnt<NK>();
+          dprod(dp, KVB);
+          tile_sync();
+          if (more) {
+            copy_v(kt + 1);
+            wait_vmcnt<NK>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          scores(sa, 0);
+        } else {
+          wait_vmcnt<0>();
+          tile_sync();  // K and V tile kt are in LDS
+          scores(sa, 0);
+          dprod(dp, KVB);
+        }
         const int kvalid = p.Skv - kt * kKT;
         float mx = -INFINITY;
 #pragma unroll
@@ -333,9 +374,14 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
         lrun = fmaf(lrun, alpha, ls);
         wrun = fmaf(wrun, alpha, ws);
         mrun = mnew;
-        tile_sync();  // K and V tile kt have been read
-        copy_tiles(kt + 1 < ntiles ? kt + 1 : 0);  // the next tile, or tile 0 for the second pass
+        tile_sync();  // K (and V) tile kt have been read
+        if constexpr (OWN) {
+          if (more) copy_k(kt + 1);
+        } else {
+          if (more) copy_tiles(kt + 1);
+        }
       }
+      copy_first();  // tile 0 again for the second pass
       const float m = half_swap_max(mrun);
       const float a = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - m);
       const float l = half_swap_sum(lrun * a);
@@ -351,11 +397,25 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dn[i][r] = 0.f;
     for (int kt = 0; kt < ntiles; ++kt) {
-      wait_vmcnt<0>();
-      tile_sync();  // K and V tile kt are in LDS
+      const bool more = kt + 1 < ntiles;
       f32x16_t sa, dp;
-      scores(sa, 0);
-      dprod(dp, KVB);
+      if constexpr (OWN) {
+        wait_vmcnt<NK>();  // V(kt) landed
+        dprod(dp, KVB);
+        tile_sync();
+        if (more) {
+          copy_v(kt + 1);
+          wait_vmcnt<NK>();  // K(kt) landed
+        } else {
+          wait_vmcnt<0>();
+        }
+        scores(sa, 0);
+      } else {
+        wait_vmcnt<0>();
+        tile_sync();  // K and V tile kt are in LDS
+        scores(sa, 0);
+        dprod(dp, KVB);
+      }
       const int kvalid = p.Skv - kt * kKT;
       float ds[16];
 #pragma unroll
@@ -376,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
           const float a0 = ds[8 * c + 2 * e], a1 = ds[8 * c + 2 * e + 1];
           const uint32_t hw = pack_bf16(a0, a1);
           dsb[c][e] = hw;
-          dsl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
+          if constexpr (SPLIT) dsl[c][e] = pack_bf16(a0 - bf16lo(hw), a1 - bf16hi(hw));
         }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -386,10 +446,14 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
           const u32x2_t hi2 = lds_read_tr16(lds + toff[dt][1] + c * 16 * kRowB);
           const u32x4_t kf = {lo[0], lo[1], hi2[0], hi2[1]};
           dn[dt] = mfma_bf16(kf, dsb[c], dn[dt]);
-          dn[dt] = mfma_bf16(kf, dsl[c], dn[dt]);
+          if constexpr (SPLIT) dn[dt] = mfma_bf16(kf, dsl[c], dn[dt]);
         }
-      tile_sync();  // K and V tile kt have been read
-      if (kt + 1 < ntiles) copy_tiles(kt + 1);
+      tile_sync();  // K (and V) tile kt have been read
+      if constexpr (OWN) {
+        if (more) copy_k(kt + 1);
+      } else {
+        if (more) copy_tiles(kt + 1);
+      }
     }
 
     // ---- epilogue: LayerNorm backward across heads, dq = g + dx -------------
