@@ -564,7 +564,10 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   constexpr int KVT = 128 * kRowB;                   // K (or V) of one head, 128 keys
   constexpr int KREG = 0, VREG = KVT;                // fp16 [key][d], rows swizzled
   constexpr int GREG = 2 * KVT;                      // per group: n tile, do tile, row data
-  constexpr int GSZ = 2 * kTileB + 3 * 32 * 4 + 2 * 32 * 4 * 4;
+  // (after the loop a group's region stages half of its output tensor: 128 keys
+  // x 144-byte rows)
+  constexpr int GTILES = 2 * kTileB + 3 * 32 * 4 + 2 * 32 * 4 * 4, GOUT = 128 * 144;
+  constexpr int GSZ = GTILES > GOUT ? GTILES : GOUT;
   __shared__ __attribute__((aligned(1024))) char smem[GREG + 2 * GSZ];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
 
@@ -591,6 +594,37 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   FNG_LDS float* il_s = lse_s + 32;        // [32] 1 / L
   FNG_LDS float* dl_s = lse_s + 64;        // [32] delta = W / L
   FNG_LDS float* part = lse_s + 96;        // [32 rows][4 waves][2] per-wave L, W
+
+  // staging split within a group: thread covers row gtid / 8, d = 16 (gtid % 8) .. + 15
+  const int srow = gtid >> 3, spart = gtid & 7;
+  const size_t qstride = (size_t)H * kD;
+  const int nblk = (brows + 31) / 32;
+  const int npair = (nblk + 1) / 2;
+  // the next block's raw values (register prefetch)
+  u32x4_t pq[2], pd[2];
+  float pmu = 0.f, pr1 = 0.f, plse = INFINITY;
+  auto fetch = [&](int blk) __attribute__((always_inline)) {
+    const int qrow = blk * 32 + srow;
+    const bool ok = blk < nblk && qrow < brows;
+    pq[0] = pq[1] = pd[0] = pd[1] = u32x4_t{0u, 0u, 0u, 0u};
+    pmu = 0.f;
+    pr1 = 0.f;
+    plse = INFINITY;
+    if (ok) {
+      const size_t grow = (size_t)(r0 + qrow);
+      const uint16_t* qs = p.Q + grow * qstride + h * kD + spart * 16;
+      const uint16_t* ds = p.do16 + grow * qstride + h * kD + spart * 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        pq[u] = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
+        pd[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
+      }
+      pmu = p.ln_mean[grow];
+      pr1 = p.ln_rstd[grow];
+      if (ACT == ACT_SOFTMAX && spart == 0) plse = p.lse[grow * H + h];
+    }
+  };
+  fetch(grp);
 
   // ---- K and V of this (batch, head) to LDS as fp16 ------------------------
   {
@@ -648,36 +682,6 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   }
   const float cq = (ACT == ACT_SOFTMAX) ? p.scale * 1.4426950408889634f : p.scale;
 
-  // staging split within a group: thread covers row gtid / 8, d = 16 (gtid % 8) .. + 15
-  const int srow = gtid >> 3, spart = gtid & 7;
-  const size_t qstride = (size_t)H * kD;
-  const int nblk = (brows + 31) / 32;
-  const int npair = (nblk + 1) / 2;
-  // the next block's raw values (register prefetch)
-  u32x4_t pq[2], pd[2];
-  float pmu = 0.f, pr1 = 0.f, plse = INFINITY;
-  auto fetch = [&](int blk) __attribute__((always_inline)) {
-    const int qrow = blk * 32 + srow;
-    const bool ok = blk < nblk && qrow < brows;
-    pq[0] = pq[1] = pd[0] = pd[1] = u32x4_t{0u, 0u, 0u, 0u};
-    pmu = 0.f;
-    pr1 = 0.f;
-    plse = INFINITY;
-    if (ok) {
-      const size_t grow = (size_t)(r0 + qrow);
-      const uint16_t* qs = p.Q + grow * qstride + h * kD + spart * 16;
-      const uint16_t* ds = p.do16 + grow * qstride + h * kD + spart * 16;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pq[u] = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
-        pd[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
-      }
-      pmu = p.ln_mean[grow];
-      pr1 = p.ln_rstd[grow];
-      if (ACT == ACT_SOFTMAX && spart == 0) plse = p.lse[grow * H + h];
-    }
-  };
-  fetch(grp);
 
   for (int it = 0; it < npair; ++it) {
     const int blk = 2 * it + grp;
@@ -789,10 +793,10 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   // two halves of d: group 1 puts out its dK, group 0 its dV; group 0 stores
   // dK = its own + group 1's, group 1 stores dV = group 0's + its own (fixed
   // order: bitwise reproducible)
-  const int slot = (kw * 64 + lane) * 32;  // 32 floats per lane and half, per group
-  FNG_LDS float* mine = (FNG_LDS float*)lds + grp * (256 * 32) + slot;
-  const FNG_LDS float* theirs = (FNG_LDS float*)lds + (1 - grp) * (256 * 32) + slot;
-  uint16_t* dst = (grp ? p.dV : p.dK) + (((size_t)b * p.Skv + (key < p.Skv ? key : 0)) * H + h) * kD;
+  // per group and half: [wave][8 chunks of 4 floats][64 lanes] (consecutive
+  // lanes at consecutive 16 bytes: no bank conflicts)
+  auto xoff = [&](int g_, int i, int r) { return g_ * (256 * 32) + ((kw * 8 + i * 4 + r / 4) * 64 + lane) * 4; };
+  FNG_LDS float* xf = (FNG_LDS float*)lds;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();  // the region is free (K / V, or the previous half, read)
@@ -802,24 +806,38 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
         const f32x16_t& src = grp ? dk[d4] : dv[d4];
-        *reinterpret_cast<FNG_LDS f32x4_t*>(mine + i * 16 + r) = f32x4_t{src[r], src[r + 1], src[r + 2], src[r + 3]};
+        *reinterpret_cast<FNG_LDS f32x4_t*>(xf + xoff(grp, i, r)) = f32x4_t{src[r], src[r + 1], src[r + 2], src[r + 3]};
       }
     }
     __syncthreads();
-    if (key < p.Skv) {
+    // the sum in bf16 to this group's region, [key][64 d] with 144-byte rows
+    // (keys 16 apart land 16 banks apart), then stored as whole 16-byte chunks
+    FNG_LDS char* const stg = lds + GREG + grp * GSZ;
+    constexpr int SROW = 144;
+    static_assert(128 * SROW <= GSZ, "output staging fits the group region");
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int d4 = 2 * half + i;
+    for (int i = 0; i < 2; ++i) {
+      const int d4 = 2 * half + i;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t o = *reinterpret_cast<const FNG_LDS f32x4_t*>(theirs + i * 16 + 4 * r4);
-          float v[4];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t o = *reinterpret_cast<const FNG_LDS f32x4_t*>(xf + xoff(1 - grp, i, 4 * r4));
+        float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = grp ? o[e] + dv[d4][4 * r4 + e] : dk[d4][4 * r4 + e] + o[e];
-          // register r of tile d4 holds d = 32 d4 + 8 (r / 4) + 4 hi + r % 4
-          *reinterpret_cast<u32x2_t*>(dst + 32 * d4 + 8 * r4 + 4 * hi) =
-              u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-        }
+        for (int e = 0; e < 4; ++e) v[e] = grp ? o[e] + dv[d4][4 * r4 + e] : dk[d4][4 * r4 + e] + o[e];
+        // register r of tile d4 holds d = 32 d4 + 8 (r / 4) + 4 hi + r % 4
+        *reinterpret_cast<FNG_LDS u32x2_t*>(stg + key * SROW + (32 * i + 8 * r4 + 4 * hi) * 2) =
+            u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+    }
+    __syncthreads();
+    uint16_t* const out = grp ? p.dV : p.dK;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ch = gtid + 256 * c;  // 128 keys x 8 chunks of 16 bytes
+      const int k = ch >> 3, q = ch & 7;
+      if (k < p.Skv) {
+        const u32x4_t v = *reinterpret_cast<const FNG_LDS u32x4_t*>(stg + k * SROW + q * 16);
+        *reinterpret_cast<u32x4_t*>(out + (((size_t)b * p.Skv + k) * H + h) * kD + 64 * half + 8 * q) = v;
       }
     }
   }
