@@ -26,10 +26,12 @@
 // norm epilogues inside a lane plus one lane-pair exchange.
 //
 // Staging: X and W tiles are copied HBM -> LDS directly (buffer_load ... lds,
-// out-of-range rows and tails read as 0) through a 4-stage ring with one
-// barrier per K tile.  X is kept [m][k] (k contiguous) and read with
-// ds_read_b128; W is kept [k][n] exactly as in memory and read k-contiguous per
-// lane with ds_read_b64_tr_b16.  16-byte chunks are XOR-swizzled per row so
+// out-of-range rows and tails read as 0) through a 4-stage ring.  The 8-wave
+// tiles run a ping-pong schedule: the two waves of each SIMD alternate
+// between reading a K tile's fragments and multiplying them, two barriers
+// per K tile; the other tiles use one barrier per K tile.  X is kept [m][k]
+// (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as in
+// memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte chunks are XOR-swizzled per row so
 // fragment reads are bank-conflict free.
 #include "fng_device.h"
 #include "fng_internal.h"
@@ -141,6 +143,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   // keeps its row reductions in an extra region after it
   constexpr bool IS_BWD = EPI == EPI_BWD_FULLN || EPI == EPI_BWD_SPLITN;
   constexpr bool IS_SPLIT = EPI == EPI_SPLITN || EPI == EPI_BWD_SPLITN;
+  // ping-pong mainloop: 8 waves in two row halves, two k16 slices per K tile.
+  // The backward keeps the single-phase loop (its last refills bring in the
+  // saved tile over all four stages), and so does the lazy pre-norm with the
+  // gain: its fold (about 50 vector instructions per slice) would make the
+  // memory phase the longer one (measured slower).
+  constexpr bool PP = NWAVES == 8 && WAVES_M == 2 && BK == 32 && !IS_BWD && !PG && EPI != EPI_SPLITN;
   constexpr int RED = IS_BWD ? S::BYTES : 0;
   constexpr int EXTRA = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
   static_assert(S::BYTES + EXTRA <= 160 * 1024, "LDS budget with the backward's reductions");
@@ -337,6 +345,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       }
       if constexpr (PG) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
     };
+    // the vector work on one slice's fragments (ping-pong memory phase)
+    auto vec = [&](Frags& f) {
+      if constexpr (EPI == EPI_PRENORM) {
+        if (ss_owner) {
+#pragma unroll
+          for (int s = 0; s < SS_SLOTS; ++s) {
+            sumsq_bf16x8_2(f.x[s], ss[s][0], ss[s][1]);
+            if constexpr (LN) sum_bf16x8_2(f.x[s], sx[s][0], sx[s][1]);
+          }
+        }
+      }
+      if constexpr (PG) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f.w[j][e] = pack_bf16(bf16lo(f.w[j][e]) * bf16lo(f.g[e]), bf16hi(f.w[j][e]) * bf16hi(f.g[e]));
+      }
+    };
+    auto mfmas = [&](Frags& f) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(f.w[j], f.x[i], acc[i][j]);
+    };
     auto mma = [&](Frags& f) {
       if constexpr (EPI == EPI_PRENORM) {
         if (ss_owner) {
@@ -399,19 +432,73 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       else { Frags fc; load(next, 0, fc); fence(); mma(fa); fence(); fa = fc; }
     };
     __syncthreads();  // the previous tile's epilogue may still read LDS
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    issue(3, 3);
-    wait_vmcnt<3 * LOADS>();
-    lds_barrier();
-    Frags fr;
-    load(0, 0, fr);
-    for (int kt = 0; kt < ktiles; kt += 4) {
-      step(kt, 0, 1, fr);
-      if (kt + 1 < ktiles) step(kt + 1, 1, 2, fr);
-      if (kt + 2 < ktiles) step(kt + 2, 2, 3, fr);
-      if (kt + 3 < ktiles) step(kt + 3, 3, 0, fr);
+    if constexpr (PP) {
+      // Ping-pong: the two waves of each SIMD (one per row half) alternate
+      // between a memory phase M(t) -- read all of K tile t's fragments,
+      // issue the copies of tile t+3 into the stage tile t-1 used, wait until
+      // this wave's copies of tile t+1 have landed, and the vector work on
+      // the fragments (sums of squares, the gain fold) -- and a compute
+      // phase C(t) of the tile's MFMAs back to back.  The row-half-0 waves
+      // run M(t) while the row-half-1 waves run C(t-1), then the roles swap;
+      // a workgroup barrier separates the phases, so the matrix core of a
+      // SIMD is fed by one wave while the other waits on LDS.
+      //   stage reuse: tile t-1's stage is refilled in M(t), after the
+      //   barrier that ends both halves' reads of tile t-1;
+      //   data: every wave has waited for its copies of tile t+1 before the
+      //   barrier that precedes the first read of tile t+1.
+      Frags f0, f1;
+      const bool first = wm == 0;
+      auto mem = [&](int t) {
+        const int st = t & 3;
+        load(st, 0, f0);
+        load(st, 1, f1);
+        issue(t + 3, (t + 3) & 3);
+        wait_vmcnt<2 * LOADS>();
+        // the sums of squares wait for their fragments: after the copies are
+        // issued, so the copies do not wait behind the LDS reads (measured)
+        fence();
+        vec(f0);
+        vec(f1);
+      };
+      auto comp = [&] {
+        fence();
+        mfmas(f0);
+        mfmas(f1);
+        fence();
+      };
+      issue(0, 0);
+      issue(1, 1);
+      issue(2, 2);
+      wait_vmcnt<2 * LOADS>();
+      lds_barrier();
+      // every wave runs M(t), C(t) with a barrier after each; the second
+      // half starts one barrier late and the first half ends one barrier
+      // later, so both pass the same number of barriers
+      if (!first) lds_barrier();
+      for (int t = 0; t < ktiles; ++t) {
+        mem(t);
+        fence();
+        lds_barrier();
+        comp();
+        lds_barrier();
+        fence();
+      }
+      if (first) lds_barrier();
+    } else {
+      issue(0, 0);
+      issue(1, 1);
+      issue(2, 2);
+      issue(3, 3);
+      wait_vmcnt<3 * LOADS>();
+      lds_barrier();
+      Frags fr;
+      load(0, 0, fr);
+      for (int kt = 0; kt < ktiles; kt += 4) {
+        step(kt, 0, 1, fr);
+        if (kt + 1 < ktiles) step(kt + 1, 1, 2, fr);
+        if (kt + 2 < ktiles) step(kt + 2, 2, 3, fr);
+        if (kt + 3 < ktiles) step(kt + 3, 3, 0, fr);
+      }
     }
     // drain the trailing zero-fill copies before the epilogue reuses the LDS
     wait_vmcnt<0>();
