@@ -159,6 +159,55 @@ def test_postnorm_ln_smalln_workload_fulln():
     assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
 
 
+SHORT_K = [8, 32, 72, 96, 136]
+
+
+@pytest.mark.parametrize("K", SHORT_K, ids=[f"K{k}" for k in SHORT_K])
+@pytest.mark.parametrize("kind", ["gemm", "prenorm", "splitn_rms", "twopass_ln", "fulln_tall_ln"])
+def test_short_k_loops(kind, K):
+    """The 8-wave tiles' ping-pong mainloop keeps three K tiles of copies in
+    flight: K loops of 1 to 5 tiles (K tails of 8 and 40 included) exercise its
+    prologue, the zero-filled refills past the last tile and the phase barriers,
+    on every path that runs it; ragged M and N, a guard band after Y."""
+    if kind in ("gemm", "prenorm"):
+        M, N = 1100, 4000  # big tiles (M * N above the small-problem size)
+    elif kind == "fulln_tall_ln":
+        M, N = 65536 + 72, 200  # 256 x 256 full-N tiles from 65536 rows on
+    else:
+        M, N = 700, 1544
+    spec, d = inputs.make_inputs("postnorm_rms_largen", M=M, K=K, N=N, seed=300 + K)
+    X, W = dev(d["X"]), dev(d["W"])
+    log(f"short K loop {kind} M={M} K={K} N={N}")
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(K).choice(M, 64, replace=False)]))
+    x = f64(d["X"][rows])
+    if kind in ("gemm", "prenorm"):
+        buf = empty_bf16(M * N + 2 * N)
+        buf.view(torch.int16).fill_(0x1234)
+        Y = buf[: M * N].view(M, N)
+        r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+        if kind == "gemm":
+            B.fng_gemm(X, W, Y)
+            ref = oracle.gemm(x, f64(d["W"]))
+        else:
+            B.fng_prenorm_rms_gemm(X, W, Y, 1e-6, rstd_out=r)
+            ref, rref = oracle.prenorm_rms_gemm(x, f64(d["W"]), 1e-6)
+        torch.cuda.synchronize()
+        assert bool((buf[M * N:].view(torch.int16) == 0x1234).all()), "write past the end of Y"
+        if kind == "prenorm":
+            assert_close_stats(r.cpu().numpy()[rows], rref, "rstd sampled")
+    else:
+        ln = kind.endswith("ln")
+        path = {"splitn_rms": B.FNG_PATH_SPLITN, "twopass_ln": B.FNG_PATH_TWOPASS,
+                "fulln_tall_ln": B.FNG_PATH_FULLN}[kind]
+        eps = 1e-5 if ln else 1e-6
+        Y, mu, r, _ = run_postnorm(d, eps, M, N, K, ln, path)
+        ref, mref, rref = oracle.gemm_postnorm(x, f64(d["W"]), eps, "ln" if ln else "rms")
+        assert_close_stats(r.cpu().numpy()[rows], rref, "rstd sampled")
+        if ln:
+            assert np.max(np.abs(mu.cpu().numpy()[rows] - mref)) < 2e-4
+    assert_parity(host(Y[torch.as_tensor(rows, device="cuda")]), ref, f"{kind} K={K}")
+
+
 @pytest.mark.parametrize("ln", [True, False])
 @pytest.mark.parametrize("path", [B.FNG_PATH_FULLN, B.FNG_PATH_SPLITN, B.FNG_PATH_TWOPASS])
 def test_postnorm_paths_ragged(ln, path):
