@@ -72,12 +72,15 @@ Workspace layout(void* base, int64_t M, int64_t N) {
 
 // automatic choice, from the measured post-LayerNorm sweep over M = 256k rows
 // and K, N in 64..2048: one workgroup across N wins up to N = 256, and at
-// N = 512 while K <= 512; beyond that the split-N exchange wins
-bool auto_fulln(int64_t N, int64_t K) { return N <= 256 || (N <= fng::fulln_max_n() && K <= 512); }
+// N = 512 with the 128 x 512 tiles (M >= 32768) at every K, with the 64 x 512
+// tiles while K <= 512; beyond that the split-N exchange wins
+bool auto_fulln(int64_t M, int64_t N, int64_t K) {
+  return N <= 256 || (N <= fng::fulln_max_n() && (K <= 512 || M >= 32768));
+}
 
 int resolve_path(int path, int64_t M, int64_t N, int64_t K) {
   if (path == FNG_PATH_AUTO) {
-    if (auto_fulln(N, K)) return FNG_PATH_FULLN;
+    if (auto_fulln(M, N, K)) return FNG_PATH_FULLN;
     if (fng::splitn_feasible(M, N)) return FNG_PATH_SPLITN;
     return FNG_PATH_TWOPASS;
   }
@@ -173,7 +176,7 @@ FNG_EXPORT int64_t fng_fulln_max_n(void) { return fng::fulln_max_n(); }
 FNG_EXPORT size_t fng_gemm_postnorm_workspace_bytes(int64_t M, int64_t N, int64_t K, int path) {
   if (M <= 0 || N <= 0) return 0;
   if (path == FNG_PATH_FULLN) return 0;
-  if (path == FNG_PATH_AUTO && auto_fulln(N, K)) return 0;
+  if (path == FNG_PATH_AUTO && auto_fulln(M, N, K)) return 0;
   return layout(nullptr, M, N).bytes;
 }
 

@@ -1111,7 +1111,8 @@ int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
   // rows, tall tiles (W is re-read from L2 once per row block, so tall tiles
   // keep that traffic small): N <= 64: 256 x 64, BK 64; N <= 128: 256 x 128;
   // N <= 256: 256 x 256.  Fewer rows: 32 x 256 tiles, so the grid still fills
-  // the GPU.  N <= 512: 64 x 512 (taller accumulators would not fit).
+  // the GPU.  N <= 512: 128 x 512 from 32768 rows on, else 64 x 512 (taller
+  // accumulators would not fit).
   const bool tall = c.M >= 256 * 256;
   if (tall && c.N <= 64)
     return launch_norm<256, 64, 64, 4, 2, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
@@ -1121,6 +1122,10 @@ int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
     return launch_norm<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   if (c.N <= 256)
     return launch_norm<32, 256, 64, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
+  // N <= 512: 128 x 512 tiles of 8 waves (64 x 128 each, the ping-pong mainloop;
+  // the 4-stage ring fills the 160 KB of LDS) once there are >= 256 of them
+  if (c.M >= 256 * 128)
+    return launch_norm<128, 512, 32, 2, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   return launch_norm<64, 512, 32, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
 }
 

@@ -419,7 +419,7 @@ def main():
                 rf.append(round(t["fused"], 1))
                 ru.append(round(t["gemm"] + t["norm"], 1))
                 rh.append(round(100.0 * (t["gemm"] + t["norm"] - t["fused"]) / t["norm"], 1))
-                rp.append("fulln" if Na <= B.fng_fulln_max_n() else "splitn")
+                rp.append("fulln" if nb == 0 else "splitn")  # the automatic path needs a workspace only for split-N
                 del Wa, Ya, Za, wsa
             fused_us.append(rf)
             unfused_us.append(ru)

@@ -58,7 +58,8 @@ typedef enum {
 /* How a post-norm GEMM reduces statistics over N. */
 typedef enum {
   FNG_PATH_AUTO = 0,    /* FULLN for N <= 256, and for N <= fng_fulln_max_n() when
-                           K <= 512; else SPLITN when the grid fits, else TWOPASS */
+                           K <= 512 or M >= 32768; else SPLITN when the grid fits,
+                           else TWOPASS */
   FNG_PATH_FULLN = 1,   /* one workgroup owns whole output rows (section 1's naive
                            fusion); requires N <= fng_fulln_max_n() */
   FNG_PATH_SPLITN = 2,  /* N split over co-resident workgroups that exchange per-row

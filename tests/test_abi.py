@@ -65,6 +65,13 @@ def test_workspace_sizes():
     assert n >= 64 * 16 * 256 * 2 * 4
     assert B.fng_gemm_postnorm_workspace_bytes(0, 4096, 1024, B.FNG_PATH_SPLITN) == 0
     assert B.fng_fulln_max_n() >= 256
+    # the automatic path (a workspace is needed exactly when it is not full-N):
+    # N = 512 takes full-N at any K once the 128 x 512 tiles apply (M >= 32768),
+    # else only while K <= 512; larger N takes split-N
+    assert B.fng_gemm_postnorm_workspace_bytes(262144, 512, 2048, B.FNG_PATH_AUTO) == 0
+    assert B.fng_gemm_postnorm_workspace_bytes(2048, 512, 512, B.FNG_PATH_AUTO) == 0
+    assert B.fng_gemm_postnorm_workspace_bytes(2048, 512, 2048, B.FNG_PATH_AUTO) > 0
+    assert B.fng_gemm_postnorm_workspace_bytes(262144, 1024, 64, B.FNG_PATH_AUTO) > 0
 
 
 # raw C calls with arguments that validation must reject -------------------

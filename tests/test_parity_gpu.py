@@ -258,10 +258,11 @@ def test_postnorm_ads_shapes(K, N):
 
 
 @pytest.mark.parametrize("ln", [True, False])
-@pytest.mark.parametrize("N", [40, 64, 104, 200])
+@pytest.mark.parametrize("N", [40, 64, 104, 200, 264, 512])
 def test_postnorm_fulln_tall_tiles(ln, N):
-    """Full-N with 256-row tiles (used from 65536 rows on), ragged M, K and N;
-    sampled rows against the oracle plus the row property on every row."""
+    """Full-N with 256-row tiles (used from 65536 rows on; 128 x 512 tiles for
+    N above 256), ragged M, K and N; sampled rows against the oracle plus the
+    row property on every row."""
     M, K = 65536 + 72, 136
     spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=N + 5)
     log(f"postnorm full-N tall ln={ln} M={M} K={K} N={N}")
@@ -520,6 +521,8 @@ def test_empty_calls_are_noops():
 @pytest.mark.parametrize("kind", ["ln", "rms"])
 def test_postnorm_affine(kind, path):
     M, K, N = 600, 264, 256 if path == B.FNG_PATH_FULLN else 1320
+    if path == B.FNG_PATH_FULLN and kind == "rms":
+        M, N = 32768 + 40, 392  # the 128 x 512 full-N tile (from 32768 rows on), ragged N
     spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=61)
     rng = np.random.Generator(np.random.PCG64(62))
     g = inputs.f32_to_bf16_bits(1.0 + 0.3 * rng.standard_normal(N).astype(np.float32))
