@@ -144,11 +144,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   constexpr bool IS_BWD = EPI == EPI_BWD_FULLN || EPI == EPI_BWD_SPLITN;
   constexpr bool IS_SPLIT = EPI == EPI_SPLITN || EPI == EPI_BWD_SPLITN;
   // ping-pong mainloop: 8 waves in two row halves, two k16 slices per K tile.
-  // The backward keeps the single-phase loop (its last refills bring in the
-  // saved tile over all four stages), and so does the lazy pre-norm with the
-  // gain: its fold (about 50 vector instructions per slice) would make the
-  // memory phase the longer one (measured slower).
-  constexpr bool PP = NWAVES == 8 && WAVES_M == 2 && BK == 32 && !IS_BWD && !PG && EPI != EPI_SPLITN;
+  // The lazy pre-norm with the gain keeps the single-phase loop: its fold
+  // (about 50 vector instructions per slice) would make the memory phase the
+  // longer one (measured slower).
+  constexpr bool PP = NWAVES == 8 && WAVES_M == 2 && BK == 32 && !PG;
   constexpr int RED = IS_BWD ? S::BYTES : 0;
   constexpr int EXTRA = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
   static_assert(S::BYTES + EXTRA <= 160 * 1024, "LDS budget with the backward's reductions");
@@ -432,6 +431,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       else { Frags fc; load(next, 0, fc); fence(); mma(fa); fence(); fa = fc; }
     };
     __syncthreads();  // the previous tile's epilogue may still read LDS
+    // The loop-invariant address and offset registers pass through an empty
+    // asm here: if the allocator spilled one of them, its reload (and the
+    // compiler's wait for it) lands before the loop.  Otherwise the wait for
+    // the reload sits inside the loop, where the compiler -- which does not
+    // count the copies issued by inline asm -- makes it a wait for every
+    // memory operation in flight, i.e. for all the copies of the next tiles
+    // (measured: the split-N LayerNorm mainloop 85 instead of 56 us per tile).
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i) asm volatile("" : "+v"(a_off[i]), "+v"(a_k[i]));
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i) asm volatile("" : "+v"(b_off[i]));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < BK / 16; ++q) {
+        uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(xaddr[i][q]);
+        asm volatile("" : "+v"(a));
+        xaddr[i][q] = reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a));
+      }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(waddr[j]);
+      asm volatile("" : "+v"(a));
+      waddr[j] = reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a));
+    }
     if constexpr (PP) {
       // Ping-pong: the two waves of each SIMD (one per row half) alternate
       // between a memory phase M(t) -- read all of K tile t's fragments,
@@ -484,6 +508,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         fence();
       }
       if (first) lds_barrier();
+      // the norm backward: the refills past the last K tile brought the saved
+      // tile into three stages; the stage of the last K tile, read by both
+      // halves before the last barrier, gets its part now
+      if constexpr (IS_BWD) issue(ktiles + 3, (ktiles + 3) & 3);
     } else {
       issue(0, 0);
       issue(1, 1);
