@@ -184,6 +184,14 @@ __device__ __forceinline__ void dma16(i32x4_t rsrc, const FNG_LDS char* lds_wave
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
 }
+// the same with a wave-uniform byte offset in the instruction's scalar offset
+// field (the buffer range check applies to the sum)
+__device__ __forceinline__ void dma16_so(i32x4_t rsrc, const FNG_LDS char* lds_wave_base, uint32_t off,
+                                         uint32_t soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer range: DMA writes zeros

@@ -295,6 +295,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           return;
         }
       }
+      if (kt < ktiles && (kt + 1) * BK <= K) {
+        // a whole K tile in range: the per-lane offsets are the tile's
+        // constants, the K step goes in the scalar offset (no vector work)
+#pragma unroll
+        for (int i = 0; i < A_PER_WAVE; ++i)
+          dma16_so(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, a_off[i], (uint32_t)(kt * BK * 2));
+#pragma unroll
+        for (int i = 0; i < B_PER_WAVE; ++i)
+          dma16_so(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024, b_off[i] | (b_ok[i] ? 0u : kOOB),
+                   (uint32_t)(kt * BK) * (uint32_t)N * 2u);
+        if constexpr (PG) {
+          if (wave == 0 && lane < KC) dma16(gr, lds + S::gm(s), (uint32_t)(kt * BK + lane * 8) * 2u);
+        }
+        return;
+      }
       const uint32_t kt_live = kt < ktiles ? 0u : kOOB;
 #pragma unroll
       for (int i = 0; i < A_PER_WAVE; ++i) {
