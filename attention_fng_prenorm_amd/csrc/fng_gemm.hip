@@ -31,8 +31,8 @@
 // between reading a K tile's fragments and multiplying them, two barriers
 // per K tile; the other tiles use one barrier per K tile.  X is kept [m][k]
 // (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as in
-// memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte chunks are XOR-swizzled per row so
-// fragment reads are bank-conflict free.
+// memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte
+// chunks are XOR-swizzled per row so fragment reads are bank-conflict free.
 #include "fng_device.h"
 #include "fng_internal.h"
 
@@ -359,7 +359,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       }
       if constexpr (PG) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
     };
-    // the vector work on one slice's fragments (ping-pong memory phase)
+    // the vector work on one slice's fragments (ping-pong memory phase; the
+    // gain fold never runs there)
     auto vec = [&](Frags& f) {
       if constexpr (EPI == EPI_PRENORM) {
         if (ss_owner) {
@@ -369,13 +370,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
             if constexpr (LN) sum_bf16x8_2(f.x[s], sx[s][0], sx[s][1]);
           }
         }
-      }
-      if constexpr (PG) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            f.w[j][e] = pack_bf16(bf16lo(f.w[j][e]) * bf16lo(f.g[e]), bf16hi(f.w[j][e]) * bf16hi(f.g[e]));
       }
     };
     auto mfmas = [&](Frags& f) {
@@ -452,7 +446,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     // the reload sits inside the loop, where the compiler -- which does not
     // count the copies issued by inline asm -- makes it a wait for every
     // memory operation in flight, i.e. for all the copies of the next tiles
-    // (measured: the split-N LayerNorm mainloop 85 instead of 56 us per tile).
+    // (measured: the split-N LayerNorm mainloop took 85 instead of ~56 us per
+    // tile of 256 x 256 x 2048).
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) asm volatile("" : "+v"(a_off[i]), "+v"(a_k[i]));
 #pragma unroll
@@ -476,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       // between a memory phase M(t) -- read all of K tile t's fragments,
       // issue the copies of tile t+3 into the stage tile t-1 used, wait until
       // this wave's copies of tile t+1 have landed, and the vector work on
-      // the fragments (sums of squares, the gain fold) -- and a compute
+      // the fragments (the lazy pre-norm's sums of squares) -- and a compute
       // phase C(t) of the tile's MFMAs back to back.  The row-half-0 waves
       // run M(t) while the row-half-1 waves run C(t-1), then the roles swap;
       // a workgroup barrier separates the phases, so the matrix core of a
@@ -537,9 +532,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         for (int t = 0; t < ktiles; ++t) tile(t, t & 3);
       }
       if (first) lds_barrier();
-      // the norm backward: the refills past the last K tile brought the saved
-      // tile into three stages; the stage of the last K tile, read by both
-      // halves before the last barrier, gets its part now
+      // the norm backward: the refills of tiles ktiles .. ktiles+2 (past the
+      // last K tile) brought the saved tile into three stages; the fourth,
+      // the last K tile's stage, read by both halves before the last
+      // barrier, gets its part now
       if constexpr (IS_BWD) issue(ktiles + 3, (ktiles + 3) & 3);
     } else {
       issue(0, 0);
