@@ -453,12 +453,12 @@ def main():
                    "parallelism": "single GPU"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         # the lazy pre-RMSNorm call is the dominant kernel: one template launched twice
-        # per call (256x256 tiles, then 256x128 tiles over the columns of the last
+        # per call (256x256 tiles, then 128x256 tiles over the columns of the last
         # partial round of workgroups); achieved = 2MNK / the call's average duration
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic("prenorm"),
-                     "kernel": "gemm_kernel<256,256,32,2,4,EPI_PRENORM> + its 256x128 tail launch, per call"},
+                     "kernel": "gemm_kernel<256,256,32,2,4,EPI_PRENORM> + its 128x256 tail launch, per call"},
         "kernels": kernels,
     }
     if "prenorm_rms_mlp" in kernels:

@@ -80,7 +80,7 @@ def test_prenorm_full_size_sampled(gamma):
 @pytest.mark.parametrize("kind", ["gemm", "prenorm", "prenorm_gamma"])
 def test_big_tiles_with_tail_launch(kind):
     # 16 x 56 tiles of 256 x 256 are 3.5 rounds of 256 CUs: the trailing 8 column
-    # blocks run as a second launch of 256 x 128 tiles (ragged here: N = 14200)
+    # blocks run as a second launch of 128 x 256 tiles (ragged here: N = 14200)
     M, K, N = 4000, 264, 14200
     spec, d = inputs.make_inputs("prenorm_rms_mlp_gamma" if kind == "prenorm_gamma" else "prenorm_rms_mlp",
                                  M=M, K=K, N=N, seed=17)
