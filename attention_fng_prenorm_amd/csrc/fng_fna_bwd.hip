@@ -280,24 +280,64 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
     // 16-byte reads (A operand of S^T = K n^T and dP^T = V do^T): key row
     // kappa(l32), chunk 2kk + hi
     const int krow = kappa(l32);
-    int koff[8];
+    // koff(kk) = base + ((2kk + hi) ^ swz) * 16 = kb + 32 (kk ^ kx).  With the
+    // GELU's high and low operand parts the kernel holds two more sets of
+    // loop operands: there the sums are formed at each use from two registers
+    // (the empty asm keeps the compiler from hoisting all eight out of the
+    // loops); held in registers they made the allocator spill a loop operand
+    // and reload it inside the key loop, behind a wait for every copy in
+    // flight.
+    // With the softmax (single bf16 operand parts, no spill) the eight
+    // precomputed addresses are cheaper than the per-use arithmetic (measured).
+    constexpr bool LEAN = SPLIT;
+    const int kb = h * kTileB + krow * kRowB + 16 * (hi ^ (swz(krow) & 1));
+    const int kx = swz(krow) >> 1;
+    int koffa[LEAN ? 1 : 8];
+    if constexpr (!LEAN) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) koff[kk] = h * kTileB + krow * kRowB + (((2 * kk + hi) ^ swz(krow)) * 16);
+      for (int kk = 0; kk < 8; ++kk) koffa[kk] = kb + 32 * (kk ^ kx);
+    }
+    auto koff = [&](int kk) __attribute__((always_inline)) {
+      if constexpr (LEAN) {
+        int b = kb, x = kx;
+        asm volatile("" : "+v"(b), "+v"(x));
+        return b + 32 * (kk ^ x);
+      } else {
+        return koffa[kk];
+      }
+    };
     // transposing reads (A operand of dn^T = K^T ds^T): lane (g4, li) reads
     // key 16c + 8 (g4 / 2) + li / 4 (+4 for the second read), d = 32 dt +
     // 16 (g4 % 2) + 4 (li % 4)
     const int g4 = lane >> 4, li = lane & 15;
     const int tkey = 8 * (g4 >> 1) + (li >> 2);
-    int toff[4][2];
+    // toff(dt, s2) = base + ((d >> 3) ^ swz(kq)) * 16 + (d & 7) * 2 with
+    // d >> 3 = 4 dt + c, c = 2 (g4 % 2) + (li % 4) / 2, (d & 7) * 2 = 8 (li % 2):
+    // = tb[s2] + 64 (dt ^ tx[s2])
+    int tb[2], tx[2];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = 32 * dt + 16 * (g4 & 1) + 4 * (li & 3);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kq = tkey + 4 * s2;
-        toff[dt][s2] = h * kTileB + kq * kRowB + (((d >> 3) ^ swz(kq)) * 16) + (d & 7) * 2;
-      }
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int kq = tkey + 4 * s2;
+      const int c = 2 * (g4 & 1) + ((li & 3) >> 1);
+      tb[s2] = h * kTileB + kq * kRowB + 16 * (c ^ (swz(kq) & 3)) + 8 * (li & 1);
+      tx[s2] = swz(kq) >> 2;
     }
+    int toffa[LEAN ? 1 : 4][2];
+    if constexpr (!LEAN) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) toffa[dt][s2] = tb[s2] + 64 * (dt ^ tx[s2]);
+    }
+    auto toff = [&](int dt, int s2) __attribute__((always_inline)) {
+      if constexpr (LEAN) {
+        int b = tb[s2], x = tx[s2];
+        asm volatile("" : "+v"(b), "+v"(x));
+        return b + 64 * (dt ^ x);
+      } else {
+        return toffa[dt][s2];
+      }
+    };
     const int ntiles = (p.Skv + kKT - 1) / kKT;
 
     auto scores = [&](f32x16_t& sa, int reg) __attribute__((always_inline)) {
@@ -305,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       for (int r = 0; r < 16; ++r) sa[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t kf = lds_read16(lds + reg + koff[kk]);
+        const u32x4_t kf = lds_read16(lds + reg + koff(kk));
         sa = mfma_bf16(kf, nb[kk], sa);
         if constexpr (SPLIT) sa = mfma_bf16(kf, nl[kk], sa);
       }
@@ -316,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t vf = lds_read16(lds + reg + koff[kk]);
+        const u32x4_t vf = lds_read16(lds + reg + koff(kk));
         dp = mfma_bf16(vf, dob[kk], dp);
         if constexpr (SPLIT) dp = mfma_bf16(vf, dol[kk], dp);
       }
@@ -442,8 +482,8 @@ __global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const u32x2_t lo = lds_read_tr16(lds + toff[dt][0] + c * 16 * kRowB);
-          const u32x2_t hi2 = lds_read_tr16(lds + toff[dt][1] + c * 16 * kRowB);
+          const u32x2_t lo = lds_read_tr16(lds + toff(dt, 0) + c * 16 * kRowB);
+          const u32x2_t hi2 = lds_read_tr16(lds + toff(dt, 1) + c * 16 * kRowB);
           const u32x4_t kf = {lo[0], lo[1], hi2[0], hi2[1]};
           dn[dt] = mfma_bf16(kf, dsb[c], dn[dt]);
           if constexpr (SPLIT) dn[dt] = mfma_bf16(kf, dsl[c], dn[dt]);
