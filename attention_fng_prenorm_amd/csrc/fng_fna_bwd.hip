@@ -771,8 +771,13 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
         }
         const float ls = key_lane_sum(ev, l32), ws = key_lane_sum(wv, l32);
         if ((l32 & 1) == 0) {
-          const int j = (l32 >> 1) & 15;
-          const int qr = 16 * (j >> 3) + 8 * hi + (j & 7);
+          // the row index is formed here from the lane id (a loop-invariant
+          // address held across the loop was spilled, and its reload inside
+          // the loop waited for the next row block's loads in flight)
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const int j = ((ln & 31) >> 1) & 15;
+          const int qr = 16 * (j >> 3) + 8 * (ln >> 5) + (j & 7);
           part[(qr * 4 + kw) * 2 + 0] = ls;
           part[(qr * 4 + kw) * 2 + 1] = ws;
         }
