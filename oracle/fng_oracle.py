@@ -233,6 +233,21 @@ def prenorm_rms_backward_dx(dy, w, x, rstd):
     return rmsnorm_backward_rows(gemm(dy, w), x * r[..., None], r)
 
 
+def prenorm_rms_backward_dw(x, dy, rstd, gamma=None):
+    """Weight gradient of the lazy pre-RMSNorm GEMM y = (rmsnorm(x) * gamma) @ W
+    (section 2's limitations: rmsnorm(A) must be rebuilt from A and rstd for
+    the gradients of both operands).  With xhat = x * rstd[:, None] (* gamma),
+    the normalized input rebuilt from x [M, K] and the forward rstd [M]:
+        dW = xhat^T @ dy,   dW [K, N], dy [M, N].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(rstd, dtype=np.float64)
+    xhat = x * r[:, None]
+    if gamma is not None:
+        xhat = xhat * np.asarray(gamma, dtype=np.float64)[None, :]
+    return xhat.T @ np.asarray(dy, dtype=np.float64)
+
+
 # ---------------------------------------------------------------------------
 # attention (section 4)
 # ---------------------------------------------------------------------------

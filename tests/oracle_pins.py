@@ -706,6 +706,66 @@ def check_prenorm_backward_torch(O):
            "lazy pre-RMS dx vs autograd")
 
 
+def check_prenorm_backward_dw_torch(O):
+    # the weight gradient of (rms_norm(x) * gamma) @ W by fp64 autograd
+    # through torch's own rms_norm, with and without the gain
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(76)
+    M, K, N = 9, 20, 13
+    x = rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))
+    x[3] = 0.0                                   # a zero row: rstd = 1/sqrt(eps), no contribution
+    W = rng.standard_normal((K, N)) / 4.0
+    gamma = 1.0 + 0.3 * rng.standard_normal(K)
+    dy = rng.standard_normal((M, N))
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + 1e-6)   # the forward's saved statistic
+    for g in (None, gamma):
+        Wt = torch.from_numpy(W.copy()).requires_grad_(True)
+        xn = F.rms_norm(torch.from_numpy(x), (K,), eps=1e-6)
+        if g is not None:
+            xn = xn * torch.from_numpy(g)
+        (xn @ Wt).backward(torch.from_numpy(dy))
+        _close(O.prenorm_rms_backward_dw(x, dy, r, g), Wt.grad.numpy(), 1e-12,
+               f"lazy pre-RMS dW (gamma={g is not None}) vs autograd")
+
+
+def check_prenorm_backward_dw_bruteforce(O):
+    # dW[k][n] = sum_m x[m][k] * rstd[m] * gamma[k] * dy[m][n], plain loops
+    rng = _rng(77)
+    M, K, N = 4, 3, 5
+    x = rng.standard_normal((M, K)).tolist()
+    dy = rng.standard_normal((M, N)).tolist()
+    r = (0.5 + rng.random(M)).tolist()
+    g = (1.0 + 0.5 * rng.standard_normal(K)).tolist()
+    for gam in (None, g):
+        want = [[sum(x[m][k] * r[m] * (gam[k] if gam else 1.0) * dy[m][n] for m in range(M))
+                 for n in range(N)] for k in range(K)]
+        got = O.prenorm_rms_backward_dw(np.array(x), np.array(dy), np.array(r),
+                                        np.array(gam) if gam else None)
+        _close(got, want, 1e-13, f"lazy pre-RMS dW brute force (gamma={gam is not None})")
+
+
+def check_prenorm_backward_dw_invariants(O):
+    rng = _rng(78)
+    M, K, N = 6, 8, 5
+    x = rng.standard_normal((M, K))
+    dy = rng.standard_normal((M, N))
+    r = 0.5 + rng.random(M)
+    dw = O.prenorm_rms_backward_dw(x, dy, r)
+    # a row scale of x with the matching rstd (x * c, rstd / c) changes nothing
+    c = np.exp(rng.standard_normal(M))
+    _close(O.prenorm_rms_backward_dw(x * c[:, None], dy, r / c), dw, 1e-12, "dW row-scale invariance")
+    # additive over the rows of the batch (the contraction axis)
+    a = O.prenorm_rms_backward_dw(x[:2], dy[:2], r[:2]) + O.prenorm_rms_backward_dw(x[2:], dy[2:], r[2:])
+    _close(a, dw, 1e-12, "dW sums over rows")
+    # a single row gives the outer product of its normalized values and its dy
+    one = O.prenorm_rms_backward_dw(x[:1], dy[:1], r[:1])
+    _close(one, np.outer(x[0] * r[0], dy[0]), 1e-13, "dW of one row")
+    # the gain scales the rows of dW
+    gam = 1.0 + rng.random(K)
+    _close(O.prenorm_rms_backward_dw(x, dy, r, gam), gam[:, None] * dw, 1e-12, "dW with gain")
+
+
 def _fna_torch_forward(q, off, k, v, eps_ln, eps_rms, scale, act):
     """FlashNormAttention from torch library routines (fp64), differentiable
     in q, k and v: layer_norm and rms_norm across all heads, softmax or the
@@ -836,6 +896,9 @@ ALL_CHECKS = [
     check_norm_backward_invariants,
     check_gemm_postnorm_backward_torch,
     check_prenorm_backward_torch,
+    check_prenorm_backward_dw_torch,
+    check_prenorm_backward_dw_bruteforce,
+    check_prenorm_backward_dw_invariants,
     check_fna_backward_torch,
     check_fna_backward_finite_differences,
     check_fna_backward_invariants,

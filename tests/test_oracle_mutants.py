@@ -361,7 +361,37 @@ def _prenorm_dx_raw_xhat(dy, w, x, rstd):
     return F.rmsnorm_backward_rows(F.gemm(dy, w), x, rstd)
 
 
+def _dw_rstd_on_columns(x, dy, rstd, gamma=None):
+    # one scale for the whole batch in place of each row's own rstd
+    x = np.asarray(x, dtype=np.float64)
+    xg = x * np.asarray(gamma)[None, :] if gamma is not None else x
+    return xg.T @ (np.asarray(dy) * np.mean(np.asarray(rstd)))
+
+
+def _dw_no_rstd(x, dy, rstd, gamma=None):
+    x = np.asarray(x, dtype=np.float64)
+    xg = x * np.asarray(gamma)[None, :] if gamma is not None else x
+    return xg.T @ np.asarray(dy, dtype=np.float64)
+
+
+def _dw_gamma_on_columns(x, dy, rstd, gamma=None):
+    xh = np.asarray(x, dtype=np.float64) * np.asarray(rstd)[:, None]
+    out = xh.T @ np.asarray(dy, dtype=np.float64)
+    if gamma is not None:
+        out = out * np.resize(np.asarray(gamma), out.shape[1])[None, :]
+    return out
+
+
+def _dw_rstd_squared(x, dy, rstd, gamma=None):
+    r = np.asarray(rstd, dtype=np.float64)
+    return F.prenorm_rms_backward_dw(x, dy, r * r, gamma)
+
+
 MUTANTS = {
+    "dw_rstd_averaged_not_per_row": dict(prenorm_rms_backward_dw=_dw_rstd_on_columns),
+    "dw_xhat_not_rebuilt": dict(prenorm_rms_backward_dw=_dw_no_rstd),
+    "dw_gamma_on_columns": dict(prenorm_rms_backward_dw=_dw_gamma_on_columns),
+    "dw_rstd_squared": dict(prenorm_rms_backward_dw=_dw_rstd_squared),
     "rms_eps_outside_sqrt": dict(rmsnorm_rows=_rms_eps_outside),
     "rms_divides_by_n_minus_1": dict(rmsnorm_rows=_rms_sum_not_mean),
     "rms_gamma_before_stats": dict(rmsnorm_rows=_rms_gamma_in_stats),
