@@ -205,14 +205,19 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
       }
       rstd = __builtin_amdgcn_rsqf(m2 * (1.0f / (H * kD)) + p.eps_ln);
     }
-    // normalized (and pre-scaled) query, split into bf16 high and low parts
-    const float mul = rstd * p.scale, add = -mu * mul;
+    // normalized (and pre-scaled) query, split into bf16 high and low parts.
+    // The mean is subtracted before the scale: x - mu is exact for the
+    // values near the mean (and 0 on a constant row, whose normalized row is
+    // then exactly 0); x * mul - mu * mul would leave the rounding of mu * mul,
+    // which the output RMSNorm amplifies by up to 1/sqrt(eps) when the
+    // attention output is that small.
+    const float mul = rstd * p.scale;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t w = raw[kk][e];
-        const float x0 = fmaf(bf16lo(w), mul, add), x1 = fmaf(bf16hi(w), mul, add);
+        const float x0 = (bf16lo(w) - mu) * mul, x1 = (bf16hi(w) - mu) * mul;
         const uint32_t hw = pack_bf16(x0, x1);
         qh[kk][e] = hw;
         ql[kk][e] = pack_bf16(x0 - bf16lo(hw), x1 - bf16hi(hw));

@@ -39,6 +39,10 @@ Backward (section 3's fusion regrouping; shapes of the forward workloads):
   prenorm_rms_mlp_bwd_dx   dY[4096,14336] ~ N(0,1), Wt[14336,4096] ~
                            N(0,1/14336), X[4096,4096] with log-normal row
                            scales (as the forward), rstd[4096] as above
+  prenorm_rms_mlp_dw       the weight gradient: X[4096,4096] with log-normal
+                           row scales, dY[4096,14336] ~ N(0,1) (seed 1033);
+                           _gamma adds gamma[4096] ~ N(1, 0.1) (seed 1043);
+                           rstd is the forward's, computed from X
   The saved tensors and statistics are drawn independently of each other:
   the backward is a function of them, whatever produced them.
 
@@ -76,6 +80,9 @@ WORKLOADS = {
                                     seed=1014),
     "prenorm_rms_mlp_bwd_dx": dict(kind="norm_bwd", M=4096, K=14336, N=4096, norm="rms",
                                    h_dist="lognormal_rows", seed=1023),
+    "prenorm_rms_mlp_dw": dict(kind="prenorm_dw", M=4096, K=4096, N=14336, eps=1e-6, gamma=False, seed=1033),
+    "prenorm_rms_mlp_dw_gamma": dict(kind="prenorm_dw", M=4096, K=4096, N=14336, eps=1e-6, gamma=True,
+                                     seed=1043),
     "flash_norm_attention": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
                                  D=128, eps_ln=1e-5, eps_rms=1e-6, act="gelu", seed=1006),
     "flash_norm_attention_bwd": dict(kind="flash_norm_attention", B=768, max_len=512, Skv=128, H=4,
@@ -194,6 +201,20 @@ def make_norm_bwd_inputs(spec):
     return {"G": f32_to_bf16_bits(g), "Wt": f32_to_bf16_bits(w), "H": f32_to_bf16_bits(h), "rstd": rstd}
 
 
+def make_dw_inputs(spec):
+    """Inputs of the lazy pre-RMSNorm weight gradient: dict X [M,K] bf16 bits
+    with log-normal row scales (the forward's recipe), dY [M,N] ~ N(0,1), gamma
+    [K] ~ N(1, 0.1) or None."""
+    rng = np.random.Generator(np.random.PCG64(spec["seed"]))
+    M, K, N = spec["M"], spec["K"], spec["N"]
+    s = np.exp(_normal(rng, (M, 1)))
+    x = s * _normal(rng, (M, K))
+    dy = _normal(rng, (M, N))
+    g = _normal(rng, (K,), var=0.1, mean=1.0) if spec.get("gamma") else None
+    return {"X": f32_to_bf16_bits(x), "dY": f32_to_bf16_bits(dy),
+            "gamma": f32_to_bf16_bits(g) if g is not None else None}
+
+
 def make_inputs(name, **overrides):
     """Spec and inputs for workload `name` (see the recipe in the header)."""
     spec = workload(name, **overrides)
@@ -203,4 +224,50 @@ def make_inputs(name, **overrides):
         return spec, make_jagged_attention_inputs(spec)
     if spec["kind"] == "norm_bwd":
         return spec, make_norm_bwd_inputs(spec)
+    if spec["kind"] == "prenorm_dw":
+        return spec, make_dw_inputs(spec)
     return spec, make_gemm_inputs(spec)
+
+
+# Degenerate rows for the edge-case parity tests.  Each kind replaces whole
+# rows (the last axis, or the last two for [T, H, D] query tensors, so that a
+# "row" is everything one normalization sees) with values drawn from its own
+# generator PCG64(seed):
+#   zero     all zeros
+#   const    one value c ~ N(0, 1) repeated over the row (a nonzero draw)
+#   tiny     z * sqrt(eps), z ~ N(0, 1): mean square about eps
+#   shifted  z + mu, z ~ N(0, 1), mu = +/- shift (rows far off zero mean)
+#   huge     z * 2^12 (mean square about 2^24)
+ROW_KINDS = ("zero", "const", "tiny", "shifted", "huge")
+
+
+def plant_rows(bits, rows, kinds, seed, eps=1e-6, shift=24.0, row_dims=1):
+    """Copy of the bf16 bit array `bits` with rows[i] replaced by a row of kind
+    kinds[i % len(kinds)] (see ROW_KINDS).  row_dims: how many trailing axes
+    form one row.  Returns (new bits, dict kind -> list of row indices)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.array(bits, copy=True)
+    lead = out.shape[: out.ndim - row_dims]
+    flat = out.reshape(int(np.prod(lead)), -1)
+    n = flat.shape[1]
+    where = {k: [] for k in ROW_KINDS}
+    for i, r in enumerate(rows):
+        kind = kinds[i % len(kinds)]
+        if kind == "zero":
+            v = np.zeros(n, dtype=np.float32)
+        elif kind == "const":
+            c = np.float32(0.0)
+            while c == 0.0:
+                c = _normal(rng, ())
+            v = np.full(n, c, dtype=np.float32)
+        elif kind == "tiny":
+            v = _normal(rng, (n,)) * np.float32(math.sqrt(eps))
+        elif kind == "shifted":
+            v = _normal(rng, (n,)) + np.float32(shift if rng.integers(0, 2) else -shift)
+        elif kind == "huge":
+            v = _normal(rng, (n,)) * np.float32(4096.0)
+        else:
+            raise ValueError(kind)
+        flat[r] = f32_to_bf16_bits(v)
+        where[kind].append(int(r))
+    return flat.reshape(out.shape), where

@@ -52,3 +52,28 @@ def assert_close_stats(got, want, what, rtol=2e-4):
     rel = np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-30))
     log(f"{what}: max rel {rel:.3e}")
     assert rel <= rtol, (what, rel)
+
+
+def bf16_floor(ref):
+    """MAE of the exact result rounded to bf16 (nearest even): what a bf16
+    output costs by itself, before any arithmetic error."""
+    ref = np.ascontiguousarray(ref, dtype=np.float64)
+    r = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    return float(np.mean(np.abs(r - ref)))
+
+
+FLOOR_MARGIN = 1e-3
+
+
+def assert_parity_floor(y, ref, what, margin=FLOOR_MARGIN):
+    """The agreed gate for outputs that are not unit-scale (gradients,
+    residual outputs): normwise max relative error <= 1e-2, and a mean
+    absolute error within `margin` of the bf16 rounding floor of the exact
+    result, never looser than 2e-3 scaled by the output's mean magnitude over
+    0.8 (the mean magnitude of a unit normal)."""
+    floor = bf16_floor(ref)
+    scaled = MAE * max(1.0, float(np.mean(np.abs(ref))) / 0.8)
+    bound = min(scaled, floor + margin)
+    e = assert_parity(y, ref, what, mae=bound)
+    log(f"{what}: bf16 floor mae={floor:.3e} excess={e['mae'] - floor:.3e} bound={bound:.3e}")
+    return e

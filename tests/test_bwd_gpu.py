@@ -16,7 +16,7 @@ import torch
 import oracle
 from attention_fng_prenorm_amd import binding as B
 from attention_fng_prenorm_amd import inputs
-from gpu_util import assert_parity, dev, empty_bf16, host, log
+from gpu_util import assert_parity, assert_parity_floor, dev, empty_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -25,8 +25,8 @@ def f64(bits):
     return oracle.bf16_to_f64(bits)
 
 
-def scaled_parity(y, ref, what, factor=1.0):
-    return assert_parity(y, ref, what, mae=factor * 2e-3 * max(1.0, float(np.mean(np.abs(ref))) / 0.8))
+def scaled_parity(y, ref, what):
+    return assert_parity_floor(y, ref, what)
 
 
 def workspace(M, N, K, path):
@@ -147,7 +147,9 @@ def test_fused_matches_unfused_bwd():
     ref = oracle.gemm_postnorm_backward(f64(d["G"]), f64(d["Wt"]), f64(d["H"]), d["rstd"], "ln")
     ef = scaled_parity(host(fused), ref, "fused ln bwd")
     # the unfused chain rounds the GEMM output to bf16 before the norm backward
-    eu = scaled_parity(host(unfused), ref, "unfused gemm + ln bwd", factor=2.0)
+    # (a baseline, not the fused path: its gate is twice the scaled MAE bound)
+    eu = assert_parity(host(unfused), ref, "unfused gemm + ln bwd",
+                       mae=2 * 2e-3 * max(1.0, float(np.mean(np.abs(ref))) / 0.8))
     assert ef["mae"] <= eu["mae"] * 1.05
 
 

@@ -10,10 +10,11 @@ the page does); the oracle recomputes everything from Q, K, V and dOut in
 fp64.  The softmax case with a single key is the sharp one: there the exact
 dK is zero, so any inconsistency between P, dP and the row term shows.
 
-Tolerance: normwise max relative error <= 1e-2 and mean absolute error <=
-2e-3, the MAE bound scaled by the gradient's mean magnitude over 0.8 where
-that is larger (dQ carries dOut through the second residual, mean |dQ| is
-about 1.1; GELU's dV sums O(1) activations over up to 512 rows)."""
+Tolerance: normwise max relative error <= 1e-2, and a mean absolute error
+within GRAD_MARGIN of the bf16 rounding floor of the exact gradient (never
+looser than 2e-3 scaled by the gradient's mean magnitude over 0.8: dQ
+carries dOut through the second residual, mean |dQ| is about 1.1; GELU's dV
+sums O(1) activations over up to 512 rows)."""
 
 import math
 
@@ -24,12 +25,16 @@ import torch
 import oracle
 from attention_fng_prenorm_amd import binding as B
 from attention_fng_prenorm_amd import inputs
-from gpu_util import assert_parity, dev, empty_bf16, host, log
+from gpu_util import assert_parity_floor, dev, empty_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 
 LENGTHS = [0, 1, 300, 37, 256, 65, 0, 129, 64, 128]
 SCALE = 1.0 / math.sqrt(128)
+# the mean absolute error may exceed the bf16 rounding floor of the exact
+# gradient by at most this much (measured excess on these inputs: dQ up to
+# 1e-4, dK and dV up to about 2e-4, more for dK with a single key)
+GRAD_MARGIN = 1e-3
 
 
 def f64(bits):
@@ -37,10 +42,7 @@ def f64(bits):
 
 
 def grad_parity(y, ref, what):
-    e = assert_parity(y, ref, what, mae=2e-3 * max(1.0, float(np.mean(np.abs(ref))) / 0.8))
-    floor = oracle.compare(torch.from_numpy(ref).to(torch.bfloat16).double().numpy(), ref)["mae"]
-    log(f"{what}: bf16 rounding floor mae={floor:.3e}")
-    return e
+    return assert_parity_floor(y, ref, what, margin=GRAD_MARGIN)
 
 
 def case(H, Skv, lengths=LENGTHS, seed=21):
