@@ -58,6 +58,7 @@ SIGNATURES = {
     "fng_gemm_postnorm_ln_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
     "fng_gemm_postnorm_rms_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
     "fng_prenorm_rms_bwd_dx": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _int, _vp]),
+    "fng_prenorm_rms_bwd_dw": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "fng_layernorm_bwd": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _vp]),
     "fng_rmsnorm_bwd": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp]),
     "fng_flash_norm_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
@@ -290,6 +291,17 @@ def fng_prenorm_rms_bwd_dx(dY, Wt, X, rstd, dX, workspace=None, path=FNG_PATH_AU
     if Wt.shape[0] != N or tuple(X.shape) != (M, K) or tuple(dX.shape) != (M, K) or tuple(rstd.shape) != (M,):
         raise ValueError("shapes: dY [M,N], Wt [N,K], X/dX [M,K], rstd [M]")
     _bwd("fng_prenorm_rms_bwd_dx", dY, Wt, X, rstd, dX, workspace, path, stream, (M, N, K))
+
+
+def fng_prenorm_rms_bwd_dw(X, rstd, dY, dW, gamma=None, stream=None):
+    M, K = X.shape
+    N = dY.shape[1]
+    if dY.shape[0] != M or tuple(dW.shape) != (K, N) or (rstd is not None and tuple(rstd.shape) != (M,)) or (
+            gamma is not None and tuple(gamma.shape) != (K,)):
+        raise ValueError("shapes: X [M,K], rstd [M], dY [M,N], dW [K,N], gamma [K]")
+    _check("fng_prenorm_rms_bwd_dw", lib().fng_prenorm_rms_bwd_dw(
+        _bf(X, "X"), _f(rstd, "rstd"), _bf(dY, "dY"), _bf(gamma, "gamma"), _bf(dW, "dW"), M, N, K,
+        _stream(stream)))
 
 
 def fng_layernorm_bwd(G, Y, rstd, dZ, stream=None):

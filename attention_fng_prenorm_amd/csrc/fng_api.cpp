@@ -293,6 +293,21 @@ FNG_EXPORT int fng_prenorm_rms_bwd_dx(const void* dY, const void* Wt, const void
   return norm_bwd(false, dY, Wt, X, rstd, true, dX, M, K, N, workspace, workspace_bytes, path, stream);
 }
 
+FNG_EXPORT int fng_prenorm_rms_bwd_dw(const void* X, const float* rstd, const void* dY, const void* gamma, void* dW,
+                                      int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 1 || N < 0 || K < 0) return FNG_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return FNG_OK;
+  if (!X || !dY || !dW || (gamma && !rstd)) return FNG_ERR_INVALID_ARG;
+  if (!aligned16(X) || (rstd && !aligned16(rstd)) || !aligned16(dY) || !aligned16(dW) || (gamma && !aligned16(gamma)))
+    return FNG_ERR_MISALIGNED;
+  if (K % 8 != 0 || N % 8 != 0) return FNG_ERR_MISALIGNED;
+  // 32-bit buffer ranges: X and dY (with one 256-row tile of overrun) below 2 GiB
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FNG_ERR_UNSUPPORTED;
+  if ((M + 256) * K * 2 >= (int64_t)INT32_MAX || (M + 256) * N * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
+  if (K * N >= ((int64_t)1 << 46)) return FNG_ERR_UNSUPPORTED;
+  return fng::launch_prenorm_dw(X, rstd, dY, gamma, dW, M, N, K, as_stream(stream));
+}
+
 FNG_EXPORT int fng_layernorm_bwd(const void* G, const void* Y, const float* rstd, void* dZ, int64_t M, int64_t N,
                                  void* stream) {
   return row_bwd(true, G, Y, rstd, dZ, M, N, false, stream);

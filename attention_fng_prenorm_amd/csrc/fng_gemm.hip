@@ -18,6 +18,14 @@
 //                their accumulators in place.
 //   EPI_PARTIAL  first kernel of the two-pass fallback: un-normalized bf16 Y
 //                plus the same per-row partials; fng_norm.hip finishes it.
+//   EPI_DW       the lazy pre-norm's weight gradient dW = X^T diag(rstd) dY
+//                (section 2's limitations: the normalized X is rebuilt from X
+//                and rstd for the gradients of both operands): the output
+//                rows are X's columns, the contraction runs over X's rows, so
+//                X is kept [contraction][out] in LDS exactly as in memory and
+//                read with transposing reads like W; rstd scales the dY
+//                fragments along the contraction; an optional gain scales the
+//                output rows.
 //
 // Block: 64 * WAVES_M * WAVES_N threads (4 or 8 waves).  Each wave owns a
 // (BM/WAVES_M) x (BN/WAVES_N) sub-tile built from 32x32 MFMA tiles.  The MFMA
@@ -41,7 +49,9 @@ namespace fng {
 enum : int {
   EPI_PLAIN = 0, EPI_PRENORM = 1, EPI_FULLN = 2, EPI_SPLITN = 3, EPI_PARTIAL = 4,
   EPI_BWD_FULLN = 5,   // norm backward over whole rows held by one workgroup
-  EPI_BWD_SPLITN = 6   // norm backward, row sums exchanged like EPI_SPLITN
+  EPI_BWD_SPLITN = 6,  // norm backward, row sums exchanged like EPI_SPLITN
+  EPI_DW = 7,          // weight gradient of the lazy pre-norm (see the header)
+  EPI_TN = 8           // the same product without the rstd scale: X^T dY (its unfused baseline)
 };
 
 struct GemmParams {
@@ -60,10 +70,11 @@ struct GemmParams {
   int tiles_m, tiles_n, total_tiles;
   int n_off, n_end;  // this launch's output columns [n_off, n_end) (plain and lazy GEMM)
   const uint16_t* H;     // norm backward: xhat [M, N], or the norm's input when h_raw
-  const float* rstd_in;  // norm backward: the forward rstd [M]
+  const float* rstd_in;  // norm backward: the forward rstd [M]; weight gradient: the contraction scale [K]
   int h_raw;
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
-  uint32_t spin_limit;
+  uint32_t wait_ticks;     // split-N: bound of one exchange wait, in 100 MHz real-time ticks
+  int poison_on_timeout;   // split-N: rows whose wait timed out are written as NaN
   const float* colsum;  // lazy LayerNorm: [cs_parts][N] partial column sums of W
   int cs_parts;
   const uint16_t* beta;  // post-norm affine: bias [N] (gamma [N] is the gain), or nullptr
@@ -134,8 +145,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   // the post-norms, their affine (per-column gain and bias) in the epilogue
   constexpr bool PG = GAMMA && EPI == EPI_PRENORM;
   constexpr bool AFF = GAMMA && (EPI == EPI_FULLN || EPI == EPI_SPLITN);
-  static_assert(!GAMMA || PG || AFF, "GAMMA only with the lazy pre-norm or the post-norms");
-  using S = Smem<BM, BN, BK, STAGES, PG>;
+  // weight gradient: X transposed in LDS (XT), fp32 scale along the
+  // contraction folded into the W-side fragments (KS), gain on output rows
+  constexpr bool XT = EPI == EPI_DW || EPI == EPI_TN;
+  constexpr bool KS = EPI == EPI_DW;
+  constexpr bool DWG = GAMMA && EPI == EPI_DW;
+  static_assert(!GAMMA || PG || AFF || DWG, "GAMMA only with the lazy pre-norm, the post-norms or dW");
+  constexpr int MC = BM / 8;    // 16-byte chunks per transposed X row of a K tile
+  static_assert(!XT || MC >= 8, "BM >= 64 for the transposed X swizzle");
+  using S = Smem<BM, BN, BK, STAGES, PG || KS>;
   static_assert(S::BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES == 4, "the ring below is written out for 4 stages");
 
@@ -178,17 +196,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   FNG_LDS char* xaddr[FM][BK / 16];
   FNG_LDS char* waddr[FN];
   {
+    const int g = lane >> 4, li = lane & 15;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int q = 0; q < BK / 16; ++q) {
-        const int row = lrow(i);
-        const int kc = 2 * q + hi;
-        uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + row * (BK * 2) + (kc ^ swz_a<KC>(row)) * 16);
+        uint32_t a;
+        if constexpr (XT) {
+          // transposed X: the same transposing-read pattern as W, over BM
+          // output rows (slice q is a plain offset, added at the read)
+          const int n = wm * WM + 32 * ((i + rot) % FM) + 16 * (g & 1) + 4 * (li & 3);
+          const int k0 = 8 * (g >> 1) + (li >> 2);
+          a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + k0 * (BM * 2) + ((n >> 3) ^ swz_b<MC>(k0)) * 16 +
+                                                    (n & 7) * 2);
+        } else {
+          const int row = lrow(i);
+          const int kc = 2 * q + hi;
+          a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + row * (BK * 2) + (kc ^ swz_a<KC>(row)) * 16);
+        }
         asm volatile("" : "+v"(a));
         xaddr[i][q] = reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a));
       }
-    const int g = lane >> 4, li = lane & 15;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = wn * WN + 32 * j + 16 * (g & 1) + 4 * (li & 3);
@@ -231,24 +259,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     // below kOOB so that kOOB offsets are always out of range
     const int64_t xrem = (int64_t)(M - m0) * K * 2;
     const uint32_t xbytes = xrem > 0x7ffffff0LL ? 0x7ffffff0u : (uint32_t)xrem;
-    const i32x4_t xr = dma_rsrc(p.X + (size_t)m0 * K, xbytes);
+    const i32x4_t xr = XT ? dma_rsrc(p.X + m0, (uint32_t)((int64_t)K * M * 2 - (int64_t)m0 * 2))
+                          : dma_rsrc(p.X + (size_t)m0 * K, xbytes);
     const i32x4_t wr = dma_rsrc(p.W + n0, (uint32_t)((int64_t)K * N * 2 - (int64_t)n0 * 2));
     i32x4_t gr;
     if constexpr (PG) gr = dma_rsrc(p.gamma, (uint32_t)K * 2);
+    if constexpr (KS) gr = dma_rsrc(p.rstd_in, (uint32_t)K * 4);
 
     // ---- this lane's share of each K tile's copies ------------------------
     // X: copy i of this wave fills LDS bytes [(wave*A_PER_WAVE + i) KB, +1 KB)
     //    of the stage; lane l writes the 16 B at +16 l, i.e. row r, physical
     //    chunk pc, which holds logical chunk pc ^ swz(r).
     uint32_t a_off[A_PER_WAVE];
-    int a_k[A_PER_WAVE];
+    int a_k[A_PER_WAVE];  // XT: 0 (chunk in range) or kOOB (past M), else the chunk's k offset
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i) {
       const int idx = (wave * A_PER_WAVE + i) * 1024 + lane * 16;
-      const int row = idx / (BK * 2), pc = (idx % (BK * 2)) / 16;
-      const int kc = pc ^ swz_a<KC>(row);
-      a_k[i] = kc * 8;
-      a_off[i] = (uint32_t)(row * K + kc * 8) * 2u;
+      if constexpr (XT) {
+        // transposed X tile [BK][BM]: k row krow, out-row chunk mc (the W scheme)
+        const int krow = idx / (BM * 2), pc = (idx % (BM * 2)) / 16;
+        const int mc = pc ^ swz_b<MC>(krow);
+        a_k[i] = m0 + mc * 8 < M ? 0 : (int)kOOB;
+        a_off[i] = (uint32_t)(krow * M + mc * 8) * 2u;
+      } else {
+        const int row = idx / (BK * 2), pc = (idx % (BK * 2)) / 16;
+        const int kc = pc ^ swz_a<KC>(row);
+        a_k[i] = kc * 8;
+        a_off[i] = (uint32_t)(row * K + kc * 8) * 2u;
+      }
     }
     uint32_t b_off[B_PER_WAVE];
     bool b_ok[B_PER_WAVE];
@@ -299,8 +337,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         // a whole K tile in range: the per-lane offsets are the tile's
         // constants, the K step goes in the scalar offset (no vector work)
 #pragma unroll
-        for (int i = 0; i < A_PER_WAVE; ++i)
-          dma16_so(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, a_off[i], (uint32_t)(kt * BK * 2));
+        for (int i = 0; i < A_PER_WAVE; ++i) {
+          if constexpr (XT)
+            dma16_so(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, a_off[i] | (uint32_t)a_k[i],
+                     (uint32_t)(kt * BK) * (uint32_t)M * 2u);
+          else
+            dma16_so(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, a_off[i], (uint32_t)(kt * BK * 2));
+        }
 #pragma unroll
         for (int i = 0; i < B_PER_WAVE; ++i)
           dma16_so(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024, b_off[i] | (b_ok[i] ? 0u : kOOB),
@@ -308,13 +351,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         if constexpr (PG) {
           if (wave == 0 && lane < KC) dma16(gr, lds + S::gm(s), (uint32_t)(kt * BK + lane * 8) * 2u);
         }
+        if constexpr (KS) {
+          if (wave == 0 && lane < BK / 4) dma16(gr, lds + S::gm(s), (uint32_t)(kt * BK + lane * 4) * 4u);
+        }
         return;
       }
       const uint32_t kt_live = kt < ktiles ? 0u : kOOB;
 #pragma unroll
       for (int i = 0; i < A_PER_WAVE; ++i) {
-        const uint32_t dead = (kt * BK + a_k[i] < K) ? kt_live : kOOB;
-        dma16(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, (a_off[i] + (uint32_t)(kt * BK * 2)) | dead);
+        if constexpr (XT) {
+          // rows past K lie beyond the buffer range: zeros
+          dma16(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024,
+                (a_off[i] + (uint32_t)(kt * BK) * (uint32_t)M * 2u) | (uint32_t)a_k[i] | kt_live);
+        } else {
+          const uint32_t dead = (kt * BK + a_k[i] < K) ? kt_live : kOOB;
+          dma16(xr, lds + S::a(s) + (wave * A_PER_WAVE + i) * 1024, (a_off[i] + (uint32_t)(kt * BK * 2)) | dead);
+        }
       }
 #pragma unroll
       for (int i = 0; i < B_PER_WAVE; ++i) {
@@ -325,6 +377,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       if constexpr (PG) {
         if (wave == 0 && lane < KC)
           dma16(gr, lds + S::gm(s), ((uint32_t)(kt * BK + lane * 8) * 2u) | kt_live);
+      }
+      if constexpr (KS) {
+        if (wave == 0 && lane < BK / 4)
+          dma16(gr, lds + S::gm(s), ((uint32_t)(kt * BK + lane * 4) * 4u) | kt_live);
       }
     };
 
@@ -346,10 +402,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       u32x4_t x[FM];
       u32x4_t w[FN];
       u32x4_t g;
+      f32x4_t s0, s1;  // KS: the contraction scale of this lane's 8 k values
     };
     auto load = [&](int s, int kk, Frags& f) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) f.x[i] = lds_read16(xaddr[i][kk] + (S::a(s) - S::A_OFF));
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (XT) {
+          const FNG_LDS char* xa = xaddr[i][0] + (S::a(s) - S::A_OFF) + kk * 16 * (BM * 2);
+          const u32x2_t lo = lds_read_tr16(xa);
+          const u32x2_t hi2 = lds_read_tr16(xa + 4 * (BM * 2));
+          f.x[i] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+        } else {
+          f.x[i] = lds_read16(xaddr[i][kk] + (S::a(s) - S::A_OFF));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const FNG_LDS char* wa = waddr[j] + S::b(s) + kk * 16 * (BN * 2);
@@ -358,10 +424,32 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         f.w[j] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
       }
       if constexpr (PG) f.g = lds_read16(lds + S::gm(s) + kk * 32 + hi * 16);
+      if constexpr (KS) {
+        f.s0 = __builtin_bit_cast(f32x4_t, lds_read16(lds + S::gm(s) + kk * 64 + hi * 32));
+        f.s1 = __builtin_bit_cast(f32x4_t, lds_read16(lds + S::gm(s) + kk * 64 + hi * 32 + 16));
+      }
     };
     // the vector work on one slice's fragments (ping-pong memory phase; the
     // gain fold never runs there)
+    auto fold_ks = [&](Frags& f) {
+      // weight gradient: rstd of the lane's 8 contraction rows scales its
+      // dY values (words 0..3 hold rows 2e, 2e + 1), once per fragment
+      float sc[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = f.s0[e];
+        sc[4 + e] = f.s1[e];
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = f.w[j][e];
+          f.w[j][e] = pack_bf16(bf16lo(w) * sc[2 * e], bf16hi(w) * sc[2 * e + 1]);
+        }
+    };
     auto vec = [&](Frags& f) {
+      if constexpr (KS) fold_ks(f);
       if constexpr (EPI == EPI_PRENORM) {
         if (ss_owner) {
 #pragma unroll
@@ -398,6 +486,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           for (int e = 0; e < 4; ++e)
             f.w[j][e] = pack_bf16(bf16lo(f.w[j][e]) * bf16lo(f.g[e]), bf16hi(f.w[j][e]) * bf16hi(f.g[e]));
       }
+      if constexpr (KS) fold_ks(f);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -620,6 +709,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         bw_hs[i] = p.h_raw ? bw_r[i] : 1.f;
       }
     }
+    // weight gradient with the forward's gain: a scale per output row
+    float dwg[DWG ? FM : 1];
+    if constexpr (DWG) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = row_of(i);
+        dwg[i] = m < M ? bf16lo((uint32_t)p.gamma[m]) : 0.f;
+      }
+    }
     // 8 B of the staged tile at this lane's (row slot i, columns col_of(j, r4) ..)
     auto stage_addr = [&](int i, int j, int r4) __attribute__((always_inline)) {
       constexpr int NCH = BN / 8;
@@ -794,7 +892,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
             const int nt = p.tiles_n;
             constexpr int BATCH = 8;
             float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f, gsum = 0.f;
-            uint32_t spins = 0;
+            // the wait is bounded in time (the real-time counter runs at a
+            // fixed 100 MHz whatever the shader clock), not in polls
+            const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+            bool timed_out = false;
             for (int q0 = 0; q0 < nt; q0 += BATCH) {
               uint64_t mb[BATCH], vb[BATCH];
               for (;;) {
@@ -812,8 +913,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
                   ready = ready && (uint32_t)(vb[u] >> 32) == ep;
                 }
                 if (ready) break;
-                if (++spins > p.spin_limit) {
+                if (__builtin_amdgcn_s_memrealtime() - t_start > (uint64_t)p.wait_ticks) {
                   __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  timed_out = true;
                   break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -850,6 +952,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               stats[tid * 2 + 0] = 0.f;
               stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(ssum / (float)N + p.eps);
             }
+            if (timed_out && p.poison_on_timeout) stats[tid * 2 + 1] = __builtin_nanf("");
           }
           __syncthreads();
 #pragma unroll
@@ -934,6 +1037,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               float a = acc[i][j][4 * r4 + e];
               // dz = rstd (g - mean(g) - xhat mean(g xhat))
               if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
+              if constexpr (DWG) a *= dwg[i];
               if constexpr (EPI == EPI_PRENORM && LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
               else if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
               if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) {
@@ -1021,7 +1125,8 @@ GemmParams base_params(const GemmCall& c) {
   p.n_off = 0;
   p.n_end = p.N;
   p.group_m = 4;
-  p.spin_limit = 1u << 22;
+  p.wait_ticks = 2000000u;  // 20 ms: peers of a round are co-resident, their waits take microseconds
+  p.poison_on_timeout = c.poison_on_timeout ? 1 : 0;
   return p;
 }
 
@@ -1264,6 +1369,31 @@ int launch_norm_bwd_splitn(const GemmCall& c, const NormBwdArgs& b, bool ln, hip
   // plain launch of a grid the GPU holds at once, as the forward split-N
   return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, true, false>(p, grid, false, s)
             : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, false, false>(p, grid, false, s);
+}
+
+// weight gradient of the lazy pre-norm: dW [K, N] = X^T diag(rstd) dY with
+// X [M, K], dY [M, N]; the kernel's rows are X's columns (K), its
+// contraction X's rows (M)
+int launch_prenorm_dw(const void* X, const float* rstd, const void* dY, const void* gamma, void* dW, int64_t M,
+                      int64_t N, int64_t K, hipStream_t s) {
+  GemmCall c{};
+  c.X = X;
+  c.W = dY;
+  c.gamma = gamma;
+  c.Y = dW;
+  c.M = K;
+  c.N = N;
+  c.K = M;
+  GemmParams p = base_params(c);
+  p.rstd_in = rstd;
+  const bool g = gamma != nullptr;
+  if (small_problem(c)) {
+    if (!rstd) return launch<64, 64, 64, 2, 2, EPI_TN, false, false>(p, 0, false, s);
+    return g ? launch<64, 64, 64, 2, 2, EPI_DW, false, true>(p, 0, false, s)
+             : launch<64, 64, 64, 2, 2, EPI_DW, false, false>(p, 0, false, s);
+  }
+  if (!rstd) return launch_big<EPI_TN, false>(p, s);
+  return g ? launch_big<EPI_DW, true>(p, s) : launch_big<EPI_DW, false>(p, s);
 }
 
 int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s) {

@@ -23,6 +23,7 @@ struct GemmCall {
   uint32_t* done;
   uint32_t* status;
   const void* beta;   // post-norm affine: bf16 [N] bias (with gamma [N] as gain), or nullptr
+  bool poison_on_timeout = false;  // split-N: write NaN rows where an exchange wait timed out
 };
 
 // fng_gemm.hip
@@ -43,6 +44,9 @@ struct NormBwdArgs {
 };
 int launch_norm_bwd_fulln(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s);
 int launch_norm_bwd_splitn(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s);
+// weight gradient of the lazy pre-RMSNorm GEMM: dW [K, N] = (X * rstd (* gamma))^T dY
+int launch_prenorm_dw(const void* X, const float* rstd, const void* dY, const void* gamma, void* dW, int64_t M,
+                      int64_t N, int64_t K, hipStream_t s);
 int splitn_feasible(int64_t M, int64_t N);
 int64_t splitn_tiles_m(int64_t M);
 int64_t splitn_tiles_n(int64_t N);

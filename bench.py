@@ -23,7 +23,7 @@ describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|prenorm_ln|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|ads|copy]
+       [--only prenorm|prenorm_gamma|prenorm_ln|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|dw|ads|copy]
 """
 
 import argparse
@@ -382,6 +382,32 @@ def main():
                           "norm_hidden_pct": round(100.0 * (t["gemm"] + t["norm_bwd"] - t["fused"]) / t["norm_bwd"], 1)}
             del sets, Gb, Wb, Hb, dZ, gtmp, wsb
         kernels["backward_regrouped"] = res
+
+    # ---------------- lazy pre-RMSNorm weight gradient ------------------------------
+    # dW = (rmsnorm(X) * gamma)^T dY with rstd along the contraction inside the
+    # product, against the unfused chain: the row RMSNorm writes rmsnorm(X),
+    # then the plain X^T dY product (same kernel family, no scale)
+    if args.only in (None, "dw"):
+        res = {}
+        for wname in ("prenorm_rms_mlp_dw", "prenorm_rms_mlp_dw_gamma"):
+            sw, dw_in = inputs.make_inputs(wname)
+            Mw, Kw, Nw = sw["M"], sw["K"], sw["N"]
+            Xw, dYw = dev(dw_in["X"]), dev(dw_in["dY"])
+            Gw = dev(dw_in["gamma"]) if dw_in["gamma"] is not None else None
+            rw = torch.from_numpy((1.0 / np.sqrt(np.mean(inputs.bf16_bits_to_f32(dw_in["X"]).astype(np.float64) ** 2,
+                                                         axis=1) + sw["eps"])).astype(np.float32)).cuda()
+            setsw = [(Xw, dYw), (Xw.flip(0).contiguous(), dYw.flip(0).contiguous())]
+            dWw = torch.empty(Kw, Nw, dtype=torch.bfloat16, device="cuda")
+            Xn = torch.empty(Mw, Kw, dtype=torch.bfloat16, device="cuda")
+            t = time_batches({
+                "fused": lambda i: B.fng_prenorm_rms_bwd_dw(setsw[i % 2][0], rw, setsw[i % 2][1], dWw, gamma=Gw),
+                "gemm": lambda i: B.fng_prenorm_rms_bwd_dw(Xn, None, setsw[i % 2][1], dWw),
+                "norm": lambda i: B.fng_rmsnorm(setsw[i % 2][0], Xn, sw["eps"], gamma=Gw),
+            }, args.reps, args.batch)
+            res[wname] = summarize(t, 2.0 * Mw * Nw * Kw, norm_bytes=4.0 * Mw * Kw)
+            log(f"{wname}: " + " ".join(f"{k} {v:.1f}" for k, v in t.items()))
+            del setsw, dWw, Xn, Xw, dYw
+        kernels["prenorm_rms_weight_gradient"] = res
 
     # ---------------- ads-shape sweep: post-LayerNorm GEMM, M = 256k rows ---------
     # K and N from 64 to 2048 (the pages' sweep of the naive full-N regime at small

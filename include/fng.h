@@ -52,7 +52,9 @@ typedef enum {
   FNG_ERR_MISALIGNED = 3,  /* pointer not 16-byte aligned, or K/N not a multiple of 8 */
   FNG_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than *_workspace_bytes() */
   FNG_ERR_HIP = 5,         /* the HIP runtime reported an error for a launch */
-  FNG_ERR_TIMEOUT = 6      /* a split-N exchange wait hit its bound (see below) */
+  FNG_ERR_TIMEOUT = 6      /* a split-N exchange wait hit its bound: 20 ms of real
+                              time per wait (peers of one round are co-resident and
+                              normally arrive within microseconds); see below */
 } fng_status;
 
 /* How a post-norm GEMM reduces statistics over N. */
@@ -175,10 +177,30 @@ int fng_gemm_postnorm_rms_bwd(const void* G, const void* Wt, const void* Y, cons
  * with the forward's sizes: dY [M, N], Wt [N, K] (W transposed, a torch
  * Linear's weight as stored), X and dX [M, K], rstd [M].  The norm runs over
  * K: paths and workspace as above with (M, K, N) in place of (M, N, K).  The
- * weight gradient X^T diag(rstd) dY is a plain GEMM and not part of this call. */
+ * weight gradient is fng_prenorm_rms_bwd_dw below. */
 int fng_prenorm_rms_bwd_dx(const void* dY, const void* Wt, const void* X, const float* rstd, void* dX,
                            int64_t M, int64_t N, int64_t K, void* workspace,
                            size_t workspace_bytes, int path, void* stream);
+
+/* Weight gradient of the lazy pre-RMSNorm GEMM Y = (rmsnorm(X) * gamma) @ W
+ * (section 2's limitations: the normalized X has to be rebuilt from X and rstd
+ * for the gradients of both operands, not only dX):
+ *   dW[k, n] = gamma[k] * sum_m X[m, k] * rstd[m] * dY[m, n]
+ * i.e. dW = (rmsnorm(X) * gamma)^T @ dY with rstd applied along the
+ * contraction (the batch rows) inside the product; rmsnorm(X) is never
+ * written.  X [M, K] bf16 (the forward's input), rstd fp32 [M] (the forward's
+ * rstd_out), dY [M, N] bf16, gamma bf16 [K] or NULL (the forward's gain),
+ * dW [K, N] bf16 (W's layout), fully overwritten.  rstd NULL (gamma NULL
+ * then too) computes the plain X^T @ dY: the product an unfused chain runs
+ * after writing rmsnorm(X) out, here as its baseline.  X, dY, dW, gamma and rstd
+ * 16-byte aligned; K % 8 == 0, N % 8 == 0; M >= 1 (FNG_ERR_INVALID_ARG for
+ * M == 0: an empty batch has a zero gradient the call does not write);
+ * K or N == 0 enqueues nothing.  Products are bf16 MFMAs with fp32
+ * accumulation; each dY value is multiplied by its row's rstd in fp32 and
+ * rounded to bf16 once before the product.  One kernel launch (two with the
+ * tail split of the last partial round of tiles) on `stream`. */
+int fng_prenorm_rms_bwd_dw(const void* X, const float* rstd, const void* dY, const void* gamma,
+                           void* dW, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Norm-sandwiched attention (section 4, FlashNormAttention, in its per-head,

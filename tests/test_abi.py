@@ -267,3 +267,20 @@ def test_binding_refuses_host_tensors():
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.fng_gemm(x, torch.zeros(8, 8, dtype=torch.bfloat16), torch.zeros(4, 8, dtype=torch.bfloat16))
+
+
+def test_weight_gradient_validation(lib):
+    f = lib.fng_prenorm_rms_bwd_dw
+    # (X, rstd, dY, gamma, dW, M, N, K, stream)
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 0, 8, 8, None) == B.FNG_ERR_INVALID_ARG     # empty batch
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 4, -1, 8, None) == B.FNG_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, None, FAKE, 4, 8, 8, None) == B.FNG_ERR_INVALID_ARG     # NULL X
+    assert f(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 8, None) == B.FNG_ERR_INVALID_ARG     # gain without rstd
+    assert f(FAKE, MIS, FAKE, None, FAKE, 4, 8, 8, None) == B.FNG_ERR_MISALIGNED       # rstd
+    assert f(FAKE, FAKE, FAKE, MIS, FAKE, 4, 8, 8, None) == B.FNG_ERR_MISALIGNED       # gamma
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 4, 8, 12, None) == B.FNG_ERR_MISALIGNED     # K % 8
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 4, 12, 8, None) == B.FNG_ERR_MISALIGNED     # N % 8
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 1 << 20, 8, 4096, None) == B.FNG_ERR_UNSUPPORTED  # X over 2 GiB
+    assert f(None, None, None, None, None, 4, 0, 8, None) == B.FNG_OK                  # nothing to write
+    assert f(None, None, None, None, None, 4, 8, 0, None) == B.FNG_OK
+
