@@ -47,6 +47,7 @@ SIGNATURES = {
     "fng_gemm_postnorm_ln": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _int, _vp]),
     "fng_gemm_postnorm_rms": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _int, _vp]),
     "fng_get_kernel_status": (_int, [_vp, _sz, _vp]),
+    "fng_gemm_postnorm_rms_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp]),
     "fng_gemm_postnorm_affine": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp, _sz,
                                         _int, _vp]),
     "fng_norm_attention": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
@@ -207,6 +208,15 @@ def fng_gemm_postnorm_affine(X, W, Y, eps, gamma, beta=None, ln=True, workspace=
         _bf(X, "X"), _bf(W, "W"), _bf(gamma, "gamma"), _bf(beta, "beta"), _bf(Y, "Y"),
         _f(mean_out, "mean_out"), _f(rstd_out, "rstd_out"), M, N, K, eps, 1 if ln else 0, wp, wb, path,
         _stream(stream)))
+
+
+def fng_gemm_postnorm_rms_noalloc(X, W, Y, eps, path=FNG_PATH_AUTO, rstd_out=None, stream=None):
+    M, K = X.shape
+    N = W.shape[1]
+    if W.shape[0] != K or tuple(Y.shape) != (M, N):
+        raise ValueError("shapes: X [M,K], W [K,N], Y [M,N]")
+    _check("fng_gemm_postnorm_rms_noalloc", lib().fng_gemm_postnorm_rms_noalloc(
+        _bf(X, "X"), _bf(W, "W"), _bf(Y, "Y"), _f(rstd_out, "rstd_out"), M, N, K, eps, path, _stream(stream)))
 
 
 def fng_get_kernel_status(workspace, stream=None):

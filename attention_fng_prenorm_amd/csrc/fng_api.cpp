@@ -8,6 +8,8 @@
 
 #include "fng_internal.h"
 
+#include <mutex>
+
 #define FNG_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -89,7 +91,7 @@ int resolve_path(int path, int64_t M, int64_t N, int64_t K) {
 
 int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, float* rstd_out, int64_t M,
              int64_t N, int64_t K, float eps, void* workspace, size_t workspace_bytes, int path,
-             void* stream, const void* gamma = nullptr, const void* beta = nullptr) {
+             void* stream, const void* gamma = nullptr, const void* beta = nullptr, bool poison = false) {
   int st = check_gemm(X, W, Y, M, N, K, eps, true);
   if (st != FNG_OK) return st;
   if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
@@ -97,7 +99,7 @@ int postnorm(bool ln, const void* X, const void* W, void* Y, float* mean_out, fl
   if ((mean_out && !aligned16(mean_out)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
   if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return FNG_ERR_MISALIGNED;
   path = resolve_path(path, M, N, K);
-  GemmCall c{X, W, gamma, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr, beta};
+  GemmCall c{X, W, gamma, Y, mean_out, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr, beta, poison};
   if (path == FNG_PATH_FULLN) {
     if (N > fng::fulln_max_n()) return FNG_ERR_UNSUPPORTED;
     return fng::launch_postnorm_fulln(c, ln, as_stream(stream));
@@ -316,6 +318,69 @@ FNG_EXPORT int fng_layernorm_bwd(const void* G, const void* Y, const float* rstd
 FNG_EXPORT int fng_rmsnorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N,
                                int h_is_input, void* stream) {
   return row_bwd(false, G, H, rstd, dZ, M, N, h_is_input != 0, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The post-RMSNorm GEMM without a caller workspace: the split-N / two-pass
+// workspace lives in a file-scope device array of fixed size, one per GPU
+// (each device that loads the library holds its own copy until the process
+// ends).  Host code never passes the array's name to a kernel or a copy (on
+// the host it is only a stand-in for the symbol): its device address comes
+// from hipGetSymbolAddress, once per device, and is kept per device.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = FNG_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte blocks");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// zero-fill of the array, in a kernel (not hipMemsetAsync, so that a caller
+// capturing the call in a graph records only kernel nodes)
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The array's device address on the current device; on the first call for a
+// device it is looked up and the array cleared on `stream` (the split-N
+// exchange needs a zeroed header once; afterwards each call leaves it
+// consistent for the next).  nullptr on a HIP error.
+void* device_scratch(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint4*>(ptr),
+                     kScratchBytes / 16);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  g_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+
+}  // namespace
+
+FNG_EXPORT int fng_gemm_postnorm_rms_noalloc(const void* X, const void* W, void* Y, float* rstd_out, int64_t M,
+                                             int64_t N, int64_t K, float eps, int path, void* stream) {
+  // validate everything that does not touch the device first
+  int st = check_gemm(X, W, Y, M, N, K, eps, true);
+  if (st != FNG_OK) return st;
+  if (path < FNG_PATH_AUTO || path > FNG_PATH_TWOPASS) return FNG_ERR_INVALID_ARG;
+  if (m_or_n_empty(M, N)) return FNG_OK;
+  const size_t need = fng_gemm_postnorm_workspace_bytes(M, N, K, path);
+  if (need > kScratchBytes) return FNG_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = device_scratch(as_stream(stream));
+    if (!ws) return FNG_ERR_HIP;
+  }
+  return postnorm(false, X, W, Y, nullptr, rstd_out, M, N, K, eps, ws, kScratchBytes, path, stream, nullptr,
+                  nullptr, true);
 }
 
 FNG_EXPORT int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream) {

@@ -145,6 +145,27 @@ int fng_gemm_postnorm_affine(const void* X, const void* W, const void* gamma,
                              int64_t M, int64_t N, int64_t K, float eps, int ln,
                              void* workspace, size_t workspace_bytes, int path, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * post-RMSNorm GEMM of fng_gemm_postnorm_rms without the workspace argument.
+ * Its split-N / two-pass workspace is a fixed array of
+ * FNG_NOALLOC_SCRATCH_BYTES (8 MiB) of device memory inside the library, one
+ * per GPU, held until the process ends; the call allocates nothing.  Paths,
+ * results and limits as fng_gemm_postnorm_rms, plus: a shape whose workspace
+ * (fng_gemm_postnorm_workspace_bytes(M, N, K, path)) exceeds the array
+ * returns FNG_ERR_WORKSPACE before anything is enqueued (the split-N path
+ * fits M x N up to 16384 x 8192).  The first call on a device clears the
+ * array (one small kernel on `stream`); every later call on that GPU reuses
+ * it as the previous call left it.  All calls on one GPU share the one array:
+ * calls that overlap in time (different streams, or other host threads)
+ * race and give wrong results; order them.  A split-N wait that hits its
+ * bound cannot be read back with fng_get_kernel_status (the caller has no
+ * workspace pointer): the rows it concerns are written as NaN instead. */
+#define FNG_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fng_gemm_postnorm_rms_noalloc(const void* X, const void* W, void* Y, float* rstd_out,
+                                  int64_t M, int64_t N, int64_t K, float eps, int path,
+                                  void* stream);
+
 /* Reads the status word a split-N call leaves in `workspace` (synchronizes
  * `stream`).  Returns FNG_OK, FNG_ERR_TIMEOUT, or a validation/HIP error. */
 int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* stream);

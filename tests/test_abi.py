@@ -284,3 +284,17 @@ def test_weight_gradient_validation(lib):
     assert f(None, None, None, None, None, 4, 0, 8, None) == B.FNG_OK                  # nothing to write
     assert f(None, None, None, None, None, 4, 8, 0, None) == B.FNG_OK
 
+
+def test_noalloc_validation(lib):
+    f = lib.fng_gemm_postnorm_rms_noalloc
+    # (X, W, Y, rstd_out, M, N, K, eps, path, stream); every case is rejected
+    # before the library's array is looked up
+    assert f(FAKE, FAKE, FAKE, None, 4, 8, 8, 0.0, 0, None) == B.FNG_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, None, 4, 8, 8, 1e-6, 7, None) == B.FNG_ERR_INVALID_ARG
+    assert f(MIS, FAKE, FAKE, None, 4, 8, 8, 1e-6, 0, None) == B.FNG_ERR_MISALIGNED
+    assert f(FAKE, FAKE, FAKE, None, 4, 4096, 8, 1e-6, B.FNG_PATH_FULLN, None) == B.FNG_ERR_UNSUPPORTED
+    # split-N workspace of 65536 x 8192 is 16 MiB, above the 8 MiB array
+    assert B.fng_gemm_postnorm_workspace_bytes(65536, 8192, 64, B.FNG_PATH_SPLITN) > (8 << 20)
+    assert f(FAKE, FAKE, FAKE, None, 65536, 8192, 64, 1e-6, B.FNG_PATH_SPLITN, None) == B.FNG_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, None, 65536, 8192, 64, 1e-6, B.FNG_PATH_TWOPASS, None) == B.FNG_ERR_WORKSPACE
+    assert f(None, None, None, None, 0, 8, 8, 1e-6, 0, None) == B.FNG_OK
