@@ -42,6 +42,8 @@ SIGNATURES = {
     "fng_prenorm_rms_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp]),
     "fng_gemm_postnorm_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "fng_prenorm_ln_workspace_bytes": (_sz, [_i64, _i64]),
+    "fng_prenorm_rms_gemm_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "fng_prenorm_rms_gemm_ws": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _vp]),
     "fng_prenorm_ln_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _vp]),
     "fng_fulln_max_n": (_i64, []),
     "fng_gemm_postnorm_ln": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp, _sz, _int, _vp]),
@@ -142,6 +144,21 @@ def fng_prenorm_rms_gemm(X, W, Y, eps, gamma=None, rstd_out=None, stream=None):
     _check("fng_prenorm_rms_gemm", lib().fng_prenorm_rms_gemm(
         _bf(X, "X"), _bf(W, "W"), _bf(gamma, "gamma"), _bf(Y, "Y"), _f(rstd_out, "rstd_out"),
         M, N, K, eps, _stream(stream)))
+
+
+def fng_prenorm_rms_gemm_workspace_bytes(M, N, K, has_gamma=False):
+    return lib().fng_prenorm_rms_gemm_workspace_bytes(M, N, K, 1 if has_gamma else 0)
+
+
+def fng_prenorm_rms_gemm_ws(X, W, Y, eps, workspace, gamma=None, rstd_out=None, stream=None):
+    M, K = X.shape
+    N = W.shape[1]
+    if W.shape[0] != K or tuple(Y.shape) != (M, N):
+        raise ValueError("shapes: X [M,K], W [K,N], Y [M,N]")
+    wp, wb = _ws(workspace)
+    _check("fng_prenorm_rms_gemm_ws", lib().fng_prenorm_rms_gemm_ws(
+        _bf(X, "X"), _bf(W, "W"), _bf(gamma, "gamma"), _bf(Y, "Y"), _f(rstd_out, "rstd_out"), M, N, K, eps,
+        wp, wb, _stream(stream)))
 
 
 def fng_prenorm_ln_workspace_bytes(N, K):

@@ -192,6 +192,26 @@ FNG_EXPORT int fng_prenorm_rms_gemm(const void* X, const void* W, const void* ga
   return fng::launch_prenorm(c, as_stream(stream));
 }
 
+FNG_EXPORT size_t fng_prenorm_rms_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_gamma) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  size_t b = ((size_t)M * 4 + 255) & ~(size_t)255;
+  if (has_gamma && fng::prenorm_ws_needs_wg(M, N)) b += (size_t)K * (size_t)N * 2;
+  return b;
+}
+
+FNG_EXPORT int fng_prenorm_rms_gemm_ws(const void* X, const void* W, const void* gamma, void* Y, float* rstd_out,
+                                       int64_t M, int64_t N, int64_t K, float eps, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const int st = check_gemm(X, W, Y, M, N, K, eps, true);
+  if (st != FNG_OK || m_or_n_empty(M, N)) return st;
+  if ((gamma && !aligned16(gamma)) || (rstd_out && !aligned16(rstd_out))) return FNG_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < fng_prenorm_rms_gemm_workspace_bytes(M, N, K, gamma != nullptr))
+    return FNG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
+  GemmCall c{X, W, gamma, Y, nullptr, rstd_out, M, N, K, eps, nullptr, nullptr, nullptr, nullptr};
+  return fng::launch_prenorm_ws(c, workspace, as_stream(stream));
+}
+
 FNG_EXPORT size_t fng_prenorm_ln_workspace_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0) return 0;
   return (size_t)fng::prenorm_ln_parts(K) * (size_t)N * 4;

@@ -18,6 +18,10 @@
 //                their accumulators in place.
 //   EPI_PARTIAL  first kernel of the two-pass fallback: un-normalized bf16 Y
 //                plus the same per-row partials; fng_norm.hip finishes it.
+//   EPI_ROWSCALE the lazy pre-norm's columns that reuse the statistic: another
+//                launch of the same call (EPI_PRENORM, on other columns of the
+//                same rows) accumulated each row's sum of squares beside its
+//                K loop and wrote rstd; these tiles only apply it.
 //   EPI_DW       the lazy pre-norm's weight gradient dW = X^T diag(rstd) dY
 //                (section 2's limitations: the normalized X is rebuilt from X
 //                and rstd for the gradients of both operands): the output
@@ -41,6 +45,8 @@
 // (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as in
 // memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte
 // chunks are XOR-swizzled per row so fragment reads are bank-conflict free.
+#include <algorithm>
+
 #include "fng_device.h"
 #include "fng_internal.h"
 
@@ -51,7 +57,8 @@ enum : int {
   EPI_BWD_FULLN = 5,   // norm backward over whole rows held by one workgroup
   EPI_BWD_SPLITN = 6,  // norm backward, row sums exchanged like EPI_SPLITN
   EPI_DW = 7,          // weight gradient of the lazy pre-norm (see the header)
-  EPI_TN = 8           // the same product without the rstd scale: X^T dY (its unfused baseline)
+  EPI_TN = 8,          // the same product without the rstd scale: X^T dY (its unfused baseline)
+  EPI_ROWSCALE = 9     // lazy pre-norm, second launch: rstd read from the first launch's output
 };
 
 struct GemmParams {
@@ -605,7 +612,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         lds_barrier();
         fence();
       };
-      if constexpr (EPI == EPI_PLAIN || EPI == EPI_PRENORM) {
+      if constexpr (EPI == EPI_PLAIN || EPI == EPI_PRENORM || EPI == EPI_ROWSCALE) {
         // unrolled over the ring so that each stage is a compile-time
         // constant (LDS addresses in the instructions' offset fields, no
         // address adds in the memory phase): ~3 % faster here; with the
@@ -653,6 +660,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     auto row_of = [&](int i) { return m0 + lrow(i); };
 
     float rs_mean[FM], rs_rstd[FM];
+    if constexpr (EPI == EPI_ROWSCALE) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = row_of(i);
+        rs_rstd[i] = m < M ? p.rstd_in[m] : 0.f;
+      }
+    }
     if constexpr (EPI == EPI_PRENORM) {
       // lazy LayerNorm: mean = sum / K, var = sumsq / K - mean^2 (both sums of
       // the raw X; the subtraction loses digits only when |mean| >> spread)
@@ -980,7 +994,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 
     // statistics outputs (one writer per row)
     if constexpr (EPI == EPI_PRENORM || EPI == EPI_FULLN || EPI == EPI_SPLITN) {
-      if (n0 == 0 && wn == 0 && hi == 0) {
+      if (n0 == p.n_off && wn == 0 && hi == 0) {  // the launch's first column tile
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int m = row_of(i);
@@ -1039,7 +1053,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
               if constexpr (DWG) a *= dwg[i];
               if constexpr (EPI == EPI_PRENORM && LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
-              else if constexpr (EPI == EPI_PRENORM) a *= rs_rstd[i];
+              else if constexpr (EPI == EPI_PRENORM || EPI == EPI_ROWSCALE) a *= rs_rstd[i];
               if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) {
                 a = (a - rs_mean[i]) * rs_rstd[i];
                 if constexpr (AFF) {
@@ -1248,7 +1262,94 @@ int launch_prenorm(const GemmCall& c, hipStream_t s) {
     return g ? launch<64, 64, 64, 2, 2, EPI_PRENORM, false, true>(p, 0, false, s)
              : launch<64, 64, 64, 2, 2, EPI_PRENORM, false, false>(p, 0, false, s);
   }
-  return g ? launch_big<EPI_PRENORM, true>(p, s) : launch_big<EPI_PRENORM, false>(p, s);
+  if (g || !c.rstd_out) return g ? launch_big<EPI_PRENORM, true>(p, s) : launch_big<EPI_PRENORM, false>(p, s);
+  // With rstd_out to hand the statistic over, a row's sum of squares is
+  // accumulated beside the K loop of one launch only (section 2 accepts the
+  // redundancy across CTAs as overlapped work; here it would be 56 sums per
+  // row on 4096 x 14336, each lengthening its tile's memory phase): launch A
+  // covers some column blocks of every row block with EPI_PRENORM and writes
+  // rstd_out from its first column tile; launch B, after it on the stream,
+  // covers the other columns with EPI_ROWSCALE, reading rstd_out.
+  //   A = the half-size tiles of the last partial round (tail_split_column),
+  //       run first; B = the whole rounds of 256 x 256 tiles;
+  //   without a partial round and with at least two rounds of tiles: A = the
+  //       first round's worth of column blocks, B = the rest.
+  const int64_t ns = tail_split_column(p.M, p.N);
+  GemmParams a = p, b = p;
+  b.rstd_in = c.rstd_out;
+  if (ns < p.N) {
+    a.n_off = (int)ns;
+    a.n_end = p.N;
+    b.n_off = 0;
+    b.n_end = (int)ns;
+    const int st = launch<kBigBM / 2, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, false>(a, 0, false, s);
+    if (st != FNG_OK) return st;
+    return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_ROWSCALE, false, false>(b, 0, false, s);
+  }
+  const int cus = device_cus();
+  const int64_t tm = (p.M + kBigBM - 1) / kBigBM, tn = (p.N + kBigBN - 1) / kBigBN;
+  if (cus <= 0 || tm * tn < 2 * cus) return launch_big<EPI_PRENORM, false>(p, s);
+  const int64_t na = std::max<int64_t>(1, std::min<int64_t>(tn - 1, cus / tm));
+  a.n_end = (int)(na * kBigBN);
+  b.n_off = a.n_end;
+  const int st = launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, false, false>(a, 0, false, s);
+  if (st != FNG_OK) return st;
+  return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_ROWSCALE, false, false>(b, 0, false, s);
+}
+
+// the gain folded into the rows of W once per call: Wg[k, n] = bf16(gamma[k] * W[k, n]),
+// one rounding, as the in-loop fold makes it.  grid (ceil(N/8 / 1024), K):
+// block (x, k) scales 16-byte chunks x*1024 + t + 256 j (j < 4) of row k.
+__global__ __launch_bounds__(256) void scale_rows_kernel(const uint16_t* W, const uint16_t* gamma, uint16_t* Wg,
+                                                         int K, int N8) {
+  const int k = blockIdx.y;
+  const float g = bf16lo((uint32_t)gamma[k]);
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(W + (size_t)k * N8 * 8);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(Wg + (size_t)k * N8 * 8);
+  const int c0 = blockIdx.x * 1024 + threadIdx.x;
+  u32x4_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (c0 + 256 * j < N8) v[j] = src[c0 + 256 * j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (c0 + 256 * j >= N8) break;
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = v[j][e];
+      o[e] = pack_bf16(bf16lo(w) * g, bf16hi(w) * g);
+    }
+    dst[c0 + 256 * j] = o;
+  }
+}
+
+// lazy pre-norm with a caller workspace: the gain folded into W by one
+// streaming pass (the in-loop fold would scale each W value once per wave
+// that reads it), and the statistic handed between the two launches through
+// rstd_out or the workspace
+bool prenorm_ws_needs_wg(int64_t M, int64_t N) {
+  GemmCall c{};
+  c.M = M;
+  c.N = N;
+  return !small_problem(c);
+}
+
+int launch_prenorm_ws(const GemmCall& c, void* ws, hipStream_t s) {
+  GemmCall d = c;
+  char* base = static_cast<char*>(ws);
+  const size_t rbytes = ((size_t)c.M * 4 + 255) & ~(size_t)255;
+  if (!d.rstd_out) d.rstd_out = reinterpret_cast<float*>(base);
+  if (c.gamma && !small_problem(c)) {
+    uint16_t* wg = reinterpret_cast<uint16_t*>(base + rbytes);
+    const int n8 = (int)(c.N / 8);
+    hipLaunchKernelGGL(scale_rows_kernel, dim3((unsigned)((n8 + 1023) / 1024), (unsigned)c.K), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(c.W), static_cast<const uint16_t*>(c.gamma), wg, (int)c.K, n8);
+    if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
+    d.W = wg;
+    d.gamma = nullptr;
+  }
+  return launch_prenorm(d, s);
 }
 
 int prenorm_ln_parts(int64_t K) { return K >= 8 * 64 ? 8 : (int)((K + 63) / 64); }

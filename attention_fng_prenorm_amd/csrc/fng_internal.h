@@ -29,6 +29,10 @@ struct GemmCall {
 // fng_gemm.hip
 int launch_gemm(const GemmCall& c, hipStream_t s);
 int launch_prenorm(const GemmCall& c, hipStream_t s);
+// the same with a caller workspace (see fng_prenorm_rms_gemm_ws): [rstd, M fp32, 256-B aligned]
+// [gamma-scaled W, K x N bf16, when prenorm_ws_needs_wg(M, N) and a gain is given]
+int launch_prenorm_ws(const GemmCall& c, void* ws, hipStream_t s);
+bool prenorm_ws_needs_wg(int64_t M, int64_t N);
 // lazy LayerNorm pre-norm: colsum receives prenorm_ln_parts(K) x N fp32 partial column sums of W
 int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s);
 int prenorm_ln_parts(int64_t K);

@@ -79,11 +79,38 @@ typedef enum {
  *   Y[m,n]  = rstd[m] * sum_k X[m,k] * gamma[k] * W[k,n]
  * i.e. Y = rmsnorm(X) * gamma @ W.  The statistic uses the raw X; gamma (bf16,
  * [K], optional: NULL means no affine) multiplies along K inside the product.
- * rstd_out: optional fp32 [M].
+ * rstd_out: optional fp32 [M].  With rstd_out given (and no gain), a shape
+ * that takes the big tiles in more than one round runs as two launches: the
+ * one over the last partial round's columns (or the first round's columns)
+ * accumulates each row's sum of squares beside its K loop and writes rstd,
+ * the other applies it; without rstd_out every tile accumulates the
+ * statistic beside its own K loop (the page's redundancy across CTAs).
  * ------------------------------------------------------------------------- */
 int fng_prenorm_rms_gemm(const void* X, const void* W, const void* gamma, void* Y,
                          float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
                          void* stream);
+
+/* The same operation with a caller workspace, for the two things the call
+ * above cannot do without one:
+ *   - with gamma (bf16 [K]), the gain is folded into the rows of W once per
+ *     call by a streaming pass into the workspace (diag(gamma) W rounded to
+ *     bf16, the rounding the in-loop fold makes), then the lazy kernel runs
+ *     as without a gain; the in-loop fold of the call above scales each W
+ *     value once per wave that reads it;
+ *   - with rstd_out NULL, the statistic is still accumulated in one launch
+ *     and handed to the other through the workspace (the call above then
+ *     accumulates it beside every tile's K loop).
+ * workspace: caller-owned device memory of
+ * fng_prenorm_rms_gemm_workspace_bytes(M, N, K, gamma != NULL) bytes, no
+ * initial contents needed, overwritten by each call (FNG_ERR_WORKSPACE if
+ * NULL or smaller): rstd (M fp32, padded to 256 B), then diag(gamma) W when a
+ * gain is given and the shape takes the big tiles.  Shapes, alignment,
+ * limits and results as fng_prenorm_rms_gemm.  Up to three kernel launches
+ * on `stream`. */
+size_t fng_prenorm_rms_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_gamma);
+int fng_prenorm_rms_gemm_ws(const void* X, const void* W, const void* gamma, void* Y,
+                            float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Lazy LayerNorm pre-norm (NOT on the page, which keeps lazy application to
  * RMSNorm because LayerNorm's elementwise part subtracts the mean): Y =

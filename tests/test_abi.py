@@ -298,3 +298,18 @@ def test_noalloc_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, 65536, 8192, 64, 1e-6, B.FNG_PATH_SPLITN, None) == B.FNG_ERR_WORKSPACE
     assert f(FAKE, FAKE, FAKE, None, 65536, 8192, 64, 1e-6, B.FNG_PATH_TWOPASS, None) == B.FNG_ERR_WORKSPACE
     assert f(None, None, None, None, 0, 8, 8, 1e-6, 0, None) == B.FNG_OK
+
+
+def test_prenorm_ws_validation(lib):
+    f = lib.fng_prenorm_rms_gemm_ws
+    # (X, W, gamma, Y, rstd_out, M, N, K, eps, ws, wsb, stream)
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 8, 0.0, FAKE, 1 << 20, None) == B.FNG_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, MIS, FAKE, None, 4, 8, 8, 1e-6, FAKE, 1 << 20, None) == B.FNG_ERR_MISALIGNED
+    assert f(FAKE, FAKE, None, FAKE, None, 4, 8, 8, 1e-6, None, 0, None) == B.FNG_ERR_WORKSPACE
+    need = B.fng_prenorm_rms_gemm_workspace_bytes(4096, 14336, 4096, True)
+    assert need >= 4096 * 14336 * 2 + 4096 * 4      # rstd + the gain-scaled W
+    assert B.fng_prenorm_rms_gemm_workspace_bytes(4096, 14336, 4096, False) == 4096 * 4
+    assert B.fng_prenorm_rms_gemm_workspace_bytes(256, 128, 128, True) == 1024   # small tiles: no scaled W
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4096, 14336, 4096, 1e-6, FAKE, need - 16, None) == B.FNG_ERR_WORKSPACE
+    assert f(FAKE, FAKE, None, FAKE, None, 4096, 14336, 4096, 1e-6, MIS, need, None) == B.FNG_ERR_MISALIGNED
+    assert f(None, None, None, None, None, 0, 8, 8, 1e-6, None, 0, None) == B.FNG_OK

@@ -111,6 +111,73 @@ def test_big_tiles_with_tail_launch(kind):
     assert_parity(y[:, 12288:], ref[:, 12288:], f"{kind} tail columns")
 
 
+@pytest.mark.parametrize("shape", [(2048, 264, 16384), (4096, 264, 14336), (2000, 136, 16360)],
+                         ids=["two_whole_rounds", "whole_rounds_plus_half", "ragged_two_rounds"])
+def test_prenorm_statistic_shared_between_launches(shape):
+    """With rstd_out given, the big-tile lazy pre-norm accumulates each row's
+    sum of squares in one launch (the half-size tiles of the last partial
+    round, or the first round's columns) and the other launch applies the
+    rstd it wrote: against the oracle, on both launches' columns, and
+    against the call that accumulates the statistic in every tile."""
+    M, K, N = shape
+    spec, d = inputs.make_inputs("prenorm_rms_mlp", M=M, K=K, N=N, seed=88)
+    X, W = dev(d["X"]), dev(d["W"])
+    Y, Y2 = empty_bf16(M, N), empty_bf16(M, N)
+    r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    log(f"lazy pre-norm, statistic shared between launches {M}x{K}x{N}")
+    B.fng_prenorm_rms_gemm(X, W, Y, spec["eps"], rstd_out=r)
+    B.fng_prenorm_rms_gemm(X, W, Y2, spec["eps"])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, M - 1],
+                                     np.random.default_rng(M).choice(M, 40, replace=False)]))
+    ref, rref = oracle.prenorm_rms_gemm(f64(d["X"][rows]), f64(d["W"]), spec["eps"])
+    y = host(Y[torch.as_tensor(rows, device="cuda")])
+    assert_parity(y, ref, "shared statistic, all columns")
+    for c0, c1 in ((0, 4096), (N - 2048, N)):
+        assert_parity(y[:, c0:c1], ref[:, c0:c1], f"columns {c0}..{c1}")
+    assert_close_stats(r.cpu().numpy(), oracle.rms_rstd(f64(d["X"]), spec["eps"]), "rstd (all rows)")
+    # the two schemes differ at most by the last bit of rstd
+    diff = (Y.float() - Y2.float()).abs().max().item()
+    assert diff <= 2.0 ** -7 * Y2.float().abs().max().item(), diff
+
+
+@pytest.mark.parametrize("gamma", [False, True], ids=["plain", "gamma"])
+@pytest.mark.parametrize("shape", [(256, 128, 128), (1100, 520, 4000), (4000, 264, 14200)],
+                         ids=["small_tiles", "big_tiles", "big_tiles_tail"])
+@pytest.mark.parametrize("with_rstd", [True, False], ids=["rstd_out", "no_rstd_out"])
+def test_prenorm_ws(shape, gamma, with_rstd):
+    """fng_prenorm_rms_gemm_ws: the gain folded into W by a streaming pass
+    into the workspace (then the lazy kernel without a gain), the statistic
+    handed between launches through rstd_out or the workspace; against the
+    oracle and against fng_prenorm_rms_gemm (the in-loop fold)."""
+    M, K, N = shape
+    spec, d = inputs.make_inputs("prenorm_rms_mlp_gamma" if gamma else "prenorm_rms_mlp", M=M, K=K, N=N, seed=91)
+    X, W = dev(d["X"]), dev(d["W"])
+    g = dev(d["gamma"]) if gamma else None
+    ws = torch.empty(B.fng_prenorm_rms_gemm_workspace_bytes(M, N, K, gamma), dtype=torch.uint8, device="cuda")
+    guard = 2 * N
+    buf = empty_bf16(M * N + guard)
+    buf.view(torch.int16).fill_(0x1234)
+    Y = buf[: M * N].view(M, N)
+    r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda") if with_rstd else None
+    log(f"prenorm ws {shape} gamma={gamma} rstd_out={with_rstd}")
+    B.fng_prenorm_rms_gemm_ws(X, W, Y, spec["eps"], ws, gamma=g, rstd_out=r)
+    Y2 = empty_bf16(M, N)
+    B.fng_prenorm_rms_gemm(X, W, Y2, spec["eps"], gamma=g)
+    torch.cuda.synchronize()
+    assert bool((buf[M * N:].view(torch.int16) == 0x1234).all()), "write past the end of Y"
+    rows = np.unique(np.concatenate([[0, 127, 128, 255, 256, M - 1],
+                                     np.random.default_rng(M + N).choice(M, 40, replace=False)]))
+    rows = rows[rows < M]
+    ref, rref = oracle.prenorm_rms_gemm(f64(d["X"][rows]), f64(d["W"]), spec["eps"], f64(d["gamma"]) if gamma else None)
+    assert_parity(host(Y[torch.as_tensor(rows, device="cuda")]), ref, f"prenorm ws {shape} gamma={gamma}")
+    if with_rstd:
+        assert_close_stats(r.cpu().numpy(), oracle.rms_rstd(f64(d["X"]), spec["eps"]), "rstd (all rows)")
+    # same products, the statistic at most one fp32 rounding apart
+    diff = (Y.float() - Y2.float()).abs().max().item()
+    assert diff <= 2.0 ** -7 * Y2.float().abs().max().item(), diff
+
+
 def test_prenorm_deterministic_and_guarded():
     spec, d = inputs.make_inputs("prenorm_rms_mlp", M=520, K=256, N=2048)
     M, N, K = 520, 2048, 256
