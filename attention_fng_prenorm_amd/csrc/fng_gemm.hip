@@ -7,7 +7,8 @@
 //                in registers for the MFMA, and rstd = 1/sqrt(ss/K + eps) is
 //                applied as a row scale in the epilogue (the row-scale
 //                commutation identity of that section).  An optional gain
-//                gamma[k] is folded into the X fragments after the statistic.
+//                gamma[k] is folded into the W fragments (the statistic uses
+//                the raw X).
 //   EPI_FULLN    section 1, naive fusion: one workgroup's tile spans all N, the
 //                row statistics come straight from the fp32 accumulators.
 //   EPI_SPLITN   section 3, multi-CTA norm without clusters: each workgroup
