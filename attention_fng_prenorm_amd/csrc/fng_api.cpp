@@ -49,8 +49,8 @@ struct Workspace {
   size_t bytes;
 };
 
-// layout: [status (256 B): timeout flag, epoch, finished row blocks] [cnt: tiles_m u32, unused]
-// [done: tiles_m u32] (256-B aligned) [partials]
+// layout: [status (256 B): timeout flag, epoch, finished workgroups] [cnt: tiles_m u32, unused]
+// [done: tiles_m u32, unused] (256-B aligned) [partials]
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 Workspace layout(void* base, int64_t M, int64_t N) {

@@ -71,7 +71,7 @@ struct GemmParams {
   float* rstd_out;
   float* part;       // [tiles_m][tiles_n][BM][2] per-row partials (split-N, two-pass)
   uint32_t* cnt;     // [tiles_m] arrivals (split-N)
-  uint32_t* done;    // [tiles_m] finished readers (split-N)
+  uint32_t* done;    // [tiles_m] unused (kept in the workspace layout)
   uint32_t* status;  // split-N timeout flag
   int M, N, K;
   float eps;
@@ -905,7 +905,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           if (tid < BM) {
             const uint64_t* pb = pt + (size_t)tm * p.tiles_n * (BM * 2) + tid * 2;
             const int nt = p.tiles_n;
-            constexpr int BATCH = 8;
+            constexpr int BATCH = (NEED1 || IS_BWD) ? 8 : 16;  // RMS forward: one round trip for 16 column tiles
             float cn = 0.f, mean = 0.f, m2 = 0.f, ssum = 0.f, gsum = 0.f;
             // the wait is bounded in time (the real-time counter runs at a
             // fixed 100 MHz whatever the shader clock), not in polls
@@ -974,20 +974,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           for (int i = 0; i < FM; ++i) {
             rs_mean[i] = stats[lrow(i) * 2 + 0];
             rs_rstd[i] = stats[lrow(i) * 2 + 1];
-          }
-          // The epoch advances once every row block has been read (the call's
-          // last workgroup to merge): done[tm] counts the row block's readers,
-          // status[2] the finished row blocks.  Off the critical path.
-          if (tid == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(p.done + tm, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (prev == (uint32_t)p.tiles_n - 1u) {
-              __hip_atomic_store(p.done + tm, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              const uint32_t f = __hip_atomic_fetch_add(p.status + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if (f == (uint32_t)p.tiles_m - 1u) {
-                __hip_atomic_store(p.status + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(p.status + 1, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-            }
           }
         }
       }
@@ -1081,6 +1067,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         const int m = m0 + row, n = n0 + ch * 8;
         const u32x4_t v = lds_read16(lds + row * (BN * 2) + ((ch ^ row) & (NCH - 1)) * 16);
         if (m < M && n < N) *reinterpret_cast<u32x4_t*>(p.Y + (size_t)m * N + n) = v;
+      }
+    }
+  }
+  if constexpr (IS_SPLIT) {
+    // The epoch advances once every workgroup of the grid has finished all
+    // its tiles (each read the old epoch at its start and has merged every
+    // partial it waited for): status[2] counts the finished workgroups, the
+    // last one resets it and publishes this call's epoch for the next call
+    // on the workspace.  One atomic per workgroup per call, after its last
+    // store, so no tile's epilogue waits on it.
+    if (tid == 0) {
+      const uint32_t f = __hip_atomic_fetch_add(p.status + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (f == G - 1u) {
+        __hip_atomic_store(p.status + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.status + 1, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
