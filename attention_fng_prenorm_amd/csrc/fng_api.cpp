@@ -143,7 +143,7 @@ int check_fna(const void* Q, const int32_t* off, const void* K, const void* V, c
   if (act != FNG_ACT_SOFTMAX && act != FNG_ACT_GELU) return FNG_ERR_INVALID_ARG;
   if (D != 128) return FNG_ERR_UNSUPPORTED;
   if (B == 0 || T == 0 || max_len == 0 || H == 0) return FNG_OK;
-  if (H != 1 && H != 2 && H != 4) return FNG_ERR_UNSUPPORTED;
+  if (H != 1 && H != 2 && H != 4 && H != 8) return FNG_ERR_UNSUPPORTED;
   if (!Q || !off || !K || !V || !O) return FNG_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (uintptr_t)off % 4 != 0)
     return FNG_ERR_MISALIGNED;
@@ -453,7 +453,7 @@ FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offs
   if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
   int st = check_fna(Q, q_offsets, K, V, out, B, T, max_len_q, Skv, H, D, act);
   if (st != FNG_OK) return st;
-  if (Skv > 128) return FNG_ERR_UNSUPPORTED;
+  if (Skv > 128 || H > 4) return FNG_ERR_UNSUPPORTED;
   if (B == 0 || H == 0) return FNG_OK;
   // dK and dV are written for every batch, even when no query row is processed
   if (!dK || !dV) return FNG_ERR_INVALID_ARG;

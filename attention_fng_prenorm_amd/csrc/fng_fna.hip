@@ -11,8 +11,9 @@
 // the plain activation attention (no norms, no residuals): the unfused
 // baseline's attention.
 //
-// Work split: one workgroup = 4 waves = (4/H row groups) x H heads; wave
-// (g, h) owns 32 query rows of head h.  The page's norms run across heads, so
+// Work split: one workgroup = max(4, H) waves = (waves/H row groups) x H
+// heads; wave (g, h) owns 32 query rows of head h (H = 8: one row group of
+// 32 rows, eight waves, one workgroup per CU).  The page's norms run across heads, so
 // where it exchanges statistics between the CTAs of a cluster, the waves of
 // one workgroup exchange per-(row, head) partials through LDS: (mean, M2) of
 // each head merged with the pairwise formula for the LayerNorm, sums of
@@ -49,7 +50,6 @@ constexpr int kD = 128;
 constexpr int kKT = 32;                 // keys per tile
 constexpr int kRowB = kD * 2;           // bytes of one head's row
 constexpr int kTileB = kKT * kRowB;     // one head's K (or V) tile, [key][d]
-constexpr int kQSB = 32 * 1024;         // a block's query rows: 32 * (4/H) rows x H * 256 B
 constexpr float kLazy = 8.0f;           // running-max hysteresis (log2 units)
 
 enum : int { ACT_SOFTMAX = 0, ACT_GELU = 1 };
@@ -84,23 +84,31 @@ __device__ __forceinline__ float gelu_tanh(float s) {
   return s * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
 }
 
+template <int H>
+constexpr int fna_waves() { return H <= 4 ? 4 : H; }
+
 template <int H, bool NORM, int ACT>
-__global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
-  constexpr int G = 4 / H;                 // row groups
+__global__ __launch_bounds__(64 * fna_waves<H>(), H <= 4 ? 2 : 1) void fna_kernel(FnaParams p) {
+  constexpr int NW = fna_waves<H>();       // waves per workgroup
+  constexpr int NT = 64 * NW;
+  constexpr int G = NW / H;                // row groups
   constexpr int BM = 32 * G;               // query rows per workgroup
   constexpr int RB = H * kRowB;            // bytes per query row (all heads)
+  constexpr int QSB = BM * RB;             // the block's query rows
   constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
-  constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one K or V tile
-  constexpr int NQ = kQSB / 4096;          // ... for the block's query rows
+  constexpr int NK = KVB / (1024 * NW);    // 1 KB copies per wave for one K or V tile
+  constexpr int NQ = QSB / (1024 * NW);    // ... for the block's query rows
   // LDS: K tile | V tile | query rows (their own region unless they fit the V
-  // region, H = 4) | statistics exchange
+  // region, H >= 4) | statistics exchange
+  constexpr bool QV = KVB == QSB;          // query rows fill the V (prologue) and K (epilogue) regions
   constexpr int KREG = 0, VREG = KVB;
-  constexpr int QPRO = (H == 4) ? VREG : 2 * KVB;      // query rows in the prologue
-  constexpr int QEPI = (H == 4) ? KREG : 2 * KVB;      // residual rows / output
-  constexpr int MAIN = (H == 4) ? 2 * KVB : 2 * KVB + kQSB;
-  static_assert(BM * RB == kQSB, "query block size");
-  static_assert(H != 4 || KVB == kQSB, "query block fills the K or V region");
-  static_assert(MAIN + BM * H * 8 <= 80 * 1024, "two workgroups per CU");
+  constexpr int QPRO = QV ? VREG : 2 * KVB;      // query rows in the prologue
+  constexpr int QEPI = QV ? KREG : 2 * KVB;      // residual rows / output
+  constexpr int MAIN = QV ? 2 * KVB : 2 * KVB + QSB;
+  static_assert(H != 4 || QV, "H = 4: the query block fills the K or V region");
+  static_assert(H <= 4 || (QV && NK * 1024 * NW == KVB && NQ * 1024 * NW == QSB), "H = 8 layout");
+  static_assert(H > 4 || MAIN + BM * H * 8 <= 80 * 1024, "two workgroups per CU");
+  static_assert(MAIN + BM * H * 8 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[MAIN + BM * H * 8];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
   FNG_LDS float* xch = (FNG_LDS float*)(lds + MAIN);  // [BM][H][2] statistics exchange
@@ -159,8 +167,8 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
   // ---- prologue: the block's query rows and the first key tile -------------
   copy_q(lds + QPRO);
   copy_kv(false, 0);
-  if constexpr (H != 4) copy_kv(true, 0);
-  wait_vmcnt<(H == 4 ? NK : 2 * NK)>();  // this wave's query copies have landed
+  if constexpr (!QV) copy_kv(true, 0);
+  wait_vmcnt<(QV ? NK : 2 * NK)>();  // this wave's query copies have landed
   lds_barrier();
 
   // lane holds d = 16kk + 8hi + 0..7 of its row and head: the MFMA B operand
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
         ql[kk][e] = pack_bf16(x0 - bf16lo(hw), x1 - bf16hi(hw));
       }
   }
-  if constexpr (H == 4) {
+  if constexpr (QV) {
     lds_barrier();  // every wave has read its query rows: the V region is free
     copy_kv(true, 0);
   }
@@ -471,8 +479,8 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
   lds_barrier();
   // whole rows back to HBM: 16 B per lane, rows of the batch only
 #pragma unroll
-  for (int i = 0; i < kQSB / (16 * 256); ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < QSB / (16 * NT); ++i) {
+    const int c = tid + NT * i;
     const int r = c / (RB / 16), lc = c % (RB / 16);
     const int q = qb * BM + r;
     if (q < len && r0 + q < p.T) {
@@ -484,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void fna_kernel(FnaParams p) {
 
 template <int H>
 int launch_h(const FnaParams& p, bool norm, int act, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.qblocks)), block(256);
+  const dim3 grid((unsigned)(p.B * p.qblocks)), block(64 * fna_waves<H>());
   if (norm) {
     if (act == ACT_GELU) hipLaunchKernelGGL((fna_kernel<H, true, ACT_GELU>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((fna_kernel<H, true, ACT_SOFTMAX>), grid, block, 0, s, p);
@@ -514,13 +522,14 @@ int launch_fna(const FnaCall& c, bool norm, hipStream_t s) {
   p.scale = c.act == FNG_ACT_SOFTMAX ? c.sm_scale * 1.4426950408889634f : c.sm_scale;
   p.eps_ln = c.eps_ln;
   p.eps_rms = c.eps_rms;
-  const int bm = 32 * (4 / (int)c.H);
+  const int bm = c.H <= 4 ? 32 * (4 / (int)c.H) : 32;
   p.qblocks = (int)((c.max_len + bm - 1) / bm);
   const int act = c.act == FNG_ACT_GELU ? ACT_GELU : ACT_SOFTMAX;
   switch (c.H) {
     case 1: return launch_h<1>(p, norm, act, s);
     case 2: return launch_h<2>(p, norm, act, s);
     case 4: return launch_h<4>(p, norm, act, s);
+    case 8: return launch_h<8>(p, norm, act, s);
     default: return FNG_ERR_UNSUPPORTED;
   }
 }

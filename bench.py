@@ -385,6 +385,34 @@ def main():
             "speedup_vs_unfused": round(base / t["fused"], 2),
         }
         del sets6, O6, st6, ln6, at6, y6
+        # the page's benchmark varies the head count: the same recipe at 1, 2, 4 and 8 heads
+        sweep = {}
+        for Hh in (1, 2, 4, 8):
+            sh, dh = inputs.make_inputs("flash_norm_attention", H=Hh)
+            Qh, Kh, Vh = dev(dh["Q"]), dev(dh["K"]), dev(dh["V"])
+            offh = torch.from_numpy(dh["offsets"]).to("cuda")
+            Th = Qh.shape[0]
+            Oh, lnh, ath, yh = (torch.empty_like(Qh) for _ in range(4))
+
+            def tail_h(i):
+                torch.add(ath, lnh, out=yh)
+                B.fng_rmsnorm(yh.view(Th, Hh * 128), ath.view(Th, Hh * 128), sh["eps_rms"])
+                torch.add(ath, Qh, out=Oh)
+            th = time_batches({
+                "fused": lambda i: B.fng_flash_norm_attention(Qh, offh, Kh, Vh, Oh, sh["max_len"], sh["eps_ln"],
+                                                              sh["eps_rms"], 0.0, sh["act"]),
+                "ln": lambda i: B.fng_layernorm(Qh.view(Th, Hh * 128), lnh.view(Th, Hh * 128), sh["eps_ln"]),
+                "attn": lambda i: B.fng_jagged_attention(lnh, offh, Kh, Vh, ath, sh["max_len"], 0.0, sh["act"]),
+                "tail": tail_h,
+            }, max(4, args.reps // 4), args.batch)
+            bh = 2.0 * (2 * Th * Hh * 128 + 2 * sh["B"] * sh["Skv"] * Hh * 128) + 12.0 * Th
+            uh = th["ln"] + th["attn"] + th["tail"]
+            sweep[f"H{Hh}"] = {"fused_us": round(th["fused"], 2), "unfused_us": round(uh, 2),
+                               "speedup_vs_unfused": round(uh / th["fused"], 2),
+                               "fused_frac_hbm": round(bh / th["fused"] / 1e3 / PEAK_HBM_GBS, 4)}
+            log(f"fna H={Hh}: fused {th['fused']:.1f} us, unfused {uh:.1f} us")
+            del Qh, Kh, Vh, Oh, lnh, ath, yh
+        kernels["flash_norm_attention"]["heads_sweep"] = sweep
 
     # ---------------- FlashNormAttention backward ---------------------------------
     # dQ, dK, dV of the jagged FlashNormAttention from the forward's output and

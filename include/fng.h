@@ -284,7 +284,8 @@ int fng_norm_attention(const void* Q, const void* K, const void* V, void* out,
  *   checked on the host; the kernel never reads or writes outside Q, out and
  *   the statistics buffers whatever they hold, but rows a batch owns beyond
  *   max_len_q, and rows no batch owns, are left unwritten.
- * H must be 1, 2 or 4 and D 128; Skv >= 1.  Optional fp32 [T] statistics:
+ * H must be 1, 2, 4 or 8 and D 128; Skv >= 1 (H = 8: one workgroup of eight
+ * waves per 32 query rows, one wave per head).  Optional fp32 [T] statistics:
  * ln mean and rstd, rms rstd (the backward below takes them).  Products are
  * bf16 MFMAs with fp32 accumulation: K and V as stored, the normalized
  * queries (pre-multiplied by sm_scale, times log2(e) for softmax) and the
@@ -317,7 +318,7 @@ int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void
  * contents needed (the first kernel writes per-row intermediates that the
  * second reads: the gradient at the RMSNorm input in fp16, and for the
  * softmax the log-sum-exp per (row, head)); FNG_ERR_WORKSPACE if NULL or
- * smaller.  Limits: H 1, 2 or 4; D 128; 1 <= Skv <= 128 (the page's short-KV
+ * smaller.  Limits: H 1, 2 or 4 (H = 8: FNG_ERR_UNSUPPORTED); D 128; 1 <= Skv <= 128 (the page's short-KV
  * case: a query row's scores over all keys stay in registers).  Products are
  * fp16 MFMAs with fp32 accumulation (K and V converted from bf16, so below
  * 65504 in magnitude).  Two kernel launches on `stream`. */

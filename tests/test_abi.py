@@ -146,8 +146,8 @@ def test_flash_norm_attention_validation(lib):
         return f(Q, off, K, V, O, None, None, None, b, T, L, skv, H, D, scale, e1, e2, act, None)
 
     assert call(D=64) == B.FNG_ERR_UNSUPPORTED
-    assert call(H=3) == B.FNG_ERR_UNSUPPORTED            # heads must be 1, 2 or 4
-    assert call(H=8) == B.FNG_ERR_UNSUPPORTED
+    assert call(H=3) == B.FNG_ERR_UNSUPPORTED            # heads must be 1, 2, 4 or 8
+    assert call(H=16) == B.FNG_ERR_UNSUPPORTED
     assert call(skv=0) == B.FNG_ERR_INVALID_ARG
     assert call(T=-1) == B.FNG_ERR_INVALID_ARG
     assert call(act=2) == B.FNG_ERR_INVALID_ARG
@@ -198,6 +198,7 @@ def test_flash_norm_attention_bwd_validation(lib):
     assert call(skv=129) == B.FNG_ERR_UNSUPPORTED        # short KV: at most 128 keys
     assert call(D=64) == B.FNG_ERR_UNSUPPORTED
     assert call(H=3) == B.FNG_ERR_UNSUPPORTED
+    assert call(H=8) == B.FNG_ERR_UNSUPPORTED             # the forward takes 8 heads, the backward 1, 2 or 4
     assert call(act=7) == B.FNG_ERR_INVALID_ARG
     assert call(scale=float("nan")) == B.FNG_ERR_INVALID_ARG
     assert call(ws=None) == B.FNG_ERR_WORKSPACE

@@ -258,7 +258,7 @@ def fna_planted(H, Skv, seed, dout=False, kinds=inputs.ROW_KINDS, shift=24.0):
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-@pytest.mark.parametrize("H", [2, 4])
+@pytest.mark.parametrize("H", [2, 4, 8])
 def test_fna_degenerate_rows(H, act):
     spec, d, rows, where = fna_planted(H, 72, seed=520 + H)
     log(f"FlashNormAttention degenerate rows H={H} act={act}: {where}")

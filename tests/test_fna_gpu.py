@@ -65,7 +65,7 @@ def run_fna(d, max_len, act, eps_ln=1e-5, eps_rms=1e-6, scale=SCALE, T_extra=0, 
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-@pytest.mark.parametrize("H", [1, 2, 4])
+@pytest.mark.parametrize("H", [1, 2, 4, 8])
 def test_fna_reduced(H, act):
     spec, d = jagged(H, 72)
     log(f"fna H={H} act={act} lengths={LENGTHS} Skv=72")
@@ -79,7 +79,7 @@ def test_fna_reduced(H, act):
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-@pytest.mark.parametrize("H", [1, 4])
+@pytest.mark.parametrize("H", [1, 4, 8])
 def test_jagged_attention_reduced(H, act):
     spec, d = jagged(H, 72, seed=8)
     log(f"jagged attention H={H} act={act}")
@@ -89,11 +89,12 @@ def test_jagged_attention_reduced(H, act):
                   mae=2e-3 * max(np.mean(np.abs(ref)), 0.8) / 0.8)
 
 
+@pytest.mark.parametrize("H", [2, 8])
 @pytest.mark.parametrize("Skv", [1, 32, 33, 200])
-def test_fna_key_counts(Skv):
+def test_fna_key_counts(Skv, H):
     lengths = [5, 70, 0, 3]
     for act in ("softmax", "gelu"):
-        spec, d = jagged(2, Skv, lengths=lengths, seed=9)
+        spec, d = jagged(H, Skv, lengths=lengths, seed=9)
         log(f"fna Skv={Skv} act={act}")
         O, _ = run_fna(d, spec["max_len"], act)
         ref, _, _, _ = oracle.flash_norm_attention(f64(d["Q"]), d["offsets"], f64(d["K"]), f64(d["V"]),
@@ -182,6 +183,28 @@ def test_fna_full_size_sampled(full_inputs, act):
         fna_parity(y[r0:r1], ref, f"fna full size batch {b} (len {r1 - r0})")
         assert_close_stats(st[2].cpu().numpy()[r0:r1], r2s, "fna rms rstd", rtol=3e-3)
     # every row: out - x has unit RMS over all heads (up to eps and bf16 rounding)
+    r = (O.float() - dev(d["Q"]).float()).reshape(O.shape[0], -1)
+    rms = torch.sqrt(torch.mean(r * r, dim=1)).cpu().numpy()
+    assert np.max(np.abs(rms - 1.0)) < 1e-2, np.max(np.abs(rms - 1.0))
+
+
+@pytest.mark.parametrize("act", ["gelu", "softmax"])
+def test_fna_eight_heads_full_batches_sampled(act):
+    """Eight heads (H * 128 = 1024 values per row: one workgroup of eight
+    waves per 32 rows) on the full 768-batch recipe, sampled batches."""
+    spec, d = inputs.make_inputs("flash_norm_attention", H=8)
+    off = d["offsets"]
+    log(f"fna H=8 full batches T={off[-1]} act={act}")
+    O, st = run_fna(d, spec["max_len"], act, spec["eps_ln"], spec["eps_rms"])
+    y = host(O)
+    lengths = np.diff(off)
+    for b in [0, int(np.argmax(lengths)), int(np.argmin(lengths)), 500, spec["B"] - 1]:
+        r0, r1 = int(off[b]), int(off[b + 1])
+        ref, mu, r1s, r2s = oracle.flash_norm_attention(
+            f64(d["Q"][r0:r1]), np.array([0, r1 - r0]), f64(d["K"][b:b + 1]), f64(d["V"][b:b + 1]),
+            spec["eps_ln"], spec["eps_rms"], SCALE, act)
+        fna_parity(y[r0:r1], ref, f"fna H=8 batch {b} (len {r1 - r0})")
+        assert_close_stats(st[1].cpu().numpy()[r0:r1], r1s, "fna H=8 ln rstd")
     r = (O.float() - dev(d["Q"]).float()).reshape(O.shape[0], -1)
     rms = torch.sqrt(torch.mean(r * r, dim=1)).cpu().numpy()
     assert np.max(np.abs(rms - 1.0)) < 1e-2, np.max(np.abs(rms - 1.0))
