@@ -86,6 +86,10 @@ struct GemmParams {
   const float* colsum;  // lazy LayerNorm: [cs_parts][N] partial column sums of W
   int cs_parts;
   const uint16_t* beta;  // post-norm affine: bias [N] (gamma [N] is the gain), or nullptr
+  // split-N placement: each XCD's tiles of a round form sn_rh row blocks x
+  // sn_cw column tiles, sn_g XCDs sharing the row blocks (sn_cw 0: every
+  // column tile of a row block on one XCD)
+  int sn_cw, sn_rh, sn_g;
 };
 
 // LDS layout: the W parts of all ring stages, then the X parts, then the
@@ -249,8 +253,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   for (int t = (int)slot; t < p.total_tiles; t += (int)G) {
     int tm, tn;
     if constexpr (IS_SPLIT) {
-      tm = t / p.tiles_n;
-      tn = t % p.tiles_n;
+      // a round is G consecutive tiles = whole row blocks, so every wait is
+      // on a peer of the same round
+      if (p.sn_cw > 0) {
+        const int r = t / (int)G, s = t - r * (int)G;
+        const int per = (int)G / 8;  // slots per XCD (slot -> XCD as in xcd_remap)
+        const int x = s / per, j = s % per;
+        tm = r * ((int)G / p.tiles_n) + (x / p.sn_g) * p.sn_rh + j % p.sn_rh;
+        tn = (x % p.sn_g) * p.sn_cw + j / p.sn_rh;
+      } else {
+        tm = t / p.tiles_n;
+        tn = t % p.tiles_n;
+      }
     } else {
       const int per_group = p.group_m * p.tiles_n;
       const int g = t / per_group;
@@ -1393,6 +1407,23 @@ int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
   return launch_norm<64, 512, 32, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
 }
 
+// Split-N placement.  With all column tiles of a row block on one XCD (16 at
+// N = 4096), an XCD's tiles of a round read all of W (8 MiB at K = 1024)
+// through its 4 MB L2.  Rectangles of 8 column tiles x (slots / 8) row blocks
+// per XCD, two or more XCDs sharing a row block, cut the XCD's unique bytes
+// per round (4 x 0.5 + 8 x 0.5 MB instead of 2 x 0.5 + 16 x 0.5 MB at
+// 16384 x 1024 x 4096).  Only for whole rounds on a grid of 8 equal XCD
+// shares; the merge order is by column tile, so the output is bitwise the same.
+void splitn_placement(GemmParams& p, int grid, int total, int tn) {
+  constexpr int cw = 8;
+  if (grid % 8 != 0 || total % grid != 0 || tn % cw != 0) return;
+  const int per = grid / 8;
+  if (per % cw != 0 || 8 % (tn / cw) != 0) return;
+  p.sn_cw = cw;
+  p.sn_rh = per / cw;
+  p.sn_g = tn / cw;
+}
+
 int splitn_feasible(int64_t M, int64_t N) {
   const int cap = max_coresident_grid<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_SPLITN, false, false>();
   if (cap <= 0) return 0;
@@ -1418,6 +1449,7 @@ int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
   // a whole number of row blocks per round, so every wait is on a co-resident peer
   int grid = (cap / tn) * tn;
   if (grid > total) grid = total;
+  splitn_placement(p, grid, total, tn);
   // A plain launch: the grid fits the GPU at once (the occupancy above, one
   // workgroup per CU), so every workgroup is dispatched while its peers wait.
   // A cooperative launch would guarantee it even on a GPU shared with other
@@ -1469,6 +1501,7 @@ int launch_norm_bwd_splitn(const GemmCall& c, const NormBwdArgs& b, bool ln, hip
   if (cap <= 0 || tn > cap) return FNG_ERR_UNSUPPORTED;
   int grid = (cap / tn) * tn;
   if (grid > total) grid = total;
+  splitn_placement(p, grid, total, tn);
   // plain launch of a grid the GPU holds at once, as the forward split-N
   return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, true, false>(p, grid, false, s)
             : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_SPLITN, false, false>(p, grid, false, s);
