@@ -627,12 +627,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         lds_barrier();
         fence();
       };
-      if constexpr (EPI == EPI_PLAIN || EPI == EPI_PRENORM || EPI == EPI_ROWSCALE) {
-        // unrolled over the ring so that each stage is a compile-time
-        // constant (LDS addresses in the instructions' offset fields, no
-        // address adds in the memory phase): ~3 % faster here; with the
-        // post-norm and backward epilogues the unrolled loop made the
-        // allocator spill more and the kernels slower (measured)
+      // unrolled over the ring so that each stage is a compile-time constant
+      // (LDS addresses in the instructions' offset fields, no address adds in
+      // the memory phase): 2-3 % faster (split-N post-RMSNorm: 142.2 -> 138.9
+      // us at 16384 x 1024 x 4096); with the norm backward, the weight
+      // gradient and the 128 x 512 full-N tile the unrolled loop makes the
+      // allocator spill and the kernels slower (measured)
+      constexpr bool UNROLL = EPI == EPI_PLAIN || EPI == EPI_PRENORM || EPI == EPI_ROWSCALE || EPI == EPI_SPLITN ||
+                              EPI == EPI_PARTIAL || EPI == EPI_TN || (EPI == EPI_FULLN && BN <= 256);
+      if constexpr (UNROLL) {
         for (int t = 0; t < ktiles; t += 4) {
           tile(t, 0);
           if (t + 1 < ktiles) tile(t + 1, 1);
