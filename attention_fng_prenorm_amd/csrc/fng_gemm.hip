@@ -126,6 +126,12 @@ __device__ __forceinline__ int swz_a(int row) {
 }
 template <int NC>
 __device__ __forceinline__ int swz_b(int krow) { return ((krow & 3) << 2) & (NC - 1); }
+//   Paired X rows (two K tiles of one row, 2*BK*2 = 128 B at BK 32; two rows
+//   share a window): XOR the 8-chunk index with (row / 2) % 8, so the 8 even
+//   and the 8 odd rows of a read each cover all 8 units of their half.  The
+//   XOR may flip chunk bit 2, so the second K tile's address is the first's
+//   XOR 64, not a constant offset.
+__device__ __forceinline__ int swz_px(int row) { return (row >> 1) & 7; }
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int EPI, bool LN, bool GAMMA>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams p) {
@@ -178,6 +184,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   // (about 50 vector instructions per slice) would make the memory phase the
   // longer one (measured slower).
   constexpr bool PP = NWAVES == 8 && WAVES_M == 2 && BK == 32 && !PG;
+  // X copied two K tiles at a time (ping-pong loop of the plain, lazy pre-norm
+  // and row-scale GEMMs): with BK 32 one K tile of an X row is 64 B, and
+  // copies of 64-byte row pieces cost half-line L2 requests (1.5x the
+  // requests of the same product on 512-byte rows, measured: 37.6 M vs 25.2 M
+  // per 4096 x 4096 x 12288 launch, with 16x the address stalls).  Paired,
+  // each group of 8 lanes reads one whole 128-byte line: the X copies of
+  // tiles 2j and 2j+1 ride with the issue of tile 2j+1 into the stages of
+  // both, laid out [row][2 tiles x 4 chunks] (swz_px).  The split-N, full-N
+  // and 256-row lazy pre-norm kernels keep the single-tile layout: the second
+  // set of fragment addresses made their allocator spill, and split-N was
+  // slower (measured).
+  constexpr bool PX = PP && (EPI == EPI_PLAIN || EPI == EPI_ROWSCALE || (EPI == EPI_PRENORM && BM <= 128));
+  constexpr int AX = PX ? 2 * A_PER_WAVE : A_PER_WAVE;  // X copies per wave per (odd) issue
+  static_assert(!PX || (STAGES == 4 && BK * 4 == 128), "paired X rows are 128 B in a 4-stage ring");
   constexpr int RED = IS_BWD ? S::BYTES : 0;
   constexpr int EXTRA = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
   static_assert(S::BYTES + EXTRA <= 160 * 1024, "LDS budget with the backward's reductions");
@@ -221,6 +241,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           const int k0 = 8 * (g >> 1) + (li >> 2);
           a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + k0 * (BM * 2) + ((n >> 3) ^ swz_b<MC>(k0)) * 16 +
                                                     (n & 7) * 2);
+        } else if constexpr (PX) {
+          // the first tile of a pair; the second is this address XOR 64
+          const int row = lrow(i);
+          const int kc = 2 * q + hi;
+          a = (uint32_t)reinterpret_cast<uintptr_t>(lds + S::A_OFF + row * (BK * 4) + (kc ^ swz_px(row)) * 16);
         } else {
           const int row = lrow(i);
           const int kc = 2 * q + hi;
@@ -292,12 +317,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     // X: copy i of this wave fills LDS bytes [(wave*A_PER_WAVE + i) KB, +1 KB)
     //    of the stage; lane l writes the 16 B at +16 l, i.e. row r, physical
     //    chunk pc, which holds logical chunk pc ^ swz(r).
-    uint32_t a_off[A_PER_WAVE];
-    int a_k[A_PER_WAVE];  // XT: 0 (chunk in range) or kOOB (past M), else the chunk's k offset
+    uint32_t a_off[AX];
+    int a_k[AX];  // XT: 0 (chunk in range) or kOOB (past M), else the chunk's k offset
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) {
-      const int idx = (wave * A_PER_WAVE + i) * 1024 + lane * 16;
-      if constexpr (XT) {
+    for (int i = 0; i < AX; ++i) {
+      const int idx = (wave * AX + i) * 1024 + lane * 16;
+      if constexpr (PX) {
+        // paired: 8 rows of 128 B per copy; lanes 8r .. 8r+7 read one row's
+        // 128-byte line (each group of 4 lanes one contiguous half)
+        const int row = idx / (BK * 4), pc = (idx % (BK * 4)) / 16;
+        const int c = pc ^ swz_px(row);
+        a_k[i] = c * 8;
+        a_off[i] = (uint32_t)(row * K + c * 8) * 2u;
+      } else if constexpr (XT) {
         // transposed X tile [BK][BM]: k row krow, out-row chunk mc (the W scheme)
         const int krow = idx / (BM * 2), pc = (idx % (BM * 2)) / 16;
         const int mc = pc ^ swz_b<MC>(krow);
@@ -340,6 +372,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       return (uint32_t)(((int64_t)(m0 + row) * N + n0 + ch * 8) * 2);
     };
     auto issue = [&](int kt, int s) {
+      if constexpr (PX) {
+        // odd tiles first copy X of the pair (kt - 1, kt) into pair slot s / 2
+        // (both its stages are free: this issue refills the stage of the tile
+        // before the current one, and the pair's other stage held the tile
+        // before that), then W of kt; even tiles copy only their W
+        if (kt & 1) {
+          const int k0 = (kt - 1) * BK;
+          FNG_LDS char* xs = lds + S::A_OFF + (s / 2) * (2 * S::A_STAGE);
+          if (kt - 1 < ktiles && k0 + 2 * BK <= K) {
+#pragma unroll
+            for (int i = 0; i < AX; ++i) dma16_so(xr, xs + (wave * AX + i) * 1024, a_off[i], (uint32_t)(k0 * 2));
+          } else {
+            const uint32_t live = kt - 1 < ktiles ? 0u : kOOB;
+#pragma unroll
+            for (int i = 0; i < AX; ++i) {
+              const uint32_t dead = (k0 + a_k[i] < K) ? live : kOOB;
+              dma16(xr, xs + (wave * AX + i) * 1024, (a_off[i] + (uint32_t)(k0 * 2)) | dead);
+            }
+          }
+        }
+        if (kt < ktiles && (kt + 1) * BK <= K) {
+#pragma unroll
+          for (int i = 0; i < B_PER_WAVE; ++i)
+            dma16_so(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024, b_off[i] | (b_ok[i] ? 0u : kOOB),
+                     (uint32_t)(kt * BK) * (uint32_t)N * 2u);
+        } else {
+          const uint32_t kt_live = kt < ktiles ? 0u : kOOB;
+#pragma unroll
+          for (int i = 0; i < B_PER_WAVE; ++i) {
+            const uint32_t dead = b_ok[i] ? kt_live : kOOB;
+            dma16(wr, lds + S::b(s) + (wave * B_PER_WAVE + i) * 1024,
+                  (b_off[i] + (uint32_t)(kt * BK) * (uint32_t)N * 2u) | dead);
+          }
+        }
+        return;
+      }
       if constexpr (IS_BWD) {
         if (kt >= ktiles) {
 #pragma unroll
@@ -434,6 +502,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
           const u32x2_t lo = lds_read_tr16(xa);
           const u32x2_t hi2 = lds_read_tr16(xa + 4 * (BM * 2));
           f.x[i] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+        } else if constexpr (PX) {
+          // the second tile of a pair at the first's address XOR 64
+          const uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(xaddr[i][kk]) ^ ((s & 1) ? 64u : 0u);
+          f.x[i] = lds_read16(reinterpret_cast<FNG_LDS char*>(static_cast<uintptr_t>(a)) + (s / 2) * (2 * S::A_STAGE));
         } else {
           f.x[i] = lds_read16(xaddr[i][kk] + (S::a(s) - S::A_OFF));
         }
@@ -560,7 +632,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     // (measured: the split-N LayerNorm mainloop took 85 instead of ~56 us per
     // tile of 256 x 256 x 2048).
 #pragma unroll
-    for (int i = 0; i < A_PER_WAVE; ++i) asm volatile("" : "+v"(a_off[i]), "+v"(a_k[i]));
+    for (int i = 0; i < AX; ++i) asm volatile("" : "+v"(a_off[i]), "+v"(a_k[i]));
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i) asm volatile("" : "+v"(b_off[i]));
 #pragma unroll
@@ -597,7 +669,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         load(st, 0, f0);
         load(st, 1, f1);
         issue(t + 3, (st + 3) & 3);
-        wait_vmcnt<2 * LOADS>();
+        // this wave's copies of tile t+1 have landed; with paired X an even
+        // tile's X came with the issue of the odd tile after it, so only the
+        // W copies of two issues may still be in flight
+        if (PX && (st & 1)) wait_vmcnt<2 * B_PER_WAVE>();
+        else wait_vmcnt<2 * LOADS>();
         // the sums of squares wait for their fragments: after the copies are
         // issued, so the copies do not wait behind the LDS reads (measured)
         fence();
@@ -613,7 +689,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       issue(0, 0);
       issue(1, 1);
       issue(2, 2);
-      wait_vmcnt<2 * LOADS>();
+      wait_vmcnt<PX ? 2 * B_PER_WAVE : 2 * LOADS>();
       lds_barrier();
       // every wave runs M(t), C(t) with a barrier after each; the second
       // half starts one barrier late and the first half ends one barrier
