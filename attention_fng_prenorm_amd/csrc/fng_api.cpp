@@ -263,6 +263,13 @@ int norm_bwd(bool ln, const void* G, const void* Wt, const void* H, const float*
   if (!aligned16(H) || reinterpret_cast<uintptr_t>(rstd) % 4 != 0) return FNG_ERR_MISALIGNED;
   if (M * N * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;  // the saved tensor's 32-bit copy offsets
   if (path == FNG_PATH_TWOPASS) return FNG_ERR_UNSUPPORTED;        // the backward has no two-pass path
+  // automatic choice: above 256 columns the full-N backward tiles (64 x 512,
+  // one workgroup per CU) are slower than split-N's 256 x 256 tiles (regrouped
+  // LayerNorm backward at 262144 x 512, K = 256: 294 vs 228 us), so split-N
+  // is taken there whenever the caller gave a workspace of its size
+  if (path == FNG_PATH_AUTO && N > 256 && workspace &&
+      workspace_bytes >= fng_gemm_postnorm_workspace_bytes(M, N, K, FNG_PATH_SPLITN) && fng::splitn_feasible(M, N))
+    path = FNG_PATH_SPLITN;
   path = resolve_path(path, M, N, K);
   if (path == FNG_PATH_TWOPASS) return FNG_ERR_UNSUPPORTED;
   GemmCall c{G, Wt, nullptr, dZ, nullptr, nullptr, M, N, K, 1.f, nullptr, nullptr, nullptr, nullptr};

@@ -25,12 +25,13 @@ T_norm of the pages, also against torch's own norm kernel where ours runs
 below 80 % of HBM bandwidth; the small pre-RMSNorm workload (256 x 128 x 128)
 in microseconds, eager and as a replayed HIP graph; and the pages'
 ads-shape sweep of the post-LayerNorm GEMM (M = 256k rows, K and N from 64 to
-2048).  The roofline object
+2048) and of its regrouped backward on the same shapes.  The roofline object
 describes the headline kernel; cpu_baseline times the fp64 oracle on a row
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       [--only prenorm|prenorm_gamma|prenorm_ln|prenorm_small|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|dw|ads]
+       [--only prenorm|prenorm_gamma|prenorm_ln|prenorm_small|postnorm_ln|postnorm_rms|attention|fna|fnabwd|bwd|dw|ads
+               |ads_bwd]
        [--profile copy|prenorm|prenorm_gamma|gemm|postnorm_ln|postnorm_rms|attention|fna|dw]  (kernel launches only,
        for rocprofv3 counter passes)
 """
@@ -470,6 +471,35 @@ def main():
                 f"backward kernels {t['norms']:.1f} us)")
             del sets7, dQ7, dK7, dV7, ws7, O7, tmp7
         kernels["flash_norm_attention_backward"] = {"T": T7, "B": s7["B"], "Skv": s7["Skv"], "H": H7, **res7}
+        # the head sweep of the backward (GELU), the recipe of the forward's sweep;
+        # the backward kernels take H <= 4
+        sweep7 = {}
+        for Hh in (1, 2, 4):
+            sh, dh = inputs.make_inputs("flash_norm_attention_bwd", H=Hh)
+            Qh, Kh, Vh, Gh = dev(dh["Q"]), dev(dh["K"]), dev(dh["V"]), dev(dh["dOut"])
+            offh = torch.from_numpy(dh["offsets"]).to("cuda")
+            Th = Qh.shape[0]
+            Oh = torch.empty_like(Qh)
+            sth = [torch.empty(Th, dtype=torch.float32, device="cuda") for _ in range(3)]
+            B.fng_flash_norm_attention(Qh, offh, Kh, Vh, Oh, sh["max_len"], sh["eps_ln"], sh["eps_rms"], 0.0, "gelu",
+                                       *sth)
+            dQh, dKh, dVh, O2h = (torch.empty_like(x) for x in (Qh, Kh, Vh, Qh))
+            wsh = torch.empty(B.fng_flash_norm_attention_bwd_workspace_bytes(Th, Hh), dtype=torch.uint8,
+                              device="cuda")
+            th = time_batches({
+                "bwd": lambda i: B.fng_flash_norm_attention_bwd(Qh, offh, Kh, Vh, Oh, Gh, sth[0], sth[1], sth[2],
+                                                                dQh, dKh, dVh, sh["max_len"], workspace=wsh,
+                                                                act="gelu"),
+                "fwd": lambda i: B.fng_flash_norm_attention(Qh, offh, Kh, Vh, O2h, sh["max_len"], sh["eps_ln"],
+                                                            sh["eps_rms"], 0.0, "gelu", *sth),
+            }, max(4, args.reps // 4), args.batch)
+            bh = 2.0 * (4 * Th * Hh * 128 + 4 * sh["B"] * sh["Skv"] * Hh * 128) + 12.0 * Th
+            sweep7[f"H{Hh}"] = {"T": Th, "bwd_us": round(th["bwd"], 2), "fwd_us": round(th["fwd"], 2),
+                                "bwd_over_fwd": round(th["bwd"] / th["fwd"], 2),
+                                "bwd_frac_hbm": round(bh / th["bwd"] / 1e3 / PEAK_HBM_GBS, 4)}
+            log(f"fna backward H={Hh} (gelu): {th['bwd']:.1f} us, forward {th['fwd']:.1f} us")
+            del Qh, Kh, Vh, Gh, Oh, sth, dQh, dKh, dVh, O2h, wsh
+        kernels["flash_norm_attention_backward"]["heads_sweep_gelu"] = sweep7
 
     # ---------------- backward by fusion regrouping --------------------------------
     # dZ = norm_bwd(G @ Wt) fused (full-N / split-N epilogue) against the plain
@@ -582,6 +612,57 @@ def main():
             "fused_us": fused_us, "unfused_us": unfused_us, "norm_hidden_pct": hidden,
         }
         log("ads sweep post-LN (M=262144): rows K, columns N, norm latency hidden %")
+        for Ka, rh in zip(dims, hidden):
+            log(f"  K={Ka:5d}: " + " ".join(f"{h:7.1f}" for h in rh))
+
+    # ---------------- ads-shape sweep of the regrouped post-LayerNorm backward ----
+    # the multi-CTA backward on the forward sweep's shapes: dZ = layernorm_bwd(G @ Wt)
+    # over N, G [M, K] the upstream gradient, Y [M, N] the saved forward output,
+    # against our GEMM + the row LayerNorm backward; G ~ N(0,1), Wt ~ N(0,1/K),
+    # Y ~ N(0,1), rstd = exp(N(0, 0.25)) drawn on the device (the backward
+    # workloads' recipe)
+    if args.only in (None, "ads_bwd"):
+        Ms = 262144
+        dims = [64, 128, 256, 512, 1024, 2048]
+        gen = torch.Generator(device="cuda").manual_seed(2027)
+        rb = torch.exp(0.5 * torch.randn(Ms, device="cuda", generator=gen))
+        fused_us, unfused_us, hidden, paths = [], [], [], []
+        for Ka in dims:
+            Ga = torch.randn(Ms, Ka, device="cuda", generator=gen).to(torch.bfloat16)
+            rf, ru, rh, rp = [], [], [], []
+            for Na in dims:
+                Wt = (torch.randn(Ka, Na, device="cuda", generator=gen) / math.sqrt(Ka)).to(torch.bfloat16)
+                Ha = torch.randn(Ms, Na, device="cuda", generator=gen).to(torch.bfloat16)
+                dZa = torch.empty(Ms, Na, dtype=torch.bfloat16, device="cuda")
+                gta = torch.empty_like(dZa)
+                # a workspace of the split-N size: the automatic path takes
+                # split-N from 257 columns on when it is given one
+                nb = B.fng_gemm_postnorm_workspace_bytes(Ms, Na, Ka, B.FNG_PATH_SPLITN)
+                wsa = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
+                t = time_batches({
+                    "fused": lambda i: B.fng_gemm_postnorm_ln_bwd(Ga, Wt, Ha, rb, dZa, wsa),
+                    "gemm": lambda i: B.fng_gemm(Ga, Wt, gta),
+                    "norm_bwd": lambda i: B.fng_layernorm_bwd(gta, Ha, rb, dZa),
+                }, 3, 5)
+                assert B.fng_get_kernel_status(wsa) == B.FNG_OK
+                if args.only == "ads_bwd":
+                    log(f"  K={Ka} N={Na}: " + " ".join(f"{k} {v:.1f}" for k, v in t.items()))
+                rf.append(round(t["fused"], 1))
+                ru.append(round(t["gemm"] + t["norm_bwd"], 1))
+                rh.append(round(100.0 * (t["gemm"] + t["norm_bwd"] - t["fused"]) / t["norm_bwd"], 1))
+                rp.append("splitn" if Na > 256 else "fulln")
+                del Wt, Ha, dZa, gta, wsa
+            fused_us.append(rf)
+            unfused_us.append(ru)
+            hidden.append(rh)
+            paths.append(rp)
+            del Ga
+            torch.cuda.empty_cache()
+        kernels["ads_sweep_postnorm_ln_backward"] = {
+            "M": Ms, "K_rows": dims, "N_cols": dims, "path": paths,
+            "fused_us": fused_us, "unfused_us": unfused_us, "norm_hidden_pct": hidden,
+        }
+        log("ads sweep post-LN backward (M=262144): rows K, columns N, norm latency hidden %")
         for Ka, rh in zip(dims, hidden):
             log(f"  K={Ka:5d}: " + " ".join(f"{h:7.1f}" for h in rh))
 

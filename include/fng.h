@@ -210,8 +210,12 @@ int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* s
  * statistic (fp32).  dZ [M, N] is the gradient at the norm's input.  `path`:
  * FNG_PATH_AUTO, FULLN (N <= fng_fulln_max_n()) or SPLITN (workspace of
  * fng_gemm_postnorm_workspace_bytes(M, N, K, FNG_PATH_SPLITN) bytes, zeroed
- * once, as the forward's); TWOPASS returns FNG_ERR_UNSUPPORTED.  M*N*2 must be
- * below 2^31.  G, Wt, Y, dZ 16-byte aligned; rstd 4-byte aligned.
+ * once, as the forward's); TWOPASS returns FNG_ERR_UNSUPPORTED.  AUTO takes
+ * the forward's choice, except that for N > 256 it takes split-N whenever
+ * `workspace` holds at least the split-N size (faster there than the full-N
+ * backward tiles); a smaller or NULL workspace keeps the forward's choice.
+ * M*N*2 must be below 2^31.  G, Wt, Y, dZ 16-byte aligned; rstd 4-byte
+ * aligned.
  * ------------------------------------------------------------------------- */
 int fng_gemm_postnorm_ln_bwd(const void* G, const void* Wt, const void* Y, const float* rstd, void* dZ,
                              int64_t M, int64_t N, int64_t K, void* workspace,

@@ -93,6 +93,32 @@ def test_postnorm_bwd_tall_narrow():
         scaled_parity(host(dZ)[rows], ref, f"tall bwd N={N}")
 
 
+# the ads shapes of the multi-CTA backward (section 3, "What about backward?"),
+# at 2048 rows: the automatic path (full-N up to its width, split-N above)
+ADS_BWD_KN = [(64, 64), (2048, 128), (256, 256), (64, 512), (512, 512), (1024, 1024), (256, 2048), (2048, 2048)]
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("K,N", ADS_BWD_KN, ids=[f"K{k}_N{n}" for k, n in ADS_BWD_KN])
+def test_postnorm_bwd_ads_shapes(K, N, kind):
+    M = 2048
+    spec, d = inputs.make_inputs("postnorm_ln_smalln_bwd", M=M, K=K, N=N, seed=K * 11 + N)
+    log(f"ads shape post-norm bwd {kind} M={M} K={K} N={N}")
+    dZ = run_postnorm_bwd(d, kind, B.FNG_PATH_AUTO)
+    ref = oracle.gemm_postnorm_backward(f64(d["G"]), f64(d["Wt"]), f64(d["H"]), d["rstd"], kind)
+    scaled_parity(host(dZ), ref, f"ads {kind} bwd K={K} N={N}")
+    if 256 < N <= B.fng_fulln_max_n():
+        # with a workspace the automatic path took split-N here; without one it
+        # keeps the forward's choice (full-N)
+        G, Wt, H = dev(d["G"]), dev(d["Wt"]), dev(d["H"])
+        r = torch.from_numpy(d["rstd"]).to("cuda")
+        dZ2 = empty_bf16(M, N)
+        fn = B.fng_gemm_postnorm_ln_bwd if kind == "ln" else B.fng_gemm_postnorm_rms_bwd
+        fn(G, Wt, H, r, dZ2, workspace=None, path=B.FNG_PATH_AUTO)
+        torch.cuda.synchronize()
+        scaled_parity(host(dZ2), ref, f"ads {kind} bwd K={K} N={N} without a workspace")
+
+
 @pytest.mark.parametrize("path", [B.FNG_PATH_FULLN, B.FNG_PATH_SPLITN], ids=["fulln", "splitn"])
 @pytest.mark.parametrize("shape", [(300, 520, 256), (260, 136, 1000)], ids=["k256", "k1000"])
 def test_prenorm_bwd_dx_reduced(shape, path):
