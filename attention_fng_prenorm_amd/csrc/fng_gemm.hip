@@ -78,7 +78,9 @@ struct GemmParams {
   int tiles_m, tiles_n, total_tiles;
   int n_off, n_end;  // this launch's output columns [n_off, n_end) (plain and lazy GEMM)
   const uint16_t* H;     // norm backward: xhat [M, N], or the norm's input when h_raw
-  const float* rstd_in;  // norm backward: the forward rstd [M]; weight gradient: the contraction scale [K]
+  const float* rstd_in;  // norm backward: the forward rstd [M]; weight gradient: the contraction scale [K];
+                         // lazy pre-norm row scale: rstd [M] from the statistic launch
+  const float* mean_in;  // lazy LayerNorm row scale: mean [M] from the statistic launch
   int h_raw;
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
   uint32_t wait_ticks;     // split-N: bound of one exchange wait, in 100 MHz real-time ticks
@@ -759,6 +761,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
       for (int i = 0; i < FM; ++i) {
         const int m = row_of(i);
         rs_rstd[i] = m < M ? p.rstd_in[m] : 0.f;
+        if constexpr (LN) rs_mean[i] = m < M ? p.mean_in[m] : 0.f;
       }
     }
     if constexpr (EPI == EPI_PRENORM) {
@@ -789,8 +792,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
     }
     // lazy LayerNorm: the column sums of W at this lane's columns, the
     // partials merged in a fixed order
-    float csum[EPI == EPI_PRENORM && LN ? FN : 1][4][4];
-    if constexpr (EPI == EPI_PRENORM && LN) {
+    constexpr bool LAZY_LN = (EPI == EPI_PRENORM || EPI == EPI_ROWSCALE) && LN;
+    float csum[LAZY_LN ? FN : 1][4][4];
+    if constexpr (LAZY_LN) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1132,7 +1136,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
               // dz = rstd (g - mean(g) - xhat mean(g xhat))
               if constexpr (IS_BWD) a = bw_r[i] * (a - rs_mean[i] - xh[e] * rs_rstd[i]);
               if constexpr (DWG) a *= dwg[i];
-              if constexpr (EPI == EPI_PRENORM && LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
+              if constexpr (LAZY_LN) a = (a - rs_mean[i] * csum[j][r4][e]) * rs_rstd[i];
               else if constexpr (EPI == EPI_PRENORM || EPI == EPI_ROWSCALE) a *= rs_rstd[i];
               if constexpr (EPI == EPI_FULLN || EPI == EPI_SPLITN) {
                 a = (a - rs_mean[i]) * rs_rstd[i];
@@ -1459,7 +1463,32 @@ int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s) {
   p.colsum = colsum;
   p.cs_parts = parts;
   if (small_problem(c)) return launch<64, 64, 64, 2, 2, EPI_PRENORM, true, false>(p, 0, false, s);
-  return launch_big<EPI_PRENORM, false, true>(p, s);
+  if (!c.mean_out || !c.rstd_out) return launch_big<EPI_PRENORM, false, true>(p, s);
+  // with mean_out and rstd_out to hand the statistics over: the split of
+  // launch_prenorm, the row-scale launch applying diag(rstd) (acc - mean colsum)
+  const int64_t ns = tail_split_column(p.M, p.N);
+  GemmParams a = p, b = p;
+  b.rstd_in = c.rstd_out;
+  b.mean_in = c.mean_out;
+  b.rstd_out = nullptr;
+  b.mean_out = nullptr;
+  if (ns < p.N) {
+    a.n_off = (int)ns;
+    a.n_end = p.N;
+    b.n_end = (int)ns;
+    const int st = launch<kBigBM / 2, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, true, false>(a, 0, false, s);
+    if (st != FNG_OK) return st;
+    return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_ROWSCALE, true, false>(b, 0, false, s);
+  }
+  const int cus = device_cus();
+  const int64_t tm = (p.M + kBigBM - 1) / kBigBM, tn = (p.N + kBigBN - 1) / kBigBN;
+  if (cus <= 0 || tm * tn < 2 * cus) return launch_big<EPI_PRENORM, false, true>(p, s);
+  const int64_t na = std::max<int64_t>(1, std::min<int64_t>(tn - 1, cus / tm));
+  a.n_end = (int)(na * kBigBN);
+  b.n_off = a.n_end;
+  const int st = launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_PRENORM, true, false>(a, 0, false, s);
+  if (st != FNG_OK) return st;
+  return launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_ROWSCALE, true, false>(b, 0, false, s);
 }
 
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {

@@ -219,14 +219,15 @@ def main():
         setsl = [(XL, sets[0][1], sets[0][2]), (XL.flip(0).contiguous(), sets[1][1], sets[1][2])]
         wsl = torch.empty(B.fng_prenorm_ln_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
         Xn = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
-        t = time_batches({
+        mul, rsl = (torch.empty(M, dtype=torch.float32, device="cuda") for _ in range(2))
+        t = time_batches({   # with mean_out and rstd_out, as a training step keeps them
             "fused": lambda i: B.fng_prenorm_ln_gemm(setsl[i % 2][0], setsl[i % 2][1], setsl[i % 2][2],
-                                                     sl["eps"], wsl),
+                                                     sl["eps"], wsl, mean_out=mul, rstd_out=rsl),
             "gemm": lambda i: B.fng_gemm(setsl[i % 2][0], setsl[i % 2][1], setsl[i % 2][2]),
             "norm": lambda i: B.fng_layernorm(setsl[i % 2][0], Xn, sl["eps"]),
         }, args.reps, args.batch)
         kernels["prenorm_ln_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K, spread=iqr(t))
-        del setsl, XL, wsl
+        del setsl, XL, wsl, mul, rsl
 
     # ---------------- small pre-RMSNorm workload (256 x 128 x 128): microseconds ----
     if args.only in (None, "prenorm_small"):

@@ -124,7 +124,9 @@ int fng_prenorm_rms_gemm_ws(const void* X, const void* W, const void* gamma, voi
  * caller-owned device memory of fng_prenorm_ln_workspace_bytes(N, K) bytes
  * (no initial contents needed; overwritten by each call), FNG_ERR_WORKSPACE if
  * NULL or smaller.  Two kernel launches (three with the tail split) on
- * `stream`. */
+ * `stream`; with both mean_out and rstd_out, as for fng_prenorm_rms_gemm, the
+ * sums are taken by one launch over some column blocks and the other launch
+ * applies diag(rstd) (X W - mean colsum(W)) from its mean_out / rstd_out. */
 size_t fng_prenorm_ln_workspace_bytes(int64_t N, int64_t K);
 int fng_prenorm_ln_gemm(const void* X, const void* W, void* Y, float* mean_out,
                         float* rstd_out, int64_t M, int64_t N, int64_t K, float eps,

@@ -35,8 +35,9 @@ def run(d, eps, M, N, K, ws=None):
     return Y, mu, r
 
 
-@pytest.mark.parametrize("shape", [(256, 128, 128), (300, 1000, 1000), (1100, 520, 4000), (4000, 264, 14200)],
-                         ids=["small", "ragged_small_tile", "ragged_large_tile", "tail_launch"])
+@pytest.mark.parametrize("shape", [(256, 128, 128), (300, 1000, 1000), (1100, 520, 4000), (4000, 264, 14200),
+                                   (4096, 264, 16384)],
+                         ids=["small", "ragged_small_tile", "ragged_large_tile", "tail_launch", "rounds_split"])
 def test_prenorm_ln_reduced(shape):
     M, K, N = shape
     spec, d = inputs.make_inputs("prenorm_ln_mlp", M=M, K=K, N=N, seed=51)
@@ -50,11 +51,13 @@ def test_prenorm_ln_reduced(shape):
     assert_close_stats(r.cpu().numpy(), ar, "lazy LN rstd")
 
 
+@pytest.mark.parametrize("shape", [(512, 1024, 1024), (4096, 256, 8192)], ids=["one_launch", "row_scale_split"])
 @pytest.mark.parametrize("shift", [8.0, 32.0])
-def test_prenorm_ln_far_off_mean(shift):
+def test_prenorm_ln_far_off_mean(shift, shape):
     # every row's mean is `shift` spreads away from zero: X W and mean colsum(W)
-    # are both `shift` times the result and cancel in the epilogue
-    M, K, N = 512, 1024, 1024
+    # are both `shift` times the result and cancel in the epilogue (at the
+    # larger shape in the row-scale launch, from the statistic launch's mean)
+    M, K, N = shape
     rng = np.random.Generator(np.random.PCG64(52))
     z = rng.standard_normal((M, K), dtype=np.float32)
     sign = np.where(rng.standard_normal((M, 1)) > 0, 1.0, -1.0).astype(np.float32)
@@ -63,10 +66,11 @@ def test_prenorm_ln_far_off_mean(shift):
     d = {"X": inputs.f32_to_bf16_bits(x), "W": inputs.f32_to_bf16_bits(w)}
     log(f"lazy LN pre-norm, |mean| = {shift} x spread")
     Y, mu, r = run(d, 1e-5, M, N, K)
-    ref, _, rr = oracle.prenorm_ln_gemm(f64(d["X"]), f64(d["W"]), 1e-5)
-    e = assert_parity(host(Y), ref, f"lazy LN shift {shift}")
+    rows = np.arange(M) if M * N <= 4e6 else np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(2).choice(M, 40, replace=False)]))
+    ref, _, rr = oracle.prenorm_ln_gemm(f64(d["X"][rows]), f64(d["W"]), 1e-5)
+    e = assert_parity(host(Y)[rows], ref, f"lazy LN shift {shift}")
     log(f"shift {shift}: {e}")
-    assert_close_stats(r.cpu().numpy(), rr, "lazy LN rstd, shifted rows", rtol=2e-3 if shift > 10 else 2e-4)
+    assert_close_stats(r.cpu().numpy()[rows], rr, "lazy LN rstd, shifted rows", rtol=2e-3 if shift > 10 else 2e-4)
 
 
 def test_prenorm_ln_full_size_sampled():
