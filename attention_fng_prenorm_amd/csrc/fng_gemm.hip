@@ -22,7 +22,8 @@
 //   EPI_ROWSCALE the lazy pre-norm's columns that reuse the statistic: another
 //                launch of the same call (EPI_PRENORM, on other columns of the
 //                same rows) accumulated each row's sum of squares beside its
-//                K loop and wrote rstd; these tiles only apply it.
+//                K loop and wrote rstd (and, for the lazy LayerNorm, the mean);
+//                these tiles only apply it (with LN: rstd (acc - mean colsum)).
 //   EPI_DW       the lazy pre-norm's weight gradient dW = X^T diag(rstd) dY
 //                (section 2's limitations: the normalized X is rebuilt from X
 //                and rstd for the gradients of both operands): the output
@@ -46,6 +47,10 @@
 // (k contiguous) and read with ds_read_b128; W is kept [k][n] exactly as in
 // memory and read k-contiguous per lane with ds_read_b64_tr_b16.  16-byte
 // chunks are XOR-swizzled per row so fragment reads are bank-conflict free.
+// In the plain, row-scale and 128-row lazy pre-norm tiles the X rows of two
+// consecutive K tiles are copied together, one 128-byte line per row.
+// Split-N places each round's tiles as rectangles of row blocks x 8 column
+// tiles per XCD (splitn_placement).
 #include <algorithm>
 
 #include "fng_device.h"
