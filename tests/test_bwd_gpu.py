@@ -79,6 +79,18 @@ def test_postnorm_bwd_splitn_wide(kind):
         assert np.max(np.abs(got - ref.sum(axis=1))) < 0.05 * N ** 0.5
 
 
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_postnorm_bwd_splitn_placement(kind):
+    # 2048 x 4096: one round of 8 row blocks x 16 column tiles placed as
+    # 2 x 8 rectangles per XCD, two XCDs sharing each row block; all rows
+    M, K, N = 2048, 200, 4096
+    spec, d = inputs.make_inputs("postnorm_rms_largen_bwd", M=M, K=K, N=N, seed=46)
+    log(f"postnorm bwd split-N placement {kind} {M}x{K}x{N}")
+    dZ = run_postnorm_bwd(d, kind, B.FNG_PATH_SPLITN)
+    ref = oracle.gemm_postnorm_backward(f64(d["G"]), f64(d["Wt"]), f64(d["H"]), d["rstd"], kind)
+    scaled_parity(host(dZ), ref, f"{kind} bwd split-N placement")
+
+
 def test_postnorm_bwd_tall_narrow():
     # tall tiles for >= 65536 rows (N <= 64, 128, 256)
     for N in (40, 104, 200):

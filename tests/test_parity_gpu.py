@@ -378,6 +378,24 @@ def test_postnorm_three_paths_agree_at_n256(ln):
     assert np.max(np.abs(outs[0] - outs[1])) <= 2 * 2.0 ** -7 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("ln", [True, False], ids=["ln", "rms"])
+def test_postnorm_splitn_placement_shared_row_blocks(ln):
+    """Split-N on 2048 x 4096 outputs: 8 row blocks x 16 column tiles = 128
+    tiles in one round, placed as rectangles of 2 row blocks x 8 column tiles
+    per XCD, two XCDs sharing each row block (their partials merged across
+    XCDs); ragged K; every row against the oracle."""
+    M, K, N = 2048, 264, 4096
+    spec, d = inputs.make_inputs("postnorm_rms_largen", M=M, K=K, N=N, seed=77)
+    eps = 1e-5 if ln else 1e-6
+    log(f"split-N placement ln={ln} M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, eps, M, N, K, ln, B.FNG_PATH_SPLITN)
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"]), f64(d["W"]), eps, "ln" if ln else "rms")
+    assert_parity(host(Y), ref, f"split-N placement ln={ln}")
+    assert_close_stats(r.cpu().numpy(), rref, "split-N placement rstd")
+    if ln:
+        assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
+
+
 def test_postnorm_ln_splitn_shifted_mean():
     """Rows whose mean is large against their spread (the merge of per-slice
     (count, mean, M2) must not cancel)."""
