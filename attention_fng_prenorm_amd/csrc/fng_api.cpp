@@ -447,7 +447,7 @@ FNG_EXPORT int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets,
 }
 
 FNG_EXPORT size_t fng_flash_norm_attention_bwd_workspace_bytes(int64_t T, int64_t H) {
-  if (T <= 0 || H <= 0 || H > 4) return 0;
+  if (T <= 0 || (H != 1 && H != 2 && H != 4 && H != 8)) return 0;
   return fng::fna_bwd_workspace_bytes(T, H);
 }
 
@@ -460,7 +460,7 @@ FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offs
   if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
   int st = check_fna(Q, q_offsets, K, V, out, B, T, max_len_q, Skv, H, D, act);
   if (st != FNG_OK) return st;
-  if (Skv > 128 || H > 4) return FNG_ERR_UNSUPPORTED;
+  if (Skv > 128 || (H != 0 && H != 1 && H != 2 && H != 4 && H != 8)) return FNG_ERR_UNSUPPORTED;
   if (B == 0 || H == 0) return FNG_OK;
   // dK and dV are written for every batch, even when no query row is processed
   if (!dK || !dV) return FNG_ERR_INVALID_ARG;

@@ -118,21 +118,27 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 // wave copies, and alone reads, its own head's K and V tiles, so the tile loop
 // needs no workgroup barrier: the waves only meet at the two cross-head
 // exchanges.
+// waves of a rows workgroup: four (two workgroups per CU) up to four heads,
+// one per head for eight (one workgroup per CU, the same eight waves per CU)
+template <int H>
+constexpr int bwd_rows_waves() { return H <= 4 ? 4 : H; }
+
 template <int H, int ACT>
-__global__ __launch_bounds__(256, 2) void fna_bwd_rows_kernel(FnaBwdParams p) {
-  constexpr int G = 4 / H;                 // row groups
+__global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_bwd_rows_kernel(FnaBwdParams p) {
+  constexpr int NW = bwd_rows_waves<H>();
+  constexpr int G = NW / H;                // row groups
   constexpr int BM = 32 * G;               // query rows per workgroup
   constexpr int RB = H * kRowB;            // bytes per query row (all heads)
   constexpr int KVB = H * kTileB;          // one K (or V) tile of every head
-  constexpr int NK = KVB / 4096;           // 1 KB copies per wave for one tile
-  constexpr bool OWN = H == 4;             // wave w copies exactly head w's tiles
+  constexpr int NK = KVB / (1024 * NW);    // 1 KB copies per wave for one tile
+  constexpr bool OWN = H == NW;            // wave w copies exactly head w's tiles
   // bf16 high + low parts of the computed operands for GELU, whose dS = dP
   // GELU'(S) passes their rounding on at full weight; with the softmax the
   // rounding reaches dS scaled by P (about 1/Skv) and single parts keep dQ
   // within 3e-5 of the bf16 rounding floor (measured on the full workload)
   constexpr bool SPLIT = ACT == ACT_GELU;
   constexpr int XCH = 2 * KVB;
-  static_assert(XCH + BM * H * 16 <= 80 * 1024, "two workgroups per CU");
+  static_assert(XCH + BM * H * 16 <= (H <= 4 ? 80 : 160) * 1024, "two workgroups per CU up to four heads");
   // hand-off of the K / V tiles: workgroup barrier, or for OWN this wave's
   // own LDS reads done (the copies' own wait is its vmcnt)
   auto tile_sync = [&]() __attribute__((always_inline)) {
@@ -890,7 +896,7 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
 
 template <int H>
 void launch_rows_h(const FnaBwdParams& p, int act, hipStream_t s) {
-  const dim3 grid((unsigned)(p.B * p.qblocks)), block(256);
+  const dim3 grid((unsigned)(p.B * p.qblocks)), block(64 * bwd_rows_waves<H>());
   if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_GELU>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_SOFTMAX>), grid, block, 0, s, p);
 }
@@ -920,7 +926,7 @@ int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
   p.Skv = (int)c.Skv;
   p.T = (int)c.T;
   p.scale = c.sm_scale;
-  const int bm = 32 * (4 / (int)c.H);
+  const int bm = c.H <= 4 ? 32 * (4 / (int)c.H) : 32;  // query rows per rows workgroup
   p.qblocks = (int)((c.max_len + bm - 1) / bm);
   const int act = c.act == FNG_ACT_GELU ? ACT_GELU : ACT_SOFTMAX;
   if (p.qblocks > 0 && p.T > 0) {  // else no query row: dK = dV = 0 from the second kernel alone
@@ -928,6 +934,7 @@ int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
       case 1: launch_rows_h<1>(p, act, s); break;
       case 2: launch_rows_h<2>(p, act, s); break;
       case 4: launch_rows_h<4>(p, act, s); break;
+      case 8: launch_rows_h<8>(p, act, s); break;
       default: return FNG_ERR_UNSUPPORTED;
     }
     if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;

@@ -472,10 +472,9 @@ def main():
                 f"backward kernels {t['norms']:.1f} us)")
             del sets7, dQ7, dK7, dV7, ws7, O7, tmp7
         kernels["flash_norm_attention_backward"] = {"T": T7, "B": s7["B"], "Skv": s7["Skv"], "H": H7, **res7}
-        # the head sweep of the backward (GELU), the recipe of the forward's sweep;
-        # the backward kernels take H <= 4
+        # the head sweep of the backward (GELU), the recipe of the forward's sweep
         sweep7 = {}
-        for Hh in (1, 2, 4):
+        for Hh in (1, 2, 4, 8):
             sh, dh = inputs.make_inputs("flash_norm_attention_bwd", H=Hh)
             Qh, Kh, Vh, Gh = dev(dh["Q"]), dev(dh["K"]), dev(dh["V"]), dev(dh["dOut"])
             offh = torch.from_numpy(dh["offsets"]).to("cuda")

@@ -324,7 +324,7 @@ int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void
  * contents needed (the first kernel writes per-row intermediates that the
  * second reads: the gradient at the RMSNorm input in fp16, and for the
  * softmax the log-sum-exp per (row, head)); FNG_ERR_WORKSPACE if NULL or
- * smaller.  Limits: H 1, 2 or 4 (H = 8: FNG_ERR_UNSUPPORTED); D 128; 1 <= Skv <= 128 (the page's short-KV
+ * smaller.  Limits: H 1, 2, 4 or 8; D 128; 1 <= Skv <= 128 (the page's short-KV
  * case: a query row's scores over all keys stay in registers).  Products are
  * fp16 MFMAs with fp32 accumulation (K and V converted from bf16, so below
  * 65504 in magnitude).  Two kernel launches on `stream`. */

@@ -198,7 +198,9 @@ def test_flash_norm_attention_bwd_validation(lib):
     assert call(skv=129) == B.FNG_ERR_UNSUPPORTED        # short KV: at most 128 keys
     assert call(D=64) == B.FNG_ERR_UNSUPPORTED
     assert call(H=3) == B.FNG_ERR_UNSUPPORTED
-    assert call(H=8) == B.FNG_ERR_UNSUPPORTED             # the forward takes 8 heads, the backward 1, 2 or 4
+    assert call(H=16) == B.FNG_ERR_UNSUPPORTED
+    assert B.fng_flash_norm_attention_bwd_workspace_bytes(16, 8) == 16 * 8 * (128 * 2 + 4)
+    assert call(H=8) == B.FNG_ERR_WORKSPACE               # eight heads: the workspace sized for two is too small
     assert call(act=7) == B.FNG_ERR_INVALID_ARG
     assert call(scale=float("nan")) == B.FNG_ERR_INVALID_ARG
     assert call(ws=None) == B.FNG_ERR_WORKSPACE

@@ -280,18 +280,18 @@ def test_fna_degenerate_rows(H, act):
     assert_close_stats(st[2].cpu().numpy(), r2, "fna rms rstd", rtol=3e-3)
 
 
+@pytest.mark.parametrize("H", [4, 8])
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-def test_fna_bwd_degenerate_rows(act):
+def test_fna_bwd_degenerate_rows(act, H):
     """Zero, constant, tiny and shifted query rows through the forward and the
     backward.  The backward rebuilds the RMSNorm output as out - Q from the
     bf16 forward output (the page's recompute), which carries out's rounding,
     about |x| 2^-9, into it: the shift is 4 spreads here, and rows of 2^12-size
     entries are left to the forward test (there out - Q keeps no digit of the
     unit-size RMSNorm output)."""
-    H = 4
     spec, d, rows, where = fna_planted(H, 72, seed=530, dout=True, kinds=("zero", "const", "tiny", "shifted"),
                                        shift=4.0)
-    log(f"FlashNormAttention backward degenerate rows act={act}: {where}")
+    log(f"FlashNormAttention backward degenerate rows H={H} act={act}: {where}")
     Q, K, V, G = dev(d["Q"]), dev(d["K"]), dev(d["V"]), dev(d["dOut"])
     off = torch.from_numpy(np.ascontiguousarray(d["offsets"])).to("cuda")
     T = Q.shape[0]

@@ -2,7 +2,7 @@
 called through the C ABI after the forward kernel, as in training) against
 the fp64 oracle's gradients on seeded bf16 inputs: jagged query batches with
 empty, single-row, tile-straddling and maximum lengths, key counts that leave
-a ragged last key tile, one, two and four heads, softmax and GELU.
+a ragged last key tile, one, two, four and eight heads, softmax and GELU.
 
 The forward's output and statistics come from the forward kernel (the
 backward rebuilds the LayerNorm output and the RMSNorm output from them, as
@@ -83,7 +83,7 @@ def check(d, dQ, dK, dV, act, what, rows=None, eps_ln=1e-5, eps_rms=1e-6):
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu"])
-@pytest.mark.parametrize("H", [1, 2, 4])
+@pytest.mark.parametrize("H", [1, 2, 4, 8])
 def test_fna_bwd_reduced(H, act):
     spec, d = case(H, 72)
     log(f"fna bwd H={H} act={act} lengths={LENGTHS} Skv=72")
