@@ -191,7 +191,9 @@ def main():
             "fused_every_tile": lambda i: B.fng_prenorm_rms_gemm(sets[i % 2][0], sets[i % 2][1], sets[i % 2][2],
                                                                  eps),
         }, args.reps, args.batch)
-        kernels["prenorm_rms_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K, spread=iqr(t))
+        sp = iqr(t)
+        t["norm_torch"] = torch_norm_us("rms", sets[0][0], eps, args.reps, args.batch)
+        kernels["prenorm_rms_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K, spread=sp)
 
     if args.only in (None, "prenorm_gamma"):
         spec_g, dg = inputs.make_inputs("prenorm_rms_mlp_gamma", M=8, N=8)
@@ -226,7 +228,9 @@ def main():
             "gemm": lambda i: B.fng_gemm(setsl[i % 2][0], setsl[i % 2][1], setsl[i % 2][2]),
             "norm": lambda i: B.fng_layernorm(setsl[i % 2][0], Xn, sl["eps"]),
         }, args.reps, args.batch)
-        kernels["prenorm_ln_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K, spread=iqr(t))
+        sp = iqr(t)
+        t["norm_torch"] = torch_norm_us("ln", setsl[0][0], sl["eps"], args.reps, args.batch)
+        kernels["prenorm_ln_mlp"] = summarize(t, flops, norm_bytes=4.0 * M * K, spread=sp)
         del setsl, XL, wsl, mul, rsl
 
     # ---------------- small pre-RMSNorm workload (256 x 128 x 128): microseconds ----
