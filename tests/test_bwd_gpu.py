@@ -5,9 +5,11 @@ the lazy pre-RMSNorm input gradient with xhat rebuilt from X and rstd
 (fng_prenorm_rms_bwd_dx), and the unfused row kernels (fng_layernorm_bwd,
 fng_rmsnorm_bwd), all through the C ABI against the fp64 oracle.
 
-Tolerance: normwise max relative error <= 1e-2 and mean absolute error <=
-2e-3, the MAE bound scaled by the output's mean magnitude over 0.8 where that
-is larger (the gradients are scaled by the forward rstd, log-normal here)."""
+Tolerance (gpu_util.assert_parity_floor): normwise max relative error <= 1e-2,
+and a mean absolute error within 1e-3 of the bf16 rounding floor of the exact
+gradient (the gradients are scaled by the forward rstd, log-normal here, so a
+fixed 2e-3 would be loose on some rows and tight on others); the bound is never
+looser than 2e-3 times max(1, mean |ref| / 0.8)."""
 
 import numpy as np
 import pytest
