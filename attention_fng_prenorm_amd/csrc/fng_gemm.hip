@@ -1168,7 +1168,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         const int row = c / NCH, ch = c % NCH;
         const int m = m0 + row, n = n0 + ch * 8;
         const u32x4_t v = lds_read16(lds + row * (BN * 2) + ((ch ^ row) & (NCH - 1)) * 16);
-        if (m < M && n < N) *reinterpret_cast<u32x4_t*>(p.Y + (size_t)m * N + n) = v;
+        // non-temporal: the output is not read again here, and streaming it
+        // past the L2 keeps the operands' lines there (measured 0.5-1.5 %
+        // faster on 4096 x 4096 x 14336 and 16384 x 1024 x 4096)
+        if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p.Y + (size_t)m * N + n));
       }
     }
   }
