@@ -80,6 +80,7 @@ using flag = std::integral_constant<bool, B>;
 template <bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kTileK + 2 * kTileV];
+  static_assert(kWaves * 32 * kD * 2 <= 2 * kTileK + 2 * kTileV, "the output rows are staged over the K/V buffers");
   FNG_LDS char* lds = (FNG_LDS char*)smem;
 
   const int tid = threadIdx.x;
@@ -373,18 +374,36 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     rstd = __builtin_amdgcn_rsqf(half_swap_sum(ss) * (1.0f / kD) + p.eps_rms);
     if (hi == 0 && q < Sq && p.rms_rstd_out) p.rms_rstd_out[((size_t)b * Sq + q) * H + h] = rstd;
   }
-  if (q >= Sq) return;
-  uint16_t* orow = p.O + (((size_t)b * Sq + q) * H + h) * kD;
+  // The wave's 32 output rows go through LDS (the K/V buffers are free once
+  // every wave is past its last key tile) and out as whole 256-byte rows,
+  // 16 bytes per lane: the lane's own values are 8-byte pieces of its row,
+  // which stored directly cost more than the staging.  Chunk c of row r sits
+  // at chunk c ^ (r % 16) of the row's 256 bytes (the 32 rows of one write
+  // spread over the banks).
+  __syncthreads();
+  FNG_LDS char* stg = lds + wave * (32 * kD * 2);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * dt + 8 * r4 + 4 * hi;
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * r4 + e] * inv * rstd;
-      *reinterpret_cast<u32x2_t*>(orow + d) = u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      const int c = 4 * dt + r4;  // 16-byte chunk of d = 8c .. 8c + 7; this lane's half: hi
+      *reinterpret_cast<FNG_LDS u32x2_t*>(stg + l32 * (kD * 2) + ((c ^ (l32 & 15)) * 16) + hi * 8) =
+          u32x2_t{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
     }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 32 * 16 / 64; ++it) {
+    const int idx = it * 64 + lane;  // 16 chunks per row, 32 rows
+    const int r = idx >> 4, c = idx & 15;
+    const int qq = qt * kBQ + wave * 32 + r;
+    if (qq < Sq) {
+      const u32x4_t v = lds_read16(stg + r * (kD * 2) + ((c ^ (r & 15)) * 16));
+      *reinterpret_cast<u32x4_t*>(p.O + (((size_t)b * Sq + qq) * H + h) * kD + 8 * c) = v;
+    }
+  }
 }
 
 int launch_attention(const AttnCall& c, bool norm, hipStream_t s) {
