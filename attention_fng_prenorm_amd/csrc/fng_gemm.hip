@@ -90,8 +90,7 @@ struct GemmParams {
   int group_m;       // row blocks per tile group (L2 locality of the tile order)
   uint32_t wait_ticks;     // split-N: bound of one exchange wait, in 100 MHz real-time ticks
   int poison_on_timeout;   // split-N: rows whose wait timed out are written as NaN
-  const float* colsum;  // lazy LayerNorm: [cs_parts][N] partial column sums of W
-  int cs_parts;
+  const float* colsum;  // lazy LayerNorm: [N] column sums of W
   const uint16_t* beta;  // post-norm affine: bias [N] (gamma [N] is the gain), or nullptr
   // split-N placement: each XCD's tiles of a round form sn_rh row blocks x
   // sn_cw column tiles, sn_g XCDs sharing the row blocks (sn_cw 0: every
@@ -806,8 +805,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         for (int r4 = 0; r4 < 4; ++r4) {
           const int c = col_of(j, r4);
           f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-          if (c < N)
-            for (int q = 0; q < p.cs_parts; ++q) v += *reinterpret_cast<const f32x4_t*>(p.colsum + (size_t)q * N + c);
+          if (c < N) v = *reinterpret_cast<const f32x4_t*>(p.colsum + c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) csum[j][r4][e] = v[e];
         }
@@ -1349,6 +1347,18 @@ __global__ __launch_bounds__(1024) void colsum_kernel(const uint16_t* W, float* 
   }
 }
 
+// the column-sum partials merged in place: part[0][n] = sum_q part[q][n],
+// so that the GEMM's epilogue reads one sum per column (reading all the
+// partials in every tile of the call cost ~16 us on 4096 x 4096 x 14336,
+// this pass ~1 us).
+__global__ __launch_bounds__(256) void colsum_merge_kernel(float* part, int N, int parts) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float v = 0.f;
+  for (int q = 0; q < parts; ++q) v += part[(size_t)q * N + n];
+  part[n] = v;
+}
+
 }  // namespace
 
 // split-N geometry shared with the workspace size computation
@@ -1472,9 +1482,13 @@ int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s) {
   hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((c.N + 255) / 256), (unsigned)parts), dim3(1024), 0, s,
                      static_cast<const uint16_t*>(c.W), colsum, (int)c.K, (int)c.N, kchunk);
   if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
+  if (parts > 1) {
+    hipLaunchKernelGGL(colsum_merge_kernel, dim3((unsigned)((c.N + 255) / 256)), dim3(256), 0, s, colsum, (int)c.N,
+                       parts);
+    if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
+  }
   GemmParams p = base_params(c);
   p.colsum = colsum;
-  p.cs_parts = parts;
   if (small_problem(c)) return launch<64, 64, 64, 2, 2, EPI_PRENORM, true, false>(p, 0, false, s);
   if (!c.mean_out || !c.rstd_out) return launch_big<EPI_PRENORM, false, true>(p, s);
   // with mean_out and rstd_out to hand the statistics over: the split of
