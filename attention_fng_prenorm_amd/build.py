@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfng.so")
-SOURCES = ["fng_api.cpp", "fng_gemm.hip", "fng_norm.hip", "fng_attention.hip", "fng_fna.hip", "fng_fna_bwd.hip"]
+SOURCES = ["fng_api.cpp", "fng_gemm.hip", "fng_fulln.hip", "fng_norm.hip", "fng_attention.hip", "fng_fna.hip",
+           "fng_fna_bwd.hip"]
 ARCH = "gfx950"
 
 # packed-fp32 ops are disabled for all device code; -O3 must not form

@@ -1533,6 +1533,8 @@ int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s) {
     return launch_norm<256, 128, 32, 2, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   if (tall && c.N <= 256)
     return launch_norm<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
+  // K, N <= 256: all of W resident in LDS, eight waves (fng_fulln.hip)
+  if (fulln_small_fits(c.N, c.K)) return launch_postnorm_fulln_small(c, ln, s);
   if (c.N <= 256)
     return launch_norm<32, 256, 64, 1, 4, EPI_FULLN>(p, ln, c.gamma != nullptr, 0, s);
   // N <= 512: 128 x 512 tiles of 8 waves (64 x 128 each, the ping-pong mainloop;

@@ -37,6 +37,9 @@ bool prenorm_ws_needs_wg(int64_t M, int64_t N);
 int launch_prenorm_ln(const GemmCall& c, float* colsum, hipStream_t s);
 int prenorm_ln_parts(int64_t K);
 int launch_postnorm_fulln(const GemmCall& c, bool ln, hipStream_t s);
+// fng_fulln.hip: the full-N post-norm for K <= 256 and N <= 256 (W resident in LDS)
+bool fulln_small_fits(int64_t N, int64_t K);
+int launch_postnorm_fulln_small(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s);
 int launch_postnorm_partial(const GemmCall& c, bool ln, hipStream_t s);
 // norm backward epilogue inputs: H = xhat [M, N] (or the norm's input when

@@ -290,6 +290,47 @@ def test_postnorm_paths_ragged(ln, path):
         assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
 
 
+SMALL_KN = [(1000, 72, 136), (333, 200, 40), (8200, 256, 256), (64, 8, 8), (97, 256, 248)]
+
+
+@pytest.mark.parametrize("ln", [True, False], ids=["ln", "rms"])
+@pytest.mark.parametrize("M,K,N", SMALL_KN, ids=[f"{m}x{k}x{n}" for m, k, n in SMALL_KN])
+def test_postnorm_fulln_small(ln, M, K, N):
+    """Full-N with all of W resident in LDS (K, N <= 256, eight waves of 32
+    columns): ragged M, K and N (zero-filled copies, partial column blocks,
+    waves with no valid column), every element and the statistics outputs."""
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=M + K + N)
+    log(f"postnorm full-N small ln={ln} M={M} K={K} N={N}")
+    Y, mu, r, _ = run_postnorm(d, spec["eps"], M, N, K, ln, B.FNG_PATH_FULLN)
+    ref, mref, rref = oracle.gemm_postnorm(f64(d["X"]), f64(d["W"]), spec["eps"], "ln" if ln else "rms")
+    assert_parity(host(Y), ref, f"full-N small {M}x{K}x{N} ln={ln}")
+    assert_close_stats(r.cpu().numpy(), rref, "rstd")
+    if ln:
+        assert np.max(np.abs(mu.cpu().numpy() - mref)) < 2e-4
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_postnorm_affine_fulln_small(kind):
+    """The affine (gain, with and without the bias) in the resident-W kernel."""
+    M, K, N = 1000, 136, 200
+    spec, d = inputs.make_inputs("postnorm_ln_smalln", M=M, K=K, N=N, seed=63)
+    rng = np.random.Generator(np.random.PCG64(64))
+    g = inputs.f32_to_bf16_bits(1.0 + 0.3 * rng.standard_normal(N).astype(np.float32))
+    b = inputs.f32_to_bf16_bits(0.5 * rng.standard_normal(N).astype(np.float32))
+    X, W, G, Bb = dev(d["X"]), dev(d["W"]), dev(g), dev(b)
+    Y = empty_bf16(M, N)
+    r = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    for beta in (Bb, None):
+        log(f"post-{kind} affine full-N small {M}x{K}x{N} beta={beta is not None}")
+        B.fng_gemm_postnorm_affine(X, W, Y, spec["eps"], G, beta, ln=(kind == "ln"), workspace=None,
+                                   path=B.FNG_PATH_FULLN, rstd_out=r)
+        torch.cuda.synchronize()
+        ref, _, rr = oracle.gemm_postnorm_affine(f64(d["X"]), f64(d["W"]), spec["eps"], kind, f64(g),
+                                                 f64(b) if beta is not None else None)
+        assert_parity_floor(host(Y), ref, f"post-{kind} affine full-N small beta={beta is not None}")
+        assert_close_stats(r.cpu().numpy(), rr, "affine rstd")
+
+
 @pytest.mark.parametrize("ln", [True, False])
 @pytest.mark.parametrize("N", [264, 392, 512])
 def test_postnorm_fulln_wide(ln, N):
