@@ -272,6 +272,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 
   const int M = p.M, N = p.N, K = p.K;
   const int ktiles = (K + BK - 1) / BK;
+  // the epilogues scale by reciprocals (v_rcp_f32, within 1 ulp): an fp32
+  // division is a dozen instructions, and the split-N merge made two per
+  // column tile on the thread that merges a row, on every tile's critical path
+  const float inv_k = __builtin_amdgcn_rcpf((float)K);
+  const float inv_n = __builtin_amdgcn_rcpf((float)N);
 
   // split-N: this call's tag = the last call's epoch + 1 (constant during the
   // call: the epoch only advances after every row block has been merged)
@@ -785,12 +790,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if constexpr (LN) {
-          rs_mean[i] = red[BM + lrow(i)] / (float)K;
-          const float var = fmaxf(red[lrow(i)] / (float)K - rs_mean[i] * rs_mean[i], 0.f);
+          rs_mean[i] = red[BM + lrow(i)] * inv_k;
+          const float var = fmaxf(red[lrow(i)] * inv_k - rs_mean[i] * rs_mean[i], 0.f);
           rs_rstd[i] = __builtin_amdgcn_rsqf(var + p.eps);
         } else {
           rs_mean[i] = 0.f;
-          rs_rstd[i] = __builtin_amdgcn_rsqf(red[lrow(i)] / (float)K + p.eps);
+          rs_rstd[i] = __builtin_amdgcn_rsqf(red[lrow(i)] * inv_k + p.eps);
         }
       }
     }
@@ -908,8 +913,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
         }
         row_reduce(part, s1);  // tile row sums
         float tmean[FM];
+        const float inv_valid = __builtin_amdgcn_rcpf((float)nvalid);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) tmean[i] = s1[i] / (float)nvalid;
+        for (int i = 0; i < FM; ++i) tmean[i] = s1[i] * inv_valid;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           float s = 0.f;
@@ -951,14 +957,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           rs_mean[i] = s1[i];
-          rs_rstd[i] = __builtin_amdgcn_rsqf(s2[i] / (float)N + p.eps);
+          rs_rstd[i] = __builtin_amdgcn_rsqf(s2[i] * inv_n + p.eps);
         }
       } else if constexpr (EPI == EPI_BWD_FULLN) {
         // backward: rs_mean = mean(g), rs_rstd = mean(g * xhat)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          rs_mean[i] = s1[i] / (float)N;
-          rs_rstd[i] = s2[i] / (float)N;
+          rs_mean[i] = s1[i] * inv_n;
+          rs_rstd[i] = s2[i] * inv_n;
         }
       } else {
         if constexpr (EPI == EPI_PARTIAL) {
@@ -1047,25 +1053,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
                 } else if constexpr (LN) {
                   // Chan et al. pairwise merge of (count, mean, M2)
                   const float nb = (float)min(BN, N - (q0 + u) * BN);
-                  const float tot = cn + nb;
+                  const float w = nb * __builtin_amdgcn_rcpf(cn + nb);  // nb / (cn + nb)
                   const float d = v1 - mean;
-                  mean += d * (nb / tot);
-                  m2 += v2 + d * d * (cn * nb / tot);
-                  cn = tot;
+                  mean += d * w;
+                  m2 += v2 + d * d * (cn * w);
+                  cn += nb;
                 } else {
                   ssum += v2;
                 }
               }
             }
             if constexpr (IS_BWD) {
-              stats[tid * 2 + 0] = gsum / (float)N;
-              stats[tid * 2 + 1] = ssum / (float)N;
+              stats[tid * 2 + 0] = gsum * inv_n;
+              stats[tid * 2 + 1] = ssum * inv_n;
             } else if constexpr (LN) {
               stats[tid * 2 + 0] = mean;
-              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(m2 / (float)N + p.eps);
+              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(m2 * inv_n + p.eps);
             } else {
               stats[tid * 2 + 0] = 0.f;
-              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(ssum / (float)N + p.eps);
+              stats[tid * 2 + 1] = __builtin_amdgcn_rsqf(ssum * inv_n + p.eps);
             }
             if (timed_out && p.poison_on_timeout) stats[tid * 2 + 1] = __builtin_nanf("");
           }
