@@ -470,6 +470,41 @@ def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_sc
     return dq, dk, dv
 
 
+def jagged_attention_backward(q, offsets, k, v, dout, sm_scale, act):
+    """Gradients of jagged_attention (the attention step of FlashNormAttention
+    without its norms and residuals; the unfused chain's attention backward)
+    with respect to q, k and v, given dout [T, H, D] at its output.
+
+    For every batch b and head h, with s = q k^T sm_scale and p = act(s):
+        dp = dout v^T,  ds = act_backward(s, p, dp) sm_scale
+        dq = ds k,  dk = ds^T q (summed over the batch's rows),  dv = p^T dout
+    Returns (dq [T, H, D], dk [B, Skv, H, D], dv [B, Skv, H, D]); rows outside
+    every batch get dq = 0, batches without rows dk = dv = 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    T, H, D = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        for h in range(H):
+            qh, kh, vh, gh = q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :], dout[r0:r1, h, :]
+            s = (qh @ kh.T) * sm_scale
+            p = _activation(s, act)
+            dv[b, :, h, :] = p.T @ gh
+            ds = activation_backward(s, p, gh @ vh.T, act) * sm_scale
+            dq[r0:r1, h, :] = ds @ kh
+            dk[b, :, h, :] = ds.T @ qh
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # the agreed comparison metric
 # ---------------------------------------------------------------------------

@@ -831,6 +831,94 @@ def check_fna_backward_finite_differences(O):
                 assert abs(fd1 - float(np.sum(g * e))) <= 1e-6 * (1.0 + abs(fd1)), (act, which, fd1)
 
 
+def _bf_jagged_attention(q, off, k, v, scale, act):
+    """Brute force (plain Python loops) of the jagged attention: softmax over
+    the keys or the tanh GELU, no norms, no residuals."""
+    T, H, D = len(q), len(q[0]), len(q[0][0])
+    out = [[[0.0] * D for _ in range(H)] for _ in range(T)]
+    for b in range(len(off) - 1):
+        for r in range(off[b], off[b + 1]):
+            for h in range(H):
+                sc = [scale * sum(q[r][h][d] * k[b][t][h][d] for d in range(D)) for t in range(len(k[b]))]
+                if act == "softmax":
+                    m = max(sc)
+                    e = [math.exp(x - m) for x in sc]
+                    p = [x / sum(e) for x in e]
+                else:
+                    p = [_bf_gelu_tanh(x) for x in sc]
+                for d in range(D):
+                    out[r][h][d] = sum(p[t] * v[b][t][h][d] for t in range(len(k[b])))
+    return out
+
+
+def check_jagged_attention_backward_torch(O):
+    import torch
+    import torch.nn.functional as F
+    q, off, k, v = _fna_case(91, [4, 0, 6], 5, 3, 8, qscale=1.3)
+    dout = _rng(92).standard_normal(q.shape)
+    for act in ("softmax", "gelu"):
+        tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_(True) for a in (q, k, v))
+        outs = []
+        for b in range(len(off) - 1):
+            heads = []
+            for h in range(q.shape[1]):
+                sc = tq[off[b]:off[b + 1], h, :] @ tk[b, :, h, :].T * 0.45
+                pr = torch.softmax(sc, dim=-1) if act == "softmax" else F.gelu(sc, approximate="tanh")
+                heads.append(pr @ tv[b, :, h, :])
+            if off[b + 1] > off[b]:
+                outs.append(torch.stack(heads, dim=1))
+        torch.cat(outs).backward(torch.from_numpy(dout))
+        dq, dk, dv = O.jagged_attention_backward(q, off, k, v, dout, 0.45, act)
+        _close(dq, tq.grad.numpy(), 1e-11, f"jagged attention backward dq ({act}) vs autograd")
+        _close(dk, tk.grad.numpy(), 1e-11, f"jagged attention backward dk ({act}) vs autograd")
+        _close(dv, tv.grad.numpy(), 1e-11, f"jagged attention backward dv ({act}) vs autograd")
+
+
+def check_jagged_attention_backward_finite_differences(O):
+    # directional derivatives of L = sum(dout * out), out from the brute force
+    q, off, k, v = _fna_case(93, [2, 3], 3, 2, 3)
+    rng = _rng(94)
+    dout = rng.standard_normal(q.shape)
+    h = 1e-6
+
+    def loss(qq, kk, vv, act):
+        out = _bf_jagged_attention(qq.tolist(), off.tolist(), kk.tolist(), vv.tolist(), 0.8, act)
+        return sum(dout[r][a][d] * out[r][a][d] for r in range(len(out)) for a in range(2) for d in range(3))
+
+    for act in ("softmax", "gelu"):
+        grads = O.jagged_attention_backward(q, off, k, v, dout, 0.8, act)
+        for which, (a, g) in enumerate(zip((q, k, v), grads)):
+            for _ in range(2):
+                e = rng.standard_normal(a.shape)
+                args_p = [q, k, v]; args_m = [q, k, v]
+                args_p[which] = a + h * e; args_m[which] = a - h * e
+                fd = (loss(*args_p, act) - loss(*args_m, act)) / (2 * h)
+                assert abs(fd - float(np.sum(g * e))) <= 1e-6 * (1.0 + abs(fd)), (act, which, fd)
+
+
+def check_jagged_attention_backward_invariants(O):
+    q, off, k, v = _fna_case(95, [3, 5, 0], 6, 2, 4)
+    dout = _rng(96).standard_normal(q.shape)
+    for act in ("softmax", "gelu"):
+        dq, dk, dv = O.jagged_attention_backward(q, off, k, v, dout, 0.6, act)
+        assert np.all(dk[2] == 0.0) and np.all(dv[2] == 0.0)  # the empty batch
+        z = O.jagged_attention_backward(q, off, k, v, np.zeros_like(dout), 0.6, act)
+        assert all(np.all(a == 0.0) for a in z)
+    # softmax: a vector added to every key shifts each score row by a constant,
+    # so the key gradients sum to zero; a value row's gradient sums the
+    # probabilities of that key times dout, and the probabilities of a row sum
+    # to one, so sum over keys of dv = sum over the batch's rows of dout
+    dq, dk, dv = O.jagged_attention_backward(q, off, k, v, dout, 0.6, "softmax")
+    _close(np.sum(dk, axis=1), np.zeros((3, 2, 4)), 1e-11, "softmax: key gradients sum to zero")
+    for b in range(2):
+        _close(np.sum(dv[b], axis=0), np.sum(dout[off[b]:off[b + 1]], axis=0), 1e-11,
+               "softmax: value gradients sum to the rows' dout")
+    # GELU with V = 0: the output is zero whatever q and k, so dq = dk = 0
+    dq, dk, dv = O.jagged_attention_backward(q, off, k, np.zeros_like(v), dout, 0.6, "gelu")
+    _close(dq, np.zeros_like(dq), 0.0, "V = 0: no query gradient")
+    _close(dk, np.zeros_like(dk), 0.0, "V = 0: no key gradient")
+
+
 def check_fna_backward_invariants(O):
     q, off, k, v = _fna_case(85, [3, 5, 0], 6, 2, 4)
     T, H, D = q.shape
@@ -902,6 +990,9 @@ ALL_CHECKS = [
     check_fna_backward_torch,
     check_fna_backward_finite_differences,
     check_fna_backward_invariants,
+    check_jagged_attention_backward_torch,
+    check_jagged_attention_backward_finite_differences,
+    check_jagged_attention_backward_invariants,
     check_compare,
 ]
 

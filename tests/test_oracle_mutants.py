@@ -78,8 +78,12 @@ def _ns(**over):
     def flash_norm_attention_backward(q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act):
         return _fna_bwd(ns, q, offsets, k, v, dout, eps_ln, eps_rms, sm_scale, act)
 
+    def jagged_attention_backward(q, offsets, k, v, dout, sm_scale, act):
+        return _jagged_bwd(ns, q, offsets, k, v, dout, sm_scale, act)
+
     for name, fn in (("gemm_postnorm_affine", gemm_postnorm_affine), ("prenorm_ln_gemm", prenorm_ln_gemm), ("activation_backward", activation_backward),
                      ("flash_norm_attention_backward", flash_norm_attention_backward),
+                     ("jagged_attention_backward", jagged_attention_backward),
                      ("prenorm_rms_gemm", prenorm_rms_gemm), ("gemm_postnorm", gemm_postnorm),
                      ("norm_attention", norm_attention), ("flash_norm_attention", flash_norm_attention),
                      ("jagged_attention", jagged_attention),
@@ -202,6 +206,33 @@ def _affine_before_norm(x, w, eps, kind, gamma, beta=None):
     z = F.gemm(x, w) * np.asarray(gamma, dtype=np.float64)[None, :]
     y, mu, r = (F.layernorm_rows(z, eps) if kind == "ln" else (F.rmsnorm_rows(z, eps)[0], None, F.rmsnorm_rows(z, eps)[1]))
     return (y + np.asarray(beta, dtype=np.float64)[None, :] if beta is not None else y), mu, r
+
+
+def _jagged_bwd(ns, q, offsets, k, v, dout, sm_scale, act, dk_scaled=True, dv_from_ds=False, dq_from_v=False):
+    """The plain jagged attention backward from the pieces in ns, with
+    switches that plant mistakes: dk without the scale, dv from ds instead of
+    p, dq through the values instead of the keys."""
+    q, k, v, dout = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(offsets) - 1):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        if r1 <= r0:
+            continue
+        for h in range(q.shape[1]):
+            qh, kh, vh, gh = q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :], dout[r0:r1, h, :]
+            s_ = (qh @ kh.T) * sm_scale
+            p = ns.softmax_rows(s_) if act == "softmax" else ns.gelu_tanh(s_)
+            ds = ns.activation_backward(s_, p, gh @ vh.T, act)
+            dv[b, :, h, :] = (ds if dv_from_ds else p).T @ gh
+            dq[r0:r1, h, :] = (ds * sm_scale) @ (vh if dq_from_v else kh)
+            dk[b, :, h, :] = (ds * (sm_scale if dk_scaled else 1.0)).T @ qh
+    return dq, dk, dv
+
+
+def _jagged_bwd_mutant(**switches):
+    def f(q, offsets, k, v, dout, sm_scale, act):
+        return _jagged_bwd(F, q, offsets, k, v, dout, sm_scale, act, **switches)
+    return f
 
 
 def _fna_bwd_mutant(**switches):
@@ -428,6 +459,9 @@ MUTANTS = {
     "fna_bwd_rms_xhat_is_its_input": dict(flash_norm_attention_backward=_fna_bwd_mutant(rms_xhat_is_o=True)),
     "fna_bwd_ln_xhat_is_raw_x": dict(flash_norm_attention_backward=_fna_bwd_mutant(ln_xhat_raw=True)),
     "softmax_backward_drops_row_term": dict(activation_backward=_softmax_bwd_no_row_term),
+    "jagged_bwd_dk_unscaled": dict(jagged_attention_backward=_jagged_bwd_mutant(dk_scaled=False)),
+    "jagged_bwd_dv_from_ds": dict(jagged_attention_backward=_jagged_bwd_mutant(dv_from_ds=True)),
+    "jagged_bwd_dq_from_values": dict(jagged_attention_backward=_jagged_bwd_mutant(dq_from_v=True)),
     "ln_lazy_without_mean_correction": dict(prenorm_ln_gemm=_ln_lazy_no_mean),
     "postnorm_affine_before_norm": dict(gemm_postnorm_affine=_affine_before_norm),
     "ln_lazy_rank1_term_unscaled": dict(prenorm_ln_gemm=_ln_lazy_rank1_unscaled),
