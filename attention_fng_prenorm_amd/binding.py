@@ -71,6 +71,8 @@ SIGNATURES = {
     "fng_flash_norm_attention_bwd_workspace_bytes": (_sz, [_i64, _i64]),
     "fng_flash_norm_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _sz, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]),
+    "fng_jagged_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64,
+                                        _i64, _i64, _f32, _int, _vp]),
     "fng_status_string": (ctypes.c_char_p, [_int]),
     "fng_version": (_int, []),
 }
@@ -389,6 +391,18 @@ def fng_flash_norm_attention_bwd(Q, q_offsets, K, V, out, dout, ln_mean, ln_rstd
         _bf(out, "out"), _bf(dout, "dout"), _f(ln_mean, "ln_mean"), _f(ln_rstd, "ln_rstd"),
         _f(rms_rstd, "rms_rstd"), _bf(dQ, "dQ"), _bf(dK, "dK"), _bf(dV, "dV"), wp, wb,
         B, T, max_len_q, Skv, H, D, sm_scale, _act(act), _stream(stream)))
+
+
+def fng_jagged_attention_bwd(Q, q_offsets, K, V, dout, dQ, dK, dV, max_len_q, workspace=None, sm_scale=0.0,
+                             act="softmax", stream=None):
+    T, H, D, B, Skv = _jagged_shapes(Q, q_offsets, K, V, dout)
+    if dQ.shape != Q.shape or dK.shape != K.shape or dV.shape != V.shape:
+        raise ValueError("shapes: dout/dQ like Q, dK/dV like K")
+    wp, wb = _ws(workspace)
+    _check("fng_jagged_attention_bwd", lib().fng_jagged_attention_bwd(
+        _bf(Q, "Q"), _ptr(q_offsets, torch.int32, "q_offsets"), _bf(K, "K"), _bf(V, "V"), _bf(dout, "dout"),
+        _bf(dQ, "dQ"), _bf(dK, "dK"), _bf(dV, "dV"), wp, wb, B, T, max_len_q, Skv, H, D, sm_scale, _act(act),
+        _stream(stream)))
 
 
 def fng_jagged_attention(Q, q_offsets, K, V, out, max_len_q, sm_scale=0.0, act="softmax",

@@ -451,12 +451,13 @@ FNG_EXPORT size_t fng_flash_norm_attention_bwd_workspace_bytes(int64_t T, int64_
   return fng::fna_bwd_workspace_bytes(T, H);
 }
 
-FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K,
-                                            const void* V, const void* out, const void* dout,
-                                            const float* ln_mean, const float* ln_rstd, const float* rms_rstd,
-                                            void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
-                                            int64_t B, int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
-                                            int64_t D, float sm_scale, int act, void* stream) {
+namespace {
+// the two backward entry points: norm = true is FlashNormAttention's (out and
+// the three statistics are inputs), false the plain jagged attention's
+int fna_bwd_call(bool norm, const void* Q, const int32_t* q_offsets, const void* K, const void* V, const void* out,
+                 const void* dout, const float* ln_mean, const float* ln_rstd, const float* rms_rstd, void* dQ,
+                 void* dK, void* dV, void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t max_len_q,
+                 int64_t Skv, int64_t H, int64_t D, float sm_scale, int act, void* stream) {
   if (!isfinite(sm_scale)) return FNG_ERR_INVALID_ARG;
   int st = check_fna(Q, q_offsets, K, V, out, B, T, max_len_q, Skv, H, D, act);
   if (st != FNG_OK) return st;
@@ -467,9 +468,9 @@ FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offs
   if (!aligned16(dK) || !aligned16(dV)) return FNG_ERR_MISALIGNED;
   const bool rows = T > 0 && max_len_q > 0;
   if (rows) {
-    if (!dout || !dQ || !ln_mean || !ln_rstd || !rms_rstd) return FNG_ERR_INVALID_ARG;
-    if (!aligned16(dout) || !aligned16(dQ) || (uintptr_t)ln_mean % 4 || (uintptr_t)ln_rstd % 4 ||
-        (uintptr_t)rms_rstd % 4)
+    if (!dout || !dQ || (norm && (!ln_mean || !ln_rstd || !rms_rstd))) return FNG_ERR_INVALID_ARG;
+    if (!aligned16(dout) || !aligned16(dQ)) return FNG_ERR_MISALIGNED;
+    if (norm && ((uintptr_t)ln_mean % 4 || (uintptr_t)ln_rstd % 4 || (uintptr_t)rms_rstd % 4))
       return FNG_ERR_MISALIGNED;
     if (!workspace || workspace_bytes < fng::fna_bwd_workspace_bytes(T, H)) return FNG_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FNG_ERR_MISALIGNED;
@@ -484,7 +485,27 @@ FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offs
   if (B * H >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;
   fng::FnaBwdCall c{Q, q_offsets, K, V, out, dout, ln_mean, ln_rstd, rms_rstd, dQ, dK, dV, workspace,
                     B, T, rows ? max_len_q : 0, Skv, H, sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)D), act};
-  return fng::launch_fna_bwd(c, as_stream(stream));
+  return fng::launch_fna_bwd(c, norm, as_stream(stream));
+}
+}  // namespace
+
+FNG_EXPORT int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K,
+                                            const void* V, const void* out, const void* dout,
+                                            const float* ln_mean, const float* ln_rstd, const float* rms_rstd,
+                                            void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                                            int64_t B, int64_t T, int64_t max_len_q, int64_t Skv, int64_t H,
+                                            int64_t D, float sm_scale, int act, void* stream) {
+  return fna_bwd_call(true, Q, q_offsets, K, V, out, dout, ln_mean, ln_rstd, rms_rstd, dQ, dK, dV, workspace,
+                      workspace_bytes, B, T, max_len_q, Skv, H, D, sm_scale, act, stream);
+}
+
+FNG_EXPORT int fng_jagged_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K, const void* V,
+                                        const void* dout, void* dQ, void* dK, void* dV, void* workspace,
+                                        size_t workspace_bytes, int64_t B, int64_t T, int64_t max_len_q,
+                                        int64_t Skv, int64_t H, int64_t D, float sm_scale, int act, void* stream) {
+  // no forward output is read: dout stands in for it in the shape checks
+  return fna_bwd_call(false, Q, q_offsets, K, V, dout, dout, nullptr, nullptr, nullptr, dQ, dK, dV, workspace,
+                      workspace_bytes, B, T, max_len_q, Skv, H, D, sm_scale, act, stream);
 }
 
 FNG_EXPORT int fng_rmsnorm(const void* X, const void* gamma, void* Y, float* rstd_out, int64_t M, int64_t N,

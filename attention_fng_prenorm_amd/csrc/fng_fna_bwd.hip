@@ -123,7 +123,11 @@ __device__ __forceinline__ float f16hi(uint32_t w) {
 template <int H>
 constexpr int bwd_rows_waves() { return H <= 4 ? 4 : H; }
 
-template <int H, int ACT>
+// NORM = false: the plain jagged attention's backward (the unfused chain's
+// attention step): no norms and no residuals, so the gradient at the
+// attention output is dout itself, the scores' operand is q * scale, and dq
+// is the accumulated ds K
+template <int H, int ACT, bool NORM>
 __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_bwd_rows_kernel(FnaBwdParams p) {
   constexpr int NW = bwd_rows_waves<H>();
   constexpr int G = NW / H;                // row groups
@@ -212,9 +216,9 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
 
   // ---- prologue: the row's values for this head, lane layout of the MFMA B
   // operand (lane holds d = 16kk + 8hi + 0..7 of its row) --------------------
-  const float mu = valid ? p.ln_mean[row] : 0.f;
-  const float r1 = valid ? p.ln_rstd[row] : 0.f;
-  const float r2 = valid ? p.rms_rstd[row] : 0.f;
+  const float mu = NORM && valid ? p.ln_mean[row] : 0.f;
+  const float r1 = NORM ? (valid ? p.ln_rstd[row] : 0.f) : 1.f;
+  const float r2 = NORM && valid ? p.rms_rstd[row] : 0.f;
   const uint32_t rbase = (uint32_t)(qi * RB + h * kRowB + hi * 16);
   float gy = 0.f;
   {
@@ -222,25 +226,27 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       xq[kk] = buffer_load16(qrs, rbase + kk * 32);
-      xo[kk] = buffer_load16(ors, rbase + kk * 32);
+      xo[kk] = NORM ? buffer_load16(ors, rbase + kk * 32) : u32x4_t{0u, 0u, 0u, 0u};
       xg[kk] = buffer_load16(grs, rbase + kk * 32);
     }
-    // sum of g * y over this head, y = out - x (the RMSNorm output)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t wq = xq[kk][e], wo = xo[kk][e], wg = xg[kk][e];
-        gy = fmaf(bf16lo(wg), bf16lo(wo) - bf16lo(wq), gy);
-        gy = fmaf(bf16hi(wg), bf16hi(wo) - bf16hi(wq), gy);
-      }
-    gy = half_swap_sum(gy);
-    if (hi == 0) xch[(lrow * H + h) * 4 + 0] = gy;
-    __syncthreads();
     float c2 = 0.f;
+    if constexpr (NORM) {
+      // sum of g * y over this head, y = out - x (the RMSNorm output)
 #pragma unroll
-    for (int j = 0; j < H; ++j) c2 += xch[(lrow * H + j) * 4 + 0];
-    c2 *= 1.0f / (H * kD);
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wq = xq[kk][e], wo = xo[kk][e], wg = xg[kk][e];
+          gy = fmaf(bf16lo(wg), bf16lo(wo) - bf16lo(wq), gy);
+          gy = fmaf(bf16hi(wg), bf16hi(wo) - bf16hi(wq), gy);
+        }
+      gy = half_swap_sum(gy);
+      if (hi == 0) xch[(lrow * H + h) * 4 + 0] = gy;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < H; ++j) c2 += xch[(lrow * H + j) * 4 + 0];
+      c2 *= 1.0f / (H * kD);
+    }
     // do = r2 (g - y c2).  do goes to the MFMA as bf16 high and low parts and
     // to the key/value kernel (and this kernel's epilogue) as fp16
     u32x4_t dob[8], dol[8];
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
           const float x = u ? bf16hi(wq) : bf16lo(wq);
           const float y = (u ? bf16hi(wo) : bf16lo(wo)) - x;
           const float gv = u ? bf16hi(wg) : bf16lo(wg);
-          d2[u] = r2 * fmaf(-y, c2, gv);
+          d2[u] = NORM ? r2 * fmaf(-y, c2, gv) : gv;
         }
         const uint32_t hw = pack_bf16(d2[0], d2[1]);
         dob[kk][e] = hw;
@@ -512,8 +518,8 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
     u32x4_t dof[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      xq[kk] = buffer_load16(qrs, rbase + kk * 32);
-      dof[kk] = valid ? *reinterpret_cast<const u32x4_t*>(dodst + 16 * kk) : u32x4_t{0u, 0u, 0u, 0u};
+      xq[kk] = NORM ? buffer_load16(qrs, rbase + kk * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      dof[kk] = (NORM && valid) ? *reinterpret_cast<const u32x4_t*>(dodst + 16 * kk) : u32x4_t{0u, 0u, 0u, 0u};
     }
     float s1 = 0.f, s2 = 0.f;
     float dnb[8][8];
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j = 2 * e + u;
-          const float v = dnb[kk][j] + (u ? f16hi(wd) : f16lo(wd));
+          const float v = NORM ? dnb[kk][j] + (u ? f16hi(wd) : f16lo(wd)) : dnb[kk][j];
           const float n = ((u ? bf16hi(wq) : bf16lo(wq)) - mu) * r1;
           dnb[kk][j] = v;
           s1 += v;
@@ -541,32 +547,39 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
         }
       }
     }
-    s1 = half_swap_sum(s1);
-    s2 = half_swap_sum(s2);
-    if (hi == 0) {
-      xch[(lrow * H + h) * 4 + 1] = s1;
-      xch[(lrow * H + h) * 4 + 2] = s2;
-    }
-    __syncthreads();
     float m1 = 0.f, m2 = 0.f;
+    if constexpr (NORM) {
+      s1 = half_swap_sum(s1);
+      s2 = half_swap_sum(s2);
+      if (hi == 0) {
+        xch[(lrow * H + h) * 4 + 1] = s1;
+        xch[(lrow * H + h) * 4 + 2] = s2;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < H; ++j) {
-      m1 += xch[(lrow * H + j) * 4 + 1];
-      m2 += xch[(lrow * H + j) * 4 + 2];
+      for (int j = 0; j < H; ++j) {
+        m1 += xch[(lrow * H + j) * 4 + 1];
+        m2 += xch[(lrow * H + j) * 4 + 2];
+      }
+      m1 *= 1.0f / (H * kD);
+      m2 *= 1.0f / (H * kD);
     }
-    m1 *= 1.0f / (H * kD);
-    m2 *= 1.0f / (H * kD);
     // dQ goes through LDS (every wave is past its key loops: the K/V tiles are
     // free) and out as whole rows of all heads, where the block's rows fit
     // there; a lane's own values are 16-byte pieces of its row and head.
     // Measured at four heads 1 % faster; at eight (one workgroup per CU, no
     // other to cover the extra barrier) 1 % slower, so not there.
     constexpr bool STG = H <= 4 && BM * H * kRowB <= XCH;
+    // without the norms' exchange above, a barrier of its own: every wave is
+    // past its key loops before the staging overwrites the K/V tiles
+    if constexpr (!NORM && STG) __syncthreads();
     if (STG || valid) {
       uint16_t* dst = p.dQ + (size_t)row * H * kD + h * kD + hi * 8;
       // dout again (an L2 hit, cheaper than holding it in 32 registers throughout)
+      if constexpr (NORM) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) xg[kk] = buffer_load16(grs, rbase + kk * 32);
+        for (int kk = 0; kk < 8; ++kk) xg[kk] = buffer_load16(grs, rbase + kk * 32);
+      }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         u32x4_t w;
@@ -576,9 +589,13 @@ __global__ __launch_bounds__(64 * bwd_rows_waves<H>(), H <= 4 ? 2 : 1) void fna_
           float v[2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const float n = ((u ? bf16hi(wq) : bf16lo(wq)) - mu) * r1;
-            const float dx = r1 * (dnb[kk][2 * e + u] - m1 - n * m2);
-            v[u] = (u ? bf16hi(wg) : bf16lo(wg)) + dx;
+            if constexpr (NORM) {
+              const float n = ((u ? bf16hi(wq) : bf16lo(wq)) - mu) * r1;
+              const float dx = r1 * (dnb[kk][2 * e + u] - m1 - n * m2);
+              v[u] = (u ? bf16hi(wg) : bf16lo(wg)) + dx;
+            } else {
+              v[u] = dnb[kk][2 * e + u];
+            }
           }
           w[e] = pack_bf16(v[0], v[1]);
         }
@@ -627,7 +644,7 @@ __device__ __forceinline__ float key_lane_sum(const float (&v)[16], int l32) {
 // 8 waves = two groups of four; group q takes the row blocks q, q + 2, ...
 // and wave w of a group owns keys 32 w .. 32 w + 31.  K and V of the (batch,
 // head) sit in LDS as fp16 for the whole loop.
-template <int ACT>
+template <int ACT, bool NORM>
 __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
   constexpr int KVT = 128 * kRowB;                   // K (or V) of one head, 128 keys
   constexpr int KREG = 0, VREG = KVT;                // fp16 [key][d], rows swizzled
@@ -687,8 +704,8 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
         pq[u] = *reinterpret_cast<const u32x4_t*>(qs + 8 * u);
         pd[u] = *reinterpret_cast<const u32x4_t*>(ds + 8 * u);
       }
-      pmu = p.ln_mean[grow];
-      pr1 = p.ln_rstd[grow];
+      pmu = NORM ? p.ln_mean[grow] : 0.f;
+      pr1 = NORM ? p.ln_rstd[grow] : 1.f;
       if (ACT == ACT_SOFTMAX && spart == 0) plse = p.lse[grow * H + h];
     }
   };
@@ -917,15 +934,20 @@ __global__ __launch_bounds__(512, 1) void fna_bwd_kv_kernel(FnaBwdParams p) {
 }
 
 template <int H>
-void launch_rows_h(const FnaBwdParams& p, int act, hipStream_t s) {
+void launch_rows_h(const FnaBwdParams& p, int act, bool norm, hipStream_t s) {
   const dim3 grid((unsigned)(p.B * p.qblocks)), block(64 * bwd_rows_waves<H>());
-  if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_GELU>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_SOFTMAX>), grid, block, 0, s, p);
+  if (norm) {
+    if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_GELU, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_SOFTMAX, true>), grid, block, 0, s, p);
+  } else {
+    if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_GELU, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fna_bwd_rows_kernel<H, ACT_SOFTMAX, false>), grid, block, 0, s, p);
+  }
 }
 
 }  // namespace
 
-int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
+int launch_fna_bwd(const FnaBwdCall& c, bool norm, hipStream_t s) {
   FnaBwdParams p{};
   p.Q = static_cast<const uint16_t*>(c.Q);
   p.off = c.offsets;
@@ -953,17 +975,22 @@ int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s) {
   const int act = c.act == FNG_ACT_GELU ? ACT_GELU : ACT_SOFTMAX;
   if (p.qblocks > 0 && p.T > 0) {  // else no query row: dK = dV = 0 from the second kernel alone
     switch (c.H) {
-      case 1: launch_rows_h<1>(p, act, s); break;
-      case 2: launch_rows_h<2>(p, act, s); break;
-      case 4: launch_rows_h<4>(p, act, s); break;
-      case 8: launch_rows_h<8>(p, act, s); break;
+      case 1: launch_rows_h<1>(p, act, norm, s); break;
+      case 2: launch_rows_h<2>(p, act, norm, s); break;
+      case 4: launch_rows_h<4>(p, act, norm, s); break;
+      case 8: launch_rows_h<8>(p, act, norm, s); break;
       default: return FNG_ERR_UNSUPPORTED;
     }
     if (hipGetLastError() != hipSuccess) return FNG_ERR_HIP;
   }
   const dim3 grid((unsigned)(c.B * c.H)), block(512);
-  if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_GELU>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_SOFTMAX>), grid, block, 0, s, p);
+  if (norm) {
+    if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_GELU, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_SOFTMAX, true>), grid, block, 0, s, p);
+  } else {
+    if (act == ACT_GELU) hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_GELU, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fna_bwd_kv_kernel<ACT_SOFTMAX, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError() == hipSuccess ? FNG_OK : FNG_ERR_HIP;
 }
 

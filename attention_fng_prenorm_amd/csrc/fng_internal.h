@@ -119,7 +119,8 @@ struct FnaBwdCall {
   float sm_scale;
   int act;
 };
-int launch_fna_bwd(const FnaBwdCall& c, hipStream_t s);
+// norm = false: the plain jagged attention's backward (Q, K, V, dO; no statistics, no output)
+int launch_fna_bwd(const FnaBwdCall& c, bool norm, hipStream_t s);
 size_t fna_bwd_workspace_bytes(int64_t T, int64_t H);
 
 }  // namespace fng

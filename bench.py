@@ -467,18 +467,26 @@ def main():
                 torch.add(tmp7, q, out=dQ7)   # stands in for the first residual's add
                 B.fng_layernorm_bwd(dQ7.view(T7, -1), q.view(T7, -1), r7, tmp7.view(T7, -1))
                 torch.add(tmp7, g, out=dQ7)   # second residual
-            t = time_batches({"bwd": bwd, "fwd": fwd, "norms": norms}, args.reps, args.batch)
+
+            # the unfused chain's attention step backward (plain jagged attention)
+            def attn(i):
+                q, k, v, g, o, st = sets7[i % 2]
+                B.fng_jagged_attention_bwd(q, off7, k, v, g, tmp7, dK7, dV7, ml7, workspace=ws7, act=act)
+            t = time_batches({"bwd": bwd, "fwd": fwd, "norms": norms, "attn": attn}, args.reps, args.batch)
             # algorithmic: read Q, out, dOut, K, V and the statistics, write dQ, dK, dV
             bytes7 = 2.0 * (4 * T7 * H7 * D7 + 4 * s7["B"] * s7["Skv"] * H7 * D7) + 12.0 * T7
             flops7 = 10.0 * T7 * H7 * s7["Skv"] * D7   # S again, dP, dS K, dS^T n, P^T dO
             res7[act] = {"bwd_us": round(t["bwd"], 2), "fwd_us": round(t["fwd"], 2),
                          "bwd_over_fwd": round(t["bwd"] / t["fwd"], 2),
                          "norm_residual_bwd_kernels_us": round(t["norms"], 2),
+                         "attention_bwd_us": round(t["attn"], 2),
+                         "unfused_bwd_us": round(t["norms"] + t["attn"], 2),
+                         "speedup_vs_unfused": round((t["norms"] + t["attn"]) / t["bwd"], 2),
                          "bwd_gbs": round(bytes7 / t["bwd"] / 1e3, 1),
                          "bwd_frac_hbm": round(bytes7 / t["bwd"] / 1e3 / PEAK_HBM_GBS, 4),
                          "bwd_tflops": round(flops7 / t["bwd"] / 1e6, 1)}
-            log(f"fna backward ({act}): {t['bwd']:.1f} us (forward {t['fwd']:.1f} us; separate norm/residual "
-                f"backward kernels {t['norms']:.1f} us)")
+            log(f"fna backward ({act}): {t['bwd']:.1f} us (forward {t['fwd']:.1f} us; unfused chain: norm/residual "
+                f"backward kernels {t['norms']:.1f} us + attention backward {t['attn']:.1f} us)")
             del sets7, dQ7, dK7, dV7, ws7, O7, tmp7
         kernels["flash_norm_attention_backward"] = {"T": T7, "B": s7["B"], "Skv": s7["Skv"], "H": H7, **res7}
         # the head sweep of the backward (GELU), the recipe of the forward's sweep

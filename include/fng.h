@@ -329,6 +329,21 @@ int fng_flash_norm_attention(const void* Q, const int32_t* q_offsets, const void
  * fp16 MFMAs with fp32 accumulation (K and V converted from bf16, so below
  * 65504 in magnitude).  Two kernel launches on `stream`. */
 size_t fng_flash_norm_attention_bwd_workspace_bytes(int64_t T, int64_t H);
+
+/* Backward of fng_jagged_attention (the attention step without norms or
+ * residuals: the unfused chain's attention, whose backward the fused call
+ * above replaces together with the norm and residual backward passes):
+ * given dout [T, H, D], writes dQ [T, H, D] and dK, dV [B, Skv, H, D] (bf16),
+ * with s = Q K^T sm_scale, P = act(s): dV = P^T dout, dS = act'(s, dout V^T)
+ * sm_scale, dQ = dS K, dK = dS^T Q (summed over each batch's rows).  The
+ * same two kernels as fng_flash_norm_attention_bwd without their norm and
+ * residual terms.  Arguments, workspace
+ * (fng_flash_norm_attention_bwd_workspace_bytes(T, H) bytes, no initial
+ * contents needed), limits, unwritten rows and precision as there. */
+int fng_jagged_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K, const void* V,
+                             const void* dout, void* dQ, void* dK, void* dV, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t T, int64_t max_len_q,
+                             int64_t Skv, int64_t H, int64_t D, float sm_scale, int act, void* stream);
 int fng_flash_norm_attention_bwd(const void* Q, const int32_t* q_offsets, const void* K,
                                  const void* V, const void* out, const void* dout,
                                  const float* ln_mean, const float* ln_rstd,

@@ -168,3 +168,49 @@ def test_fna_bwd_full_size_sampled(full_inputs, act):
         grad_parity(yk[b:b + 1], rk, f"full size batch {b} dK")
         grad_parity(yv[b:b + 1], rv, f"full size batch {b} dV")
     assert np.all(np.isfinite(yq)) and np.all(np.isfinite(yk)) and np.all(np.isfinite(yv))
+
+
+# ---------------------------------------------------------------------------
+# the plain jagged attention's backward (fng_jagged_attention_bwd): the
+# unfused chain's attention step, the same kernels without the norm and
+# residual terms, against oracle.jagged_attention_backward
+# ---------------------------------------------------------------------------
+
+def run_plain(d, max_len, act):
+    Q, K, V, dO = dev(d["Q"]), dev(d["K"]), dev(d["V"]), dev(d["dOut"])
+    off = torch.from_numpy(np.ascontiguousarray(d["offsets"])).to("cuda")
+    dQ, dK, dV = empty_bf16(*Q.shape), empty_bf16(*K.shape), empty_bf16(*V.shape)
+    ws = torch.empty(B.fng_flash_norm_attention_bwd_workspace_bytes(Q.shape[0], Q.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    B.fng_jagged_attention_bwd(Q, off, K, V, dO, dQ, dK, dV, max_len, workspace=ws, sm_scale=SCALE, act=act)
+    torch.cuda.synchronize()
+    return dQ, dK, dV
+
+
+def check_plain(d, dQ, dK, dV, act, what):
+    off = d["offsets"]
+    rq, rk, rv = oracle.jagged_attention_backward(f64(d["Q"]), off, f64(d["K"]), f64(d["V"]), f64(d["dOut"]),
+                                                  SCALE, act)
+    owned = np.concatenate([np.arange(off[b], off[b + 1]) for b in range(len(off) - 1)]).astype(np.int64)
+    grad_parity(host(dQ)[owned], rq[owned], f"{what} dQ")
+    grad_parity(host(dK), rk, f"{what} dK")
+    grad_parity(host(dV), rv, f"{what} dV")
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu"])
+@pytest.mark.parametrize("H", [1, 2, 4, 8])
+def test_jagged_attention_bwd_reduced(H, act):
+    spec, d = case(H, 72, seed=31)
+    log(f"jagged attention bwd H={H} act={act} lengths={LENGTHS} Skv=72")
+    dQ, dK, dV = run_plain(d, spec["max_len"], act)
+    check_plain(d, dQ, dK, dV, act, f"jagged attention bwd H={H} {act}")
+
+
+@pytest.mark.parametrize("Skv", [1, 33, 128])
+def test_jagged_attention_bwd_key_counts(Skv):
+    lengths = [5, 70, 0, 3]
+    for act in ("softmax", "gelu"):
+        spec, d = case(4, Skv, lengths=lengths, seed=32)
+        log(f"jagged attention bwd Skv={Skv} act={act}")
+        dQ, dK, dV = run_plain(d, spec["max_len"], act)
+        check_plain(d, dQ, dK, dV, act, f"jagged attention bwd Skv={Skv} {act}")
