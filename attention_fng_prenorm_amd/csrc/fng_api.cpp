@@ -263,11 +263,16 @@ int norm_bwd(bool ln, const void* G, const void* Wt, const void* H, const float*
   if (!aligned16(H) || reinterpret_cast<uintptr_t>(rstd) % 4 != 0) return FNG_ERR_MISALIGNED;
   if (M * N * 2 >= (int64_t)INT32_MAX) return FNG_ERR_UNSUPPORTED;  // the saved tensor's 32-bit copy offsets
   if (path == FNG_PATH_TWOPASS) return FNG_ERR_UNSUPPORTED;        // the backward has no two-pass path
-  // automatic choice: above 256 columns the full-N backward tiles (64 x 512,
-  // one workgroup per CU) are slower than split-N's 256 x 256 tiles (regrouped
-  // LayerNorm backward at 262144 x 512, K = 256: 294 vs 228 us), so split-N
-  // is taken there whenever the caller gave a workspace of its size
-  if (path == FNG_PATH_AUTO && N > 256 && workspace &&
+  // automatic choice: above 256 columns the full-N backward tiles of 64 x 512
+  // (four waves, one workgroup per CU) are slower than split-N's 256 x 256
+  // tiles (regrouped LayerNorm backward at 262144 x 512, K = 256: 294 vs
+  // 228 us), so split-N is taken there whenever the caller gave a workspace
+  // of its size; tall inputs keep full-N up to 512 columns and K = 1024, where
+  // their eight-wave 128 x 512 tiles are 0-7 % faster than split-N (262144
+  // rows: N = 384, K = 64: 167.6 vs 180.0 us; N = 512, K = 512: 271.6 vs
+  // 281.9 us; at K = 2048 split-N is 3-4 % faster)
+  const bool tall_fulln = fng::bwd_fulln_tall(M) && N <= fng::fulln_max_n() && K <= 1024;
+  if (path == FNG_PATH_AUTO && N > 256 && !tall_fulln && workspace &&
       workspace_bytes >= fng_gemm_postnorm_workspace_bytes(M, N, K, FNG_PATH_SPLITN) && fng::splitn_feasible(M, N))
     path = FNG_PATH_SPLITN;
   path = resolve_path(path, M, N, K);

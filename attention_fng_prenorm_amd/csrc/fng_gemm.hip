@@ -204,8 +204,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(GemmParams
   constexpr bool PX = PP && (EPI == EPI_PLAIN || EPI == EPI_ROWSCALE || (EPI == EPI_PRENORM && BM <= 128));
   constexpr int AX = PX ? 2 * A_PER_WAVE : A_PER_WAVE;  // X copies per wave per (odd) issue
   static_assert(!PX || (STAGES == 4 && BK * 4 == 128), "paired X rows are 128 B in a 4-stage ring");
-  constexpr int RED = IS_BWD ? S::BYTES : 0;
-  constexpr int EXTRA = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
+  // the backward's row reductions: an extra region after the ring, or, where
+  // that would pass the 160 KB of LDS (the 128 x 512 tile fills it), the
+  // ring's tail beyond the saved tile, free once the epilogue starts
+  constexpr int RED_BYTES = IS_BWD ? (WAVES_N * BM * 4 > BM * 8 ? WAVES_N * BM * 4 : BM * 8) : 0;
+  constexpr bool RED_IN_RING = IS_BWD && S::BYTES + RED_BYTES > 160 * 1024;
+  constexpr int RED = !IS_BWD ? 0 : RED_IN_RING ? BM * BN * 2 : S::BYTES;
+  constexpr int EXTRA = RED_IN_RING ? 0 : RED_BYTES;
+  static_assert(!RED_IN_RING || BM * BN * 2 + RED_BYTES <= S::BYTES, "reductions fit beside the saved tile");
   static_assert(S::BYTES + EXTRA <= 160 * 1024, "LDS budget with the backward's reductions");
   __shared__ __attribute__((aligned(1024))) char smem[S::BYTES + EXTRA];
   FNG_LDS char* lds = (FNG_LDS char*)smem;
@@ -1604,12 +1610,14 @@ int launch_postnorm_splitn(const GemmCall& c, bool ln, hipStream_t s) {
 
 // norm backward by regrouping: dZ = norm_bwd(G @ Wt), whole rows per
 // workgroup (the forward full-N tiles) or split-N with the exchange
+bool bwd_fulln_tall(int64_t M) { return M >= 256 * 256; }
+
 int launch_norm_bwd_fulln(const GemmCall& c, const NormBwdArgs& b, bool ln, hipStream_t s) {
   GemmParams p = base_params(c);
   p.H = static_cast<const uint16_t*>(b.H);
   p.rstd_in = b.rstd;
   p.h_raw = b.h_raw ? 1 : 0;
-  const bool tall = c.M >= 256 * 256;
+  const bool tall = bwd_fulln_tall(c.M);
   // (the forward's 256 x 64 tile with BK 64 fills all 160 KB of LDS; the
   // backward needs room for its row reductions)
   if (tall && c.N <= 64)
@@ -1621,6 +1629,11 @@ int launch_norm_bwd_fulln(const GemmCall& c, const NormBwdArgs& b, bool ln, hipS
   if (tall && c.N <= 256)
     return ln ? launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_FULLN, true, false>(p, 0, false, s)
               : launch<kBigBM, kBigBN, kBigBK, kBigWM, kBigWN, EPI_BWD_FULLN, false, false>(p, 0, false, s);
+  // whole 512-column rows in eight waves for tall inputs (the forward's
+  // full-N tile), so no row sums cross workgroups
+  if (tall && c.N <= 512)
+    return ln ? launch<128, 512, 32, 2, 4, EPI_BWD_FULLN, true, false>(p, 0, false, s)
+              : launch<128, 512, 32, 2, 4, EPI_BWD_FULLN, false, false>(p, 0, false, s);
   if (c.N <= 256)
     return ln ? launch<32, 256, 64, 1, 4, EPI_BWD_FULLN, true, false>(p, 0, false, s)
               : launch<32, 256, 64, 1, 4, EPI_BWD_FULLN, false, false>(p, 0, false, s);

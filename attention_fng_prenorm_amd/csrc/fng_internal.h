@@ -59,6 +59,9 @@ int64_t splitn_tiles_m(int64_t M);
 int64_t splitn_tiles_n(int64_t N);
 int64_t splitn_bm();
 int64_t fulln_max_n();
+// the norm backward's full-N tiles for >= 65536 rows (one row block per
+// workgroup, 256 x <= 256 or 128 x 512)
+bool bwd_fulln_tall(int64_t M);
 
 // fng_norm.hip
 int launch_rownorm_bwd(const void* G, const void* H, const float* rstd, void* dZ, int64_t M, int64_t N,

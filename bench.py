@@ -653,7 +653,8 @@ def main():
                 dZa = torch.empty(Ms, Na, dtype=torch.bfloat16, device="cuda")
                 gta = torch.empty_like(dZa)
                 # a workspace of the split-N size: the automatic path takes
-                # split-N from 257 columns on when it is given one
+                # split-N from 257 columns on when it is given one (for these
+                # tall inputs: above 512 columns or K = 1024)
                 nb = B.fng_gemm_postnorm_workspace_bytes(Ms, Na, Ka, B.FNG_PATH_SPLITN)
                 wsa = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
                 t = time_batches({
@@ -667,7 +668,7 @@ def main():
                 rf.append(round(t["fused"], 1))
                 ru.append(round(t["gemm"] + t["norm_bwd"], 1))
                 rh.append(round(100.0 * (t["gemm"] + t["norm_bwd"] - t["fused"]) / t["norm_bwd"], 1))
-                rp.append("splitn" if Na > 256 else "fulln")
+                rp.append("splitn" if Na > 512 or (Na > 256 and Ka > 1024) else "fulln")
                 del Wt, Ha, dZa, gta, wsa
             fused_us.append(rf)
             unfused_us.append(ru)

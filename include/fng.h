@@ -215,7 +215,9 @@ int fng_get_kernel_status(const void* workspace, size_t workspace_bytes, void* s
  * once, as the forward's); TWOPASS returns FNG_ERR_UNSUPPORTED.  AUTO takes
  * the forward's choice, except that for N > 256 it takes split-N whenever
  * `workspace` holds at least the split-N size (faster there than the full-N
- * backward tiles); a smaller or NULL workspace keeps the forward's choice.
+ * backward tiles), unless M >= 65536, N <= 512 and K <= 1024 (then full-N,
+ * whose tiles for such tall inputs are faster); a smaller or NULL workspace
+ * keeps the forward's choice.
  * M*N*2 must be below 2^31.  G, Wt, Y, dZ 16-byte aligned; rstd 4-byte
  * aligned.
  * ------------------------------------------------------------------------- */

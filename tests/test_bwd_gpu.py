@@ -107,6 +107,24 @@ def test_postnorm_bwd_tall_narrow():
         scaled_parity(host(dZ)[rows], ref, f"tall bwd N={N}")
 
 
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("N", [328, 512])
+@pytest.mark.parametrize("path", [B.FNG_PATH_FULLN, B.FNG_PATH_SPLITN], ids=["fulln", "splitn"])
+def test_postnorm_bwd_tall_wide(path, N, kind):
+    # whole rows of up to 512 columns per workgroup for >= 65536 rows (the
+    # automatic choice there), and split-N on the same rows (a ragged
+    # last row block: 65608 = 512 * 128 + 72; a ragged column tile at N = 328)
+    M, K = 65608, 72
+    spec, d = inputs.make_inputs("postnorm_ln_smalln_bwd", M=M, K=K, N=N, seed=44 + N)
+    log(f"postnorm bwd tall {kind} M={M} N={N} path={path}")
+    dZ = run_postnorm_bwd(d, kind, path)
+    rows = np.unique(np.concatenate([[0, 127, 128, 65535, 65536, M - 73, M - 1],
+                                     np.random.default_rng(N).choice(M, 60, replace=False)]))
+    ref = oracle.gemm_postnorm_backward(f64(d["G"][rows]), f64(d["Wt"]), f64(d["H"][rows]),
+                                        d["rstd"][rows], kind)
+    scaled_parity(host(dZ)[rows], ref, f"tall {kind} bwd N={N}")
+
+
 # the ads shapes of the multi-CTA backward (section 3, "What about backward?"),
 # at 2048 rows: the automatic path (full-N up to its width, split-N above)
 ADS_BWD_KN = [(64, 64), (2048, 128), (256, 256), (64, 512), (512, 512), (1024, 1024), (256, 2048), (2048, 2048)]
